@@ -1,0 +1,152 @@
+"""Pins for the oracle's V-Smooth clustering: sketch, k-means, permutation.
+
+Checks use brute force (explicit squared distances), exact rational means,
+SplitMix64's published output sequence, planted clusters with a known
+answer, and invariants (monotone SSE, bijection, stability).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import vc_oracle as O
+
+
+def test_splitmix64_published_sequence():
+    # SplitMix64 (Vigna) started from state 0: the state advances by the golden
+    # gamma before each output, so output i is splitmix64 of i*gamma.
+    gamma = 0x9E3779B97F4A7C15
+    outs = [O.splitmix64((i * gamma) & O.MASK64) for i in range(3)]
+    assert outs == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_sketch_scaling_and_range():
+    rng = np.random.default_rng(0)
+    for scale in (1e-3, 0.7, 1.0, 3.5, 1000.0):
+        v = rng.standard_normal((300, 128)) * scale
+        v = v.astype(np.float32).astype(np.float64)
+        x = O.sketch(v)
+        a = np.abs(v).max()
+        e = int(np.floor(np.log2(a)))
+        shift = 7 - e
+        assert 128 <= np.abs(x).max() <= 255
+        # x is v * 2^shift rounded to the nearest integer, within half a unit
+        assert np.all(np.abs(x - v * 2.0 ** shift) <= 0.5 + 1e-12)
+    assert not np.any(O.sketch(np.zeros((5, 128))))
+
+
+def test_init_positions_distinct_in_range():
+    for S in (1, 2, 3, 7, 128, 129, 1000, 4096, 73397):
+        for k in (1, 2, 3, 32, 64):
+            if k > S:
+                continue
+            for bh in (0, 1, 55):
+                t = O.init_positions(S, k, 0, bh)
+                assert len(set(t.tolist())) == k
+                assert t.min() >= 0 and t.max() < S
+
+
+def brute_assign(x, cent):
+    out = []
+    for row in x:
+        d = [int(((row - c) ** 2).sum()) for c in cent]
+        m = min(d)
+        out.append(d.index(m))              # first (lowest) cluster among ties
+    return np.array(out)
+
+
+def test_assign_equals_bruteforce_distances():
+    rng = np.random.default_rng(1)
+    for trial in range(5):
+        x = rng.integers(-255, 256, (200, 128))
+        cent = rng.integers(-255, 256, (7, 128))
+        cent[3] = cent[5]                    # duplicate centroid: tie must go to 3
+        assert np.array_equal(O.kmeans_assign(x, cent), brute_assign(x, cent))
+
+
+def test_update_is_mean_rounded_half_up_exact():
+    rng = np.random.default_rng(2)
+    x = rng.integers(-255, 256, (50, 128))
+    assign = rng.integers(0, 4, 50)
+    assign[assign == 2] = 1                  # cluster 2 empty: keeps its centroid
+    cent = rng.integers(-255, 256, (4, 128))
+    new = O.kmeans_update(x, assign, cent)
+    for c in range(4):
+        members = x[assign == c]
+        if len(members) == 0:
+            assert np.array_equal(new[c], cent[c])
+            continue
+        for d in range(128):
+            mean = Fraction(int(members[:, d].sum()), len(members))
+            exp = (mean + Fraction(1, 2)).__floor__()
+            assert new[c, d] == exp
+
+
+def sse(x, cent, assign):
+    return int(((x - cent[assign]) ** 2).sum())
+
+
+def test_sse_nonincreasing():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((1000, 128)) + 3 * rng.standard_normal((1, 128))
+    x = O.sketch(v)
+    _, _, hist = O.kmeans(x, 8, 8, 0, 0)
+    prev = None
+    for c in hist:
+        a = O.kmeans_assign(x, c)
+        s = sse(x, c, a)
+        if prev is not None:
+            assert s <= prev
+        prev = s
+
+
+def test_k1_identity_perm():
+    rng = np.random.default_rng(4)
+    v = rng.standard_normal((333, 128))
+    hv = O.prepare_v_head(v, k=1, iters=3)
+    assert np.array_equal(hv.perm, np.arange(333))
+    assert not np.any(hv.assign)
+
+
+def test_planted_clusters_recovered():
+    # 4 well-separated prototypes; tokens of cluster c sit at the strided init
+    # positions' ranges so every initial centroid starts in a different cluster.
+    rng = np.random.default_rng(5)
+    S, k = 400, 4
+    protos = np.zeros((k, 128))
+    for c in range(k):
+        protos[c, 32 * c:32 * (c + 1)] = 8.0
+    labels = np.repeat(np.arange(k), S // k)          # positions 100c..100c+99 -> cluster c
+    # shuffle within each range but keep each init position inside its cluster's range
+    t = O.init_positions(S, k, 0, 0)
+    assert np.array_equal(t // (S // k), np.arange(k))
+    order = rng.permutation(S)
+    labels_shuf = labels.copy()
+    # move tokens around while keeping the init tokens fixed
+    free = np.setdiff1d(np.arange(S), t)
+    labels_shuf[free] = labels[free][rng.permutation(free.size)]
+    v = protos[labels_shuf] + 0.3 * rng.standard_normal((S, 128))
+    hv = O.prepare_v_head(v, k=k, iters=3)
+    # cluster ids follow the init order, so assign equals the planted labels
+    assert np.array_equal(hv.assign, labels_shuf)
+    # and the permutation lists cluster 0's tokens ascending, then cluster 1's, ...
+    expect = np.concatenate([np.flatnonzero(labels_shuf == c) for c in range(k)])
+    assert np.array_equal(hv.perm, expect)
+    del order
+
+
+def test_perm_is_stable_bijection():
+    rng = np.random.default_rng(6)
+    a = rng.integers(0, 9, 5000)
+    p = O.cluster_perm(a)
+    assert np.array_equal(np.sort(p), np.arange(5000))
+    assert np.all(np.diff(a[p]) >= 0)
+    same = np.diff(a[p]) == 0
+    assert np.all(np.diff(p)[same] > 0)
+
+
+def test_zero_v_head():
+    hv = O.prepare_v_head(np.zeros((300, 128)), k=5, iters=2)
+    assert np.array_equal(hv.perm, np.arange(300))
+    assert hv.v_scale == np.float32(1.0)
+    assert not np.any(hv.v8 & 0x7F)
