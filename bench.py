@@ -1,0 +1,197 @@
+"""Benchmark of the VC-Attention forward pass on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already in
+HBM: vc_prepare_v (k-means reorder, block means, E4M3 residual),
+vc_prepare_qk (per-block E4M3 Q and gathered K) and vc_attention_fwd (the
+fused FP8 kernel).  Throughput is attention FLOP per step, 4*B*H*S^2*D,
+divided by the step time.
+
+Default workload: B=1, S=73397, H=56, D=128, bf16 (the MiniMax-H3-shaped
+layer; "Open VC Attention", Description), V-Smooth k=32, T=5.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 (E4M3) MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="synthetic workload id (3, 4 or 5)")
+    ap.add_argument("--heads", type=int, default=None, help="override H (config 4: 7, 14 or 56)")
+    ap.add_argument("--seq", type=int, default=None, help="override S")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle's timed sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_fwd_traffic.json"),
+                    help="HBM bytes per attention launch measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, rows_n: int) -> dict:
+    """The oracle, as is, on one head: full prepare plus a sample of query rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import vc_oracle as O
+    import synth
+
+    qn = q[0, :, 0].double().cpu().numpy()
+    kn = k[0, :, 0].double().cpu().numpy()
+    vn = v[0, :, 0].double().cpu().numpy()
+    S = w.S
+    rows = synth.sample_rows(S, rows_n).numpy()
+    t0 = time.perf_counter()
+    hv = O.prepare_v_head(vn, k=w.k, iters=w.iters, repair_budget=w.repair_budget)
+    hq = O.prepare_qk_head(qn, kn, hv.perm)
+    t1 = time.perf_counter()
+    O.attend_head(hq, hv, rows)
+    t2 = time.perf_counter()
+    t_full_head = (t1 - t0) + (t2 - t1) * S / rows.size       # labelled extrapolation
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    tflops = 4.0 * S * S * w.D / t_full_head / 1e12
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"one head (b=0,h=0) of the same workload: full prepare_v+prepare_qk "
+                   f"({t1 - t0:.2f} s) plus attention for {rows.size} sampled query rows ({t2 - t1:.2f} s); "
+                   f"value = 4*S^2*D / (t_prepare + t_rows*S/{rows.size}) (extrapolated to the full head)"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(attention heads would shard across GPUs with no exchange; that path is not built)", file=sys.stderr)
+        return 2
+    import torch
+
+    import bit_attention_video_vc_amd as vc
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    kw = {}
+    if args.heads is not None:
+        kw["H"] = args.heads
+    if args.seq is not None:
+        kw["S"] = args.seq
+    w = synth.workload(args.config, **kw)
+    log(f"workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype} k={w.k} T={w.iters} beta={w.repair_budget}")
+    t0 = time.time()
+    q, k, v = synth.generate(w, "cpu")
+    log(f"generated inputs on the host in {time.time() - t0:.1f} s")
+    qd, kd, vd = (t.to("cuda") for t in (q, k, v))
+    torch.cuda.synchronize()
+
+    opts = vc.v_opts(True, w.k, w.iters, 0, w.repair_budget)
+    ws = vc.alloc_workspace(vd, opts)
+    out = torch.empty(qd.shape, dtype=torch.bfloat16, device="cuda")
+    lay = vc.vc_workspace_layout(vd, opts)
+    log(f"workspace {lay.total / 2**30:.2f} GiB")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        vc.vc_prepare_v(vd, opts, ws, stream)
+        vc.vc_prepare_qk(qd, kd, opts, ws, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        vc.vc_attention_fwd(out, opts, ws, 0.0, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    log(f"timed {args.steps} steps in {t_total:.3f} s")
+
+    ms_per_step = 1e3 * t_total / args.steps
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    attn_tflops = flops / (attn_avg_ms * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            key = f"B{w.B}_H{w.H}_S{w.S}"
+            traffic = tj.get(key, {}).get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    res = {
+        "metric": "FP8 attention fwd TFLOPS + % of MI355X FP8 MFMA peak at S~73k, D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D} {str(w.dtype).replace('torch.', '')} in, bf16 out, "
+                        f"non-causal, V-Smooth k={w.k} T={w.iters}, repair={w.repair_budget}",
+            "step": "full call: vc_prepare_v + vc_prepare_qk + vc_attention_fwd",
+            "flop_per_step": flops,
+            "parallelism": "single GPU",
+        },
+        "pct_of_fp8_peak_full_call": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "kernel_only": {"tflops": round(attn_tflops, 2), "avg_ms": round(attn_avg_ms, 4),
+                        "pct_of_fp8_peak": round(100 * attn_tflops / PEAK_FP8_TFLOPS, 2)},
+        "prepare_ms_per_step": round(ms_per_step - attn_avg_ms, 3),
+        "roofline": {
+            "kernel": "k_vc_attn_fwd",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,193 @@
+"""Python binding of libvc.so, the gfx950 VC-Attention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/vc.h``.  PyTorch supplies
+device memory and the current stream.  Importing this module does not load
+the library; the first call does, and raises if it has not been built.
+
+Entry points (same names as the C ABI):
+  vc_workspace_layout(v_like, opts)                 -> VcWsLayout
+  vc_prepare_v(v, opts, ws)
+  vc_prepare_qk(q, k, opts, ws)
+  vc_attention_fwd(out, opts, ws, sm_scale=0.0)
+plus the convenience ``attention(q, k, v, ...)`` that runs all three.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "VcDesc", "VcVOpts", "VcAttnOpts", "VcWsLayout", "VcHeadHdr", "VCError", "lib", "lib_path",
+    "v_opts", "desc_of", "vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd",
+    "alloc_workspace", "attention", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libvc.so")
+
+VC_OK, VC_ERR_ARG, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_DEVICE = range(5)
+VC_F16, VC_BF16 = 0, 1
+
+# symbols the header declares (checked by the ABI tests)
+EXPORTS = ("vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd",
+           "vc_status_string", "vc_last_error", "vc_version")
+
+
+class VcDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("sB", ctypes.c_int64), ("sS", ctypes.c_int64), ("sH", ctypes.c_int64)]
+
+
+class VcVOpts(ctypes.Structure):
+    _fields_ = [("smooth", ctypes.c_int32), ("k", ctypes.c_int32), ("iters", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64), ("repair_budget", ctypes.c_float),
+                ("reserved2", ctypes.c_float)]
+
+
+class VcAttnOpts(ctypes.Structure):
+    _fields_ = [("sm_scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+class VcWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "total", "q8", "q_scale", "k8", "k_scale", "v8", "v_mean", "v_meanp", "hdr",
+        "assign", "perm", "rep_pos", "rep_k8", "rep_ks", "rep_e8", "scratch")] + \
+        [("nblk", ctypes.c_int32), ("nrep", ctypes.c_int32), ("nrep_pad", ctypes.c_int32),
+         ("reserved", ctypes.c_int32)]
+
+
+class VcHeadHdr(ctypes.Structure):
+    _fields_ = [("v_scale", ctypes.c_float), ("v_inv", ctypes.c_float), ("v_amax_bits", ctypes.c_uint32),
+                ("r_amax_bits", ctypes.c_uint32), ("shift", ctypes.c_int32), ("nrep", ctypes.c_int32),
+                ("rep_scale", ctypes.c_float), ("e_amax_bits", ctypes.c_uint32)]
+
+
+class VCError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvc.so (in-tree build) and declare its signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is not built; run `python -m bit_attention_video_vc_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        P = ctypes.POINTER
+        L.vc_workspace_layout.argtypes = [P(VcDesc), P(VcVOpts), P(VcWsLayout)]
+        L.vc_prepare_v.argtypes = [P(VcDesc), ctypes.c_void_p, P(VcVOpts), ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p]
+        L.vc_prepare_qk.argtypes = [P(VcDesc), ctypes.c_void_p, P(VcDesc), ctypes.c_void_p, P(VcVOpts),
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.vc_attention_fwd.argtypes = [P(VcDesc), ctypes.c_void_p, P(VcVOpts), P(VcAttnOpts), ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]
+        for f in ("vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd"):
+            getattr(L, f).restype = ctypes.c_int
+        L.vc_status_string.argtypes = [ctypes.c_int]
+        for f in ("vc_status_string", "vc_last_error", "vc_version"):
+            getattr(L, f).restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != VC_OK:
+        L = lib()
+        raise VCError(status, f"{L.vc_status_string(status).decode()}: {L.vc_last_error().decode()}")
+
+
+def v_opts(smooth: bool = True, k: int = 32, iters: int = 5, seed: int = 0, repair_budget: float = 0.0) -> VcVOpts:
+    return VcVOpts(int(bool(smooth)), int(k), int(iters), 0, int(seed), float(repair_budget), 0.0)
+
+
+def desc_of(t: torch.Tensor) -> VcDesc:
+    """Descriptor of a [B,S,H,128] or [S,H,128] fp16/bf16 tensor (D contiguous)."""
+    if t.dim() == 3:
+        t = t.unsqueeze(0)
+    if t.dim() != 4:
+        raise ValueError("expected a [B,S,H,D] or [S,H,D] tensor")
+    if t.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    dt = {torch.float16: VC_F16, torch.bfloat16: VC_BF16}.get(t.dtype, -1)
+    B, S, H, D = t.shape
+    return VcDesc(B, S, H, D, dt, 0, t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def vc_workspace_layout(v_like: torch.Tensor | VcDesc, opts: VcVOpts) -> VcWsLayout:
+    d = v_like if isinstance(v_like, VcDesc) else desc_of(v_like)
+    out = VcWsLayout()
+    _check(lib().vc_workspace_layout(ctypes.byref(d), ctypes.byref(opts), ctypes.byref(out)))
+    return out
+
+
+def alloc_workspace(v_like: torch.Tensor, opts: VcVOpts) -> torch.Tensor:
+    lay = vc_workspace_layout(v_like, opts)
+    return torch.empty(lay.total, dtype=torch.uint8, device=v_like.device)
+
+
+def vc_prepare_v(v: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, stream=None) -> None:
+    d = desc_of(v)
+    _check(lib().vc_prepare_v(ctypes.byref(d), ctypes.c_void_p(v.data_ptr()), ctypes.byref(opts),
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def vc_prepare_qk(q: torch.Tensor, k: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, stream=None) -> None:
+    dq, dk = desc_of(q), desc_of(k)
+    _check(lib().vc_prepare_qk(ctypes.byref(dq), ctypes.c_void_p(q.data_ptr()), ctypes.byref(dk),
+                               ctypes.c_void_p(k.data_ptr()), ctypes.byref(opts), ctypes.c_void_p(ws.data_ptr()),
+                               ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def vc_attention_fwd(out: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, sm_scale: float = 0.0,
+                     stream=None) -> None:
+    d = desc_of(out)
+    a = VcAttnOpts(float(sm_scale), 0)
+    _check(lib().vc_attention_fwd(ctypes.byref(d), ctypes.c_void_p(out.data_ptr()), ctypes.byref(opts),
+                                  ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, smooth: bool = True, clusters: int = 32,
+              iters: int = 5, seed: int = 0, repair_budget: float = 0.0, sm_scale: float = 0.0,
+              ws: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Full call: prepare_v, prepare_qk and the fused forward; returns bf16 [B,S,H,128] (or [S,H,128])."""
+    o = v_opts(smooth, clusters, iters, seed, repair_budget)
+    if ws is None:
+        ws = alloc_workspace(v, o)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    vc_prepare_v(v, o, ws, stream)
+    vc_prepare_qk(q, k, o, ws, stream)
+    vc_attention_fwd(out, o, ws, sm_scale, stream)
+    return out
+
+
+@dataclass
+class WorkspaceView:
+    """Host-side views of a prepared workspace (copies), for tests and diagnostics."""
+
+    layout: VcWsLayout
+    B: int
+    S: int
+    H: int
+
+    def region(self, ws: torch.Tensor, name: str, dtype: torch.dtype, count: int) -> torch.Tensor:
+        off = getattr(self.layout, name)
+        nbytes = count * torch.tensor([], dtype=dtype).element_size()
+        return ws[off:off + nbytes].view(dtype).cpu()

@@ -1,0 +1,148 @@
+// vc_common.hpp -- device helpers shared by the VC-Attention kernels (gfx950).
+//
+// E4M3 here is the OCP E4M3FN format that gfx950's FP8 MFMA consumes
+// (cbsz/blgp = 0): sign, 4 exponent bits (bias 7), 3 mantissa bits, no
+// infinities, 0x7F/0xFF NaN, largest finite 448 (0x7E).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "vc.h"
+
+namespace vc {
+
+constexpr int kD = 128;          // head dimension
+constexpr int kBlock = 128;      // tokens per quantisation block / KV tile
+constexpr int kTileBytes = kBlock * kD;
+constexpr int kMaxK = 64;        // clusters per head
+constexpr int kAsgTok = 128;     // tokens per k-means assignment / sort block
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---- input loads ------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
+}
+
+// Load 8 consecutive elements (16 bytes, 16-byte aligned) as float.
+__device__ __forceinline__ void load8(const void* base, int64_t off, int dtype, float* out) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  if (dtype == VC_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+      out[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = f16_bits_to_f32(w[i] & 0xFFFFu);
+      out[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
+    }
+  }
+}
+
+__device__ __forceinline__ float load1(const void* base, int64_t off, int dtype) {
+  const uint32_t b = reinterpret_cast<const uint16_t*>(base)[off];
+  return dtype == VC_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- OCP E4M3FN encode: round half to even, saturate to +-448 ----------------
+// The sign bit follows the input's sign, also when the magnitude rounds to 0.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {                       // below 2^-6: quantum 2^-9 (subnormal codes)
+    return sign | static_cast<uint32_t>(rintf(a * 512.0f));
+  }
+  const int e = static_cast<int>(__float_as_uint(a) >> 23) - 127;   // floor(log2 a), -6..8
+  const uint32_t m = static_cast<uint32_t>(rintf(ldexpf(a, 3 - e)));   // 8..16, exact scaling
+  const uint32_t code = static_cast<uint32_t>((e + 7) * 8) + (m - 8u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// E4M3 decode (finite codes).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? static_cast<float>(m) * 0.001953125f
+                           : ldexpf(1.0f + static_cast<float>(m) * 0.125f, static_cast<int>(e) - 7);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// ---- packed tile offsets (see vc.h) -----------------------------------------
+// Row tile: operand rows of 16, two 16-byte halves of each 32-byte lane slice.
+__device__ __forceinline__ int row_tile_off(int r, int d) {
+  return ((((r >> 4) * 2 + ((d & 31) >> 4)) * 64 + (r & 15) + 16 * (d >> 5)) << 4) + (d & 15);
+}
+// Transposed tile: key j and channel d, in the P^T slot order of the score
+// accumulator (16x16 MFMA output rows 4g..4g+3 of key sub-tile t).
+__device__ __forceinline__ int tr_tile_off(int j, int d) {
+  const int g = (j & 15) >> 2;
+  const int i = 4 * (j >> 4) + (j & 3);
+  return ((((d >> 4) * 2 + (i >> 4)) * 64 + (d & 15) + 16 * g) << 4) + (i & 15);
+}
+
+// ---- reductions ---------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Max over a block of blockDim.x threads (multiple of 64); `red` holds >= 16 floats.
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < nw; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+// Splitmix64 output for one state value (Vigna's public definition).
+__device__ __host__ __forceinline__ uint64_t splitmix64(uint64_t z) {
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Workspace scratch (k-means state, sort counters, repair scores), offsets
+// relative to the scratch region; computed identically on host and device.
+struct Scratch {
+  size_t cent, csum, ccount, chunk_hist, chunk_off, rep_norm, rep_sel, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+__host__ __device__ inline Scratch scratch_layout(int64_t BH, int S, int k, int nrep) {
+  Scratch s;
+  size_t o = 0;
+  const int64_t nchunk = (S + kAsgTok - 1) / kAsgTok;
+  s.cent = o;        o = align256(o + sizeof(int32_t) * BH * k * kD);
+  s.csum = o;        o = align256(o + sizeof(int32_t) * BH * k * kD);
+  s.ccount = o;      o = align256(o + sizeof(int32_t) * BH * k);
+  s.chunk_hist = o;  o = align256(o + sizeof(int32_t) * BH * nchunk * k);
+  s.chunk_off = o;   o = align256(o + sizeof(int32_t) * BH * nchunk * k);
+  s.rep_norm = o;    o = align256(o + (nrep > 0 ? sizeof(double) * BH * S : 0));
+  s.rep_sel = o;     o = align256(o + (nrep > 0 ? sizeof(int32_t) * BH * 4 : 0));
+  s.total = o;
+  return s;
+}
+
+}  // namespace vc

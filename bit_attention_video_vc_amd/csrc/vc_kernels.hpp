@@ -1,0 +1,54 @@
+// vc_kernels.hpp -- internal launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vc.h"
+
+namespace vc {
+
+// A [B,S,H,128] fp16/bf16 view (element strides; D contiguous).
+struct TensorArg {
+  const void* p;
+  int64_t sB, sS, sH;
+  int dtype;
+};
+
+// Typed pointers into one workspace.
+struct WsPtrs {
+  uint8_t *q8, *k8, *v8, *rep_k8, *rep_e8;
+  float *q_scale, *k_scale, *v_mean, *v_meanp, *rep_ks;
+  vc_head_hdr* hdr;
+  int32_t *assign, *perm, *rep_pos;
+  int32_t *cent, *csum, *ccount, *chunk_hist, *chunk_off;
+  double* rep_norm;
+  int nblk, nrep, nrep_pad;
+};
+
+struct AttnArgs {
+  const uint8_t* q8;
+  const float* q_scale;
+  const uint8_t* k8;
+  const float* k_scale;
+  const uint8_t* v8;
+  const float* v_meanp;
+  const vc_head_hdr* hdr;
+  const uint8_t* rep_k8;
+  const float* rep_ks;
+  const uint8_t* rep_e8;
+  uint16_t* out;
+  int64_t osB, osS, osH;
+  int S, H, nblk, nrep_pad, total_wg;
+  float sm_scale;
+};
+
+hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_opts& o, const WsPtrs& ws,
+                            hipStream_t st);
+hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& k, int B, int S, int H, const WsPtrs& ws,
+                             hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int BH, hipStream_t st);
+hipError_t init_kernel_attributes();
+size_t kmeans_assign_smem(int k);
+
+}  // namespace vc

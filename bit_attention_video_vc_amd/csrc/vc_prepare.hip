@@ -1,0 +1,695 @@
+// vc_prepare.hip -- prepare kernels for the VC-Attention forward (gfx950).
+//
+// V-Smooth ("VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+// Attention", Abstract; "Nunchux AI lanza VC-Attention kernel ...",
+// paragraph 2): value tokens of each (batch, head) are clustered by k-means
+// and reordered by cluster; each 128-position block's mean is subtracted and
+// only the residual is quantised to E4M3 with one scale per head ("Open VC
+// Attention", Description).  K is gathered through the same permutation so
+// keys stay paired with values (non-causal attention is invariant to a joint
+// key/value reordering); Q keeps its order.  Q and K get one E4M3 scale per
+// 128-token block.
+//
+// The clustering runs on an integer sketch of V (V scaled by an exact power
+// of two and rounded to [-255, 255]); every distance, sum and count is an
+// exact integer, so assignments and the permutation do not depend on
+// summation order.  All kernels are HBM-bound streaming passes except the
+// distance loop of k_kmeans_assign.
+#include "vc_common.hpp"
+#include "vc_kernels.hpp"
+
+namespace vc {
+
+// ---------------------------------------------------------------------------
+__global__ void k_fill_u32(uint32_t* p, uint32_t value, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+// max|v| over each (b,h).  grid (ceil(S/64), H, B), 256 threads.
+__global__ void __launch_bounds__(256) k_v_absmax(TensorArg v, int S, vc_head_hdr* hdr) {
+  __shared__ float red[16];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y;
+  const int s0 = blockIdx.x * 64;
+  float m = 0.0f;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int s = s0 + it * 16 + (threadIdx.x >> 4);
+    if (s < S) {
+      float x[8];
+      load8(v.p, b * v.sB + s * v.sS + h * v.sH + 8 * (threadIdx.x & 15), v.dtype, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+    }
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0 && m > 0.0f) atomicMax(&hdr[b * H + h].v_amax_bits, __float_as_uint(m));
+}
+
+__device__ __forceinline__ float sketch1(float x, int shift) {
+  return fminf(fmaxf(rintf(ldexpf(x, shift)), -255.0f), 255.0f);
+}
+
+// Sketch shift and seeded strided initial centroids.  grid (BH), 128 threads.
+__global__ void __launch_bounds__(128) k_kmeans_init(TensorArg v, int S, int H, int k, uint64_t seed,
+                                                     vc_head_hdr* hdr, int32_t* cent, int32_t* csum,
+                                                     int32_t* ccount) {
+  const int bh = blockIdx.x, b = bh / H, h = bh % H, d = threadIdx.x;
+  const float a = __uint_as_float(hdr[bh].v_amax_bits);
+  int shift = 0;
+  if (a > 0.0f) {
+    int e;
+    frexpf(a, &e);              // a in [2^(e-1), 2^e)
+    shift = 8 - e;              // 7 - floor(log2 a)
+  }
+  if (d == 0) hdr[bh].shift = shift;
+  const int stride = S / k > 1 ? S / k : 1;
+  const int phi = static_cast<int>(splitmix64(seed ^ static_cast<uint64_t>(bh)) % static_cast<uint64_t>(stride));
+  for (int c = 0; c < k; ++c) {
+    const int t = static_cast<int>((static_cast<int64_t>(c) * S) / k) + phi;
+    const float x = load1(v.p, b * v.sB + t * v.sS + h * v.sH + d, v.dtype);
+    cent[(static_cast<int64_t>(bh) * k + c) * kD + d] = static_cast<int32_t>(sketch1(x, shift));
+    csum[(static_cast<int64_t>(bh) * k + c) * kD + d] = 0;
+  }
+  if (d < k) ccount[bh * k + d] = 0;
+}
+
+// One Lloyd assignment pass over 128 tokens per block.
+//   ACCUM: add the block's per-cluster sketch sums and counts to csum/ccount.
+//   FINAL: write assign[] and the block's cluster histogram (for the sort).
+// grid (ceil(S/128), H, B), 128 threads (one token per thread in the
+// distance loop).  Scores |c|^2 - 2 x.c are exact integers (|x|,|c| <= 255,
+// 128 terms: below 2^24 per dot product), ties go to the lowest cluster.
+constexpr int kTokPitch = kD + 8;   // int16 row pitch (272 B): staggers LDS banks
+
+template <bool ACCUM, bool FINAL>
+__global__ void __launch_bounds__(kAsgTok) k_kmeans_assign(TensorArg v, int S, int k, const vc_head_hdr* hdr,
+                                                           const int32_t* cent, int32_t* csum, int32_t* ccount,
+                                                           int32_t* assign, int32_t* chunk_hist) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int16_t* tok = reinterpret_cast<int16_t*>(smem);                               // [128][136]
+  float* cl = reinterpret_cast<float*>(smem + kAsgTok * kTokPitch * 2);          // [k][128]
+  int32_t* part = reinterpret_cast<int32_t*>(cl + k * kD);                       // [k][128]
+  int32_t* cnorm = part + k * kD;                                                // [k]
+  int32_t* cnt = cnorm + kMaxK;                                                  // [k]
+  int32_t* asg = cnt + kMaxK;                                                    // [128]
+
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
+  const int s0 = blockIdx.x * kAsgTok;
+  const int tid = threadIdx.x;
+  const int shift = hdr[bh].shift;
+  const int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
+
+  for (int i = tid; i < k * kD; i += kAsgTok) {
+    cl[i] = static_cast<float>(cg[i]);
+    if (ACCUM) part[i] = 0;
+  }
+  if (tid < kMaxK) cnt[tid] = 0;
+  // stage the block's sketch rows: 16 threads per token row, 8 channels each
+  for (int i = tid; i < kAsgTok * 16; i += kAsgTok) {
+    const int r = i >> 4, c8 = (i & 15) * 8;
+    const int s = s0 + r;
+    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (s < S) load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tok[r * kTokPitch + c8 + j] = static_cast<int16_t>(sketch1(x[j], shift));
+  }
+  __syncthreads();
+  if (tid < k) {
+    int32_t n2 = 0;
+    for (int d = 0; d < kD; ++d) {
+      const int32_t c = static_cast<int32_t>(cl[tid * kD + d]);
+      n2 += c * c;
+    }
+    cnorm[tid] = n2;
+  }
+  __syncthreads();
+
+  const int s = s0 + tid;
+  int best_c = 0;
+  if (s < S) {
+    float x[kD];
+#pragma unroll
+    for (int d = 0; d < kD; ++d) x[d] = static_cast<float>(tok[tid * kTokPitch + d]);
+    int32_t best = 0x7FFFFFFF;
+    for (int c0 = 0; c0 < k; c0 += 4) {
+      float acc[4] = {0, 0, 0, 0};
+      const int nc = k - c0 < 4 ? k - c0 : 4;
+#pragma unroll 8
+      for (int d = 0; d < kD; d += 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int cj = c0 + (j < nc ? j : 0);
+          const float4 cv = *reinterpret_cast<const float4*>(&cl[cj * kD + d]);
+          acc[j] = fmaf(x[d], cv.x, acc[j]);
+          acc[j] = fmaf(x[d + 1], cv.y, acc[j]);
+          acc[j] = fmaf(x[d + 2], cv.z, acc[j]);
+          acc[j] = fmaf(x[d + 3], cv.w, acc[j]);
+        }
+      }
+      for (int j = 0; j < nc; ++j) {
+        const int32_t sc = cnorm[c0 + j] - 2 * static_cast<int32_t>(acc[j]);
+        if (sc < best) {
+          best = sc;
+          best_c = c0 + j;
+        }
+      }
+    }
+    asg[tid] = best_c;
+    atomicAdd(&cnt[best_c], 1);
+    if (FINAL) assign[static_cast<int64_t>(bh) * S + s] = best_c;
+  } else {
+    asg[tid] = -1;
+  }
+  __syncthreads();
+
+  if (ACCUM) {
+    // thread owns channel d; walk the block's tokens in order
+    const int d = tid;
+    for (int r = 0; r < kAsgTok; ++r) {
+      const int c = asg[r];
+      if (c >= 0) part[c * kD + d] += tok[r * kTokPitch + d];
+    }
+    __syncthreads();
+    int32_t* gs = csum + static_cast<int64_t>(bh) * k * kD;
+    for (int i = tid; i < k * kD; i += kAsgTok)
+      if (part[i] != 0) atomicAdd(&gs[i], part[i]);
+    if (tid < k && cnt[tid] != 0) atomicAdd(&ccount[bh * k + tid], cnt[tid]);
+  }
+  if (FINAL && tid < k) {
+    const int nchunk = (S + kAsgTok - 1) / kAsgTok;
+    chunk_hist[(static_cast<int64_t>(bh) * nchunk + blockIdx.x) * k + tid] = cnt[tid];
+  }
+}
+
+size_t kmeans_assign_smem(int k) {
+  return static_cast<size_t>(kAsgTok) * kTokPitch * 2 + static_cast<size_t>(k) * kD * 4 * 2 +
+         (2 * kMaxK + kAsgTok) * 4;
+}
+
+hipError_t init_kernel_attributes() {
+  const int bytes = static_cast<int>(kmeans_assign_smem(kMaxK));
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_kmeans_assign<true, false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(k_kmeans_assign<false, true>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+// New centroid = floor((2*sum + n) / (2n)) (mean rounded half up); empty
+// clusters keep their centroid; sums and counts are cleared for the next pass.
+// grid (BH), 256 threads.
+__global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int32_t* csum, int32_t* ccount) {
+  const int bh = blockIdx.x;
+  int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
+  int32_t* sg = csum + static_cast<int64_t>(bh) * k * kD;
+  for (int i = threadIdx.x; i < k * kD; i += blockDim.x) {
+    const int64_t n = ccount[bh * k + i / kD];
+    if (n > 0) {
+      const int64_t num = 2 * static_cast<int64_t>(sg[i]) + n, den = 2 * n;
+      int64_t q = num / den;
+      if ((num % den != 0) && (num < 0)) q -= 1;     // floor division
+      cg[i] = static_cast<int32_t>(q);
+    }
+    sg[i] = 0;
+  }
+  __syncthreads();
+  if (threadIdx.x < k) ccount[bh * k + threadIdx.x] = 0;
+}
+
+// Per-cluster start offsets and per-chunk offsets for the stable scatter.
+// grid (BH), 64 threads (thread = cluster).
+__global__ void __launch_bounds__(64) k_cluster_scan(int S, int k, const int32_t* chunk_hist, int32_t* chunk_off) {
+  __shared__ int32_t tot[kMaxK];
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const int nchunk = (S + kAsgTok - 1) / kAsgTok;
+  const int32_t* hst = chunk_hist + static_cast<int64_t>(bh) * nchunk * k;
+  int32_t* off = chunk_off + static_cast<int64_t>(bh) * nchunk * k;
+  int32_t t = 0;
+  if (c < k)
+    for (int j = 0; j < nchunk; ++j) t += hst[j * k + c];
+  tot[c] = t;
+  __syncthreads();
+  int32_t start = 0;
+  for (int j = 0; j < c && j < k; ++j) start += tot[j];
+  if (c < k) {
+    int32_t run = start;
+    for (int j = 0; j < nchunk; ++j) {
+      off[j * k + c] = run;
+      run += hst[j * k + c];
+    }
+  }
+}
+
+// Stable counting-sort scatter: perm[pos] = token, ordered by (cluster, token).
+// grid (ceil(S/128), H, B), 128 threads (2 waves).
+__global__ void __launch_bounds__(kAsgTok) k_cluster_scatter(int S, int k, const int32_t* assign,
+                                                             const int32_t* chunk_off, int32_t* perm) {
+  __shared__ int32_t wcount[kAsgTok / 64][kMaxK];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < (kAsgTok / 64) * kMaxK; i += kAsgTok) (&wcount[0][0])[i] = 0;
+  __syncthreads();
+  const int s = blockIdx.x * kAsgTok + tid;
+  const bool valid = s < S;
+  const int c = valid ? assign[static_cast<int64_t>(bh) * S + s] : -1;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t rem = __ballot(valid);
+  int rank = 0;
+  while (rem) {
+    const int leader = __ffsll(static_cast<unsigned long long>(rem)) - 1;
+    const int cl = __builtin_amdgcn_readlane(c, leader);
+    const uint64_t m = __ballot(valid && c == cl);
+    if (valid && c == cl) rank = __popcll(m & lt);
+    if (lane == 0) wcount[w][cl] = __popcll(m);
+    rem &= ~m;
+  }
+  __syncthreads();
+  if (valid) {
+    const int nchunk = (S + kAsgTok - 1) / kAsgTok;
+    int pos = chunk_off[(static_cast<int64_t>(bh) * nchunk + blockIdx.x) * k + c] + rank;
+    for (int j = 0; j < w; ++j) pos += wcount[j][c];
+    perm[static_cast<int64_t>(bh) * S + pos] = s;
+  }
+}
+
+// smooth = 0: identity order, cluster 0.  grid (ceil(S/256), H, B).
+__global__ void k_identity_perm(int S, int32_t* assign, int32_t* perm) {
+  const int bh = blockIdx.z * gridDim.y + blockIdx.y;
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s < S) {
+    perm[static_cast<int64_t>(bh) * S + s] = s;
+    assign[static_cast<int64_t>(bh) * S + s] = 0;
+  }
+}
+
+// Block means over permuted positions and the residual amax per head.
+// mu = fp32(fp64(sum) / n); R = fp32(v - mu).  grid (nblk, H, B), 128 threads.
+__global__ void __launch_bounds__(128) k_v_block_stats(TensorArg v, int S, int smooth, const int32_t* perm,
+                                                       float* v_mean, vc_head_hdr* hdr) {
+  __shared__ int32_t pp[kBlock];
+  __shared__ float red[16];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x;
+  const int d = threadIdx.x;
+  const int p0 = blk * kBlock;
+  const int n = S - p0 < kBlock ? S - p0 : kBlock;
+  if (d < n) pp[d] = perm[static_cast<int64_t>(bh) * S + p0 + d];
+  __syncthreads();
+  float mu = 0.0f;
+  if (smooth) {
+    double sum = 0.0;
+    for (int j = 0; j < n; ++j) sum += static_cast<double>(load1(v.p, b * v.sB + pp[j] * v.sS + h * v.sH + d, v.dtype));
+    mu = static_cast<float>(sum / static_cast<double>(n));
+  }
+  v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + d] = mu;
+  float m = 0.0f;
+  for (int j = 0; j < n; ++j) {
+    const float x = load1(v.p, b * v.sB + pp[j] * v.sS + h * v.sH + d, v.dtype);
+    m = fmaxf(m, fabsf(x - mu));
+  }
+  m = block_max(m, red);
+  if (d == 0 && m > 0.0f) atomicMax(&hdr[bh].r_amax_bits, __float_as_uint(m));
+}
+
+__device__ __forceinline__ void v_scales(const vc_head_hdr& hd, float* s, float* inv) {
+  const float a = __uint_as_float(hd.r_amax_bits);
+  *inv = a > 0.0f ? 448.0f / a : 1.0f;
+  *s = a > 0.0f ? a / 448.0f : 1.0f;
+}
+
+// Gather a 128x128 code block into a transposed (P^T slot order) tile.
+__device__ __forceinline__ void store_tr_tile(const uint8_t* codes /*[128][128] in LDS*/, uint8_t* dst) {
+  for (int ch = threadIdx.x; ch < kTileBytes / 16; ch += blockDim.x) {
+    const int lane = ch & 63, hh = (ch >> 6) & 1, dt = ch >> 7;
+    const int g = lane >> 4, d = 16 * dt + (lane & 15);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bi = 16 * hh + 4 * q + e;                    // slot byte 0..31
+        const int j = 16 * (bi >> 2) + 4 * g + (bi & 3);       // key within the tile
+        word |= static_cast<uint32_t>(codes[j * kD + d]) << (8 * e);
+      }
+      w[q] = word;
+    }
+    *reinterpret_cast<uint4*>(dst + ch * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// E4M3 residual codes, written as transposed tiles; mu' = mu / s_v.
+// grid (nblk, H, B), 256 threads.
+__global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const int32_t* perm, const float* v_mean,
+                                                      vc_head_hdr* hdr, uint8_t* v8, float* v_meanp) {
+  __shared__ __align__(16) uint8_t codes[kTileBytes];
+  __shared__ float mu[kD];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
+  float s_v, inv;
+  v_scales(hdr[bh], &s_v, &inv);
+  if (threadIdx.x < kD) {
+    const float m = v_mean[(static_cast<int64_t>(bh) * nblk + blk) * kD + threadIdx.x];
+    mu[threadIdx.x] = m;
+    v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kD + threadIdx.x] = m / s_v;
+  }
+  if (blk == 0 && threadIdx.x == 0) {
+    hdr[bh].v_scale = s_v;
+    hdr[bh].v_inv = inv;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < kBlock * 16; t += blockDim.x) {
+    const int j = t >> 4, c8 = (t & 15) * 8;
+    const int p = blk * kBlock + j;
+    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (p < S) {
+      const int s = perm[static_cast<int64_t>(bh) * S + p];
+      float x[8];
+      load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = e4m3_encode((x[e] - mu[c8 + e]) * inv);
+    }
+    *reinterpret_cast<uint2*>(&codes[j * kD + c8]) =
+        make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+  }
+  __syncthreads();
+  store_tr_tile(codes, v8 + (static_cast<int64_t>(bh) * nblk + blk) * kTileBytes);
+}
+
+// Per-block amax E4M3 quantisation of 128 rows into a row tile.  GATHER: row
+// p is token perm[p] (K); otherwise row p is token p (Q).
+// grid (nblk, H, B), 256 threads; 4 (row, 16-channel) tasks per thread.
+template <bool GATHER>
+__global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const int32_t* perm, uint8_t* out8,
+                                                    float* scale) {
+  __shared__ float red[16];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
+  float val[4][16];
+  float m = 0.0f;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int task = threadIdx.x + 256 * it;
+    const int r = task >> 3, c16 = (task & 7) * 16;
+    const int p = blk * kBlock + r;
+    if (p < S) {
+      const int s = GATHER ? perm[static_cast<int64_t>(bh) * S + p] : p;
+      const int64_t off = b * x.sB + s * x.sS + h * x.sH + c16;
+      load8(x.p, off, x.dtype, &val[it][0]);
+      load8(x.p, off + 8, x.dtype, &val[it][8]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) val[it][e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(val[it][e]));
+  }
+  m = block_max(m, red);
+  const float inv = m > 0.0f ? 448.0f / m : 1.0f;
+  const float sc = m > 0.0f ? m / 448.0f : 1.0f;
+  uint8_t* tile = out8 + (static_cast<int64_t>(bh) * nblk + blk) * kTileBytes;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int task = threadIdx.x + 256 * it;
+    const int r = task >> 3, c16 = (task & 7) * 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) word |= e4m3_encode(val[it][4 * q + e] * inv) << (8 * e);
+      w[q] = word;
+    }
+    *reinterpret_cast<uint4*>(tile + row_tile_off(r, c16)) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (threadIdx.x == 0) scale[static_cast<int64_t>(bh) * nblk + blk] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// Residual repair ("Open VC Attention", Description): the quantisation error
+// e = fp32(R - fp32(s_v * dec(code))) of the worst-rounded value tokens.
+__device__ __forceinline__ void resid_err(const float* xv /*8*/, const float* mu /*8*/, float s_v, float inv,
+                                          float* e /*8*/) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float r = xv[i] - mu[i];
+    const float deq = s_v * e4m3_decode(e4m3_encode(r * inv));
+    e[i] = r - deq;
+  }
+}
+
+// Squared error norm per permuted position (sequential fp64 sum over d).
+// grid (nblk, H, B), 128 threads (one key per thread).
+__global__ void __launch_bounds__(128) k_repair_norm(TensorArg v, int S, const int32_t* perm, const float* v_mean,
+                                                     const vc_head_hdr* hdr, double* norm) {
+  __shared__ float mu[kD];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x;
+  mu[threadIdx.x] = v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + threadIdx.x];
+  __syncthreads();
+  const int p = blk * kBlock + threadIdx.x;
+  if (p >= S) return;
+  const int s = perm[static_cast<int64_t>(bh) * S + p];
+  float s_v, inv;
+  v_scales(hdr[bh], &s_v, &inv);
+  double acc = 0.0;
+  for (int c8 = 0; c8 < kD; c8 += 8) {
+    float x[8], e[8];
+    load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
+    resid_err(x, mu + c8, s_v, inv, e);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = acc + static_cast<double>(e[i]) * static_cast<double>(e[i]);
+  }
+  norm[static_cast<int64_t>(bh) * S + p] = acc;
+}
+
+// Top-nrep positions by error norm (ties to the smaller position), written in
+// ascending position order; radix select on the fp64 bit patterns (the norms
+// are >= 0, so their bits order like the values).  grid (BH), 256 threads.
+__global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep_pad, const double* norm,
+                                                       int32_t* rep_pos, vc_head_hdr* hdr) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t sh_prefix;
+  __shared__ int32_t sh_remaining;
+  __shared__ int32_t wsum[2][4];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t* key = reinterpret_cast<const uint64_t*>(norm) + static_cast<int64_t>(bh) * S;
+  if (tid == 0) {
+    sh_prefix = 0;
+    sh_remaining = nrep;
+    hdr[bh].nrep = nrep;
+  }
+  uint64_t mask = 0;
+  for (int pos = 7; pos >= 0; --pos) {
+    hist[tid] = 0;
+    __syncthreads();
+    const uint64_t prefix = sh_prefix;
+    for (int p = tid; p < S; p += 256) {
+      const uint64_t u = key[p];
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> (8 * pos)) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int32_t rem = sh_remaining, cum = 0;
+      int sel = 0;
+      for (int bin = 255; bin >= 0; --bin) {
+        if (cum + static_cast<int32_t>(hist[bin]) >= rem) {
+          sel = bin;
+          break;
+        }
+        cum += hist[bin];
+      }
+      sh_remaining = rem - cum;
+      sh_prefix = prefix | (static_cast<uint64_t>(sel) << (8 * pos));
+    }
+    mask |= 0xFFull << (8 * pos);
+    __syncthreads();
+  }
+  const uint64_t T = sh_prefix;
+  const int32_t need_eq = sh_remaining;   // keys equal to T to take, lowest positions first
+  int32_t carry_eq = 0, carry_out = 0;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t* out = rep_pos + static_cast<int64_t>(bh) * nrep_pad;
+  for (int base = 0; base < S; base += 256) {
+    const int p = base + tid;
+    const uint64_t u = p < S ? key[p] : 0;
+    const bool eq = p < S && u == T;
+    const uint64_t meq = __ballot(eq);
+    if (lane == 0) wsum[0][w] = __popcll(meq);
+    __syncthreads();
+    int32_t eq_rank = carry_eq + __popcll(meq & lt);
+    for (int j = 0; j < w; ++j) eq_rank += wsum[0][j];
+    const bool take = p < S && (u > T || (eq && eq_rank < need_eq));
+    const uint64_t mt = __ballot(take);
+    if (lane == 0) wsum[1][w] = __popcll(mt);
+    __syncthreads();
+    int32_t idx = carry_out + __popcll(mt & lt);
+    for (int j = 0; j < w; ++j) idx += wsum[1][j];
+    if (take) out[idx] = p;
+    for (int j = 0; j < 4; ++j) {
+      carry_eq += wsum[0][j];
+      carry_out += wsum[1][j];
+    }
+    __syncthreads();
+  }
+  for (int i = nrep + tid; i < nrep_pad; i += 256) out[i] = -1;
+}
+
+// Largest |e| over the repaired rows.  grid (nrep_pad/128, H, B), 128 threads.
+__global__ void __launch_bounds__(128) k_repair_eamax(TensorArg v, int S, int nrep_pad, const int32_t* perm,
+                                                      const float* v_mean, const int32_t* rep_pos, vc_head_hdr* hdr) {
+  __shared__ float red[16];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
+  const int nblk = (S + kBlock - 1) / kBlock;
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  const int p = rep_pos[static_cast<int64_t>(bh) * nrep_pad + i];
+  float m = 0.0f;
+  if (p >= 0) {
+    const int s = perm[static_cast<int64_t>(bh) * S + p];
+    const float* mu = v_mean + (static_cast<int64_t>(bh) * nblk + p / kBlock) * kD;
+    float s_v, inv;
+    v_scales(hdr[bh], &s_v, &inv);
+    for (int c8 = 0; c8 < kD; c8 += 8) {
+      float x[8], e[8];
+      load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
+      resid_err(x, mu + c8, s_v, inv, e);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(e[q]));
+    }
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0 && m > 0.0f) atomicMax(&hdr[bh].e_amax_bits, __float_as_uint(m));
+}
+
+// E4M3 repair residuals as transposed tiles (key = repair index).
+// grid (nrep_pad/128, H, B), 256 threads.
+__global__ void __launch_bounds__(256) k_repair_epack(TensorArg v, int S, int nrep_pad, const int32_t* perm,
+                                                      const float* v_mean, const int32_t* rep_pos, vc_head_hdr* hdr,
+                                                      uint8_t* rep_e8) {
+  __shared__ __align__(16) uint8_t codes[kTileBytes];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
+  const int nblk = (S + kBlock - 1) / kBlock;
+  const float a = __uint_as_float(hdr[bh].e_amax_bits);
+  const float inv_e = a > 0.0f ? 448.0f / a : 1.0f;
+  const float s_e = a > 0.0f ? a / 448.0f : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) hdr[bh].rep_scale = s_e;
+  float s_v, inv;
+  v_scales(hdr[bh], &s_v, &inv);
+  for (int t = threadIdx.x; t < kBlock * 16; t += blockDim.x) {
+    const int j = t >> 4, c8 = (t & 15) * 8;
+    const int p = rep_pos[static_cast<int64_t>(bh) * nrep_pad + blockIdx.x * kBlock + j];
+    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (p >= 0) {
+      const int s = perm[static_cast<int64_t>(bh) * S + p];
+      const float* mu = v_mean + (static_cast<int64_t>(bh) * nblk + p / kBlock) * kD;
+      float x[8], e[8];
+      load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
+      resid_err(x, mu + c8, s_v, inv, e);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) c[q] = e4m3_encode(e[q] * inv_e);
+    }
+    *reinterpret_cast<uint2*>(&codes[j * kD + c8]) =
+        make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+  }
+  __syncthreads();
+  store_tr_tile(codes, rep_e8 + (static_cast<int64_t>(bh) * (nrep_pad / kBlock) + blockIdx.x) * kTileBytes);
+}
+
+// Copy the K code rows of the repaired positions into row tiles, with their
+// block scales.  grid (nrep_pad/128, H, B), 256 threads.
+__global__ void __launch_bounds__(256) k_repair_kpack(int S, int nrep_pad, const int32_t* rep_pos, const uint8_t* k8,
+                                                      const float* k_scale, uint8_t* rep_k8, float* rep_ks) {
+  const int bh = blockIdx.z * gridDim.y + blockIdx.y;
+  const int nblk = (S + kBlock - 1) / kBlock;
+  uint8_t* dst = rep_k8 + (static_cast<int64_t>(bh) * (nrep_pad / kBlock) + blockIdx.x) * kTileBytes;
+  for (int t = threadIdx.x; t < kBlock * 8; t += blockDim.x) {
+    const int r = t >> 3, c16 = (t & 7) * 16;
+    const int i = blockIdx.x * kBlock + r;
+    const int p = rep_pos[static_cast<int64_t>(bh) * nrep_pad + i];
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (p >= 0) {
+      const uint8_t* src = k8 + (static_cast<int64_t>(bh) * nblk + p / kBlock) * kTileBytes;
+      val = *reinterpret_cast<const uint4*>(src + row_tile_off(p % kBlock, c16));
+    }
+    *reinterpret_cast<uint4*>(dst + row_tile_off(r, c16)) = val;
+    if (c16 == 0) rep_ks[static_cast<int64_t>(bh) * nrep_pad + i] = p >= 0 ? k_scale[static_cast<int64_t>(bh) * nblk + p / kBlock] : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch sequences (called from the C ABI after validation).
+#define VC_LAUNCH_CHECK()                                   \
+  do {                                                      \
+    hipError_t _e = hipGetLastError();                      \
+    if (_e != hipSuccess) return _e;                        \
+  } while (0)
+
+hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_opts& o, const WsPtrs& ws,
+                            hipStream_t st) {
+  const int BH = B * H, nblk = (S + kBlock - 1) / kBlock, k = o.k;
+  const dim3 gblk(nblk, H, B);
+  hipLaunchKernelGGL(k_fill_u32, dim3(64), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws.hdr), 0u,
+                     static_cast<int64_t>(BH) * (sizeof(vc_head_hdr) / 4));
+  VC_LAUNCH_CHECK();
+  if (o.smooth) {
+    const int nch = (S + kAsgTok - 1) / kAsgTok;
+    hipLaunchKernelGGL(k_v_absmax, dim3((S + 63) / 64, H, B), dim3(256), 0, st, v, S, ws.hdr);
+    VC_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_kmeans_init, dim3(BH), dim3(128), 0, st, v, S, H, k, o.seed, ws.hdr, ws.cent, ws.csum,
+                       ws.ccount);
+    VC_LAUNCH_CHECK();
+    const size_t sm = kmeans_assign_smem(k);
+    for (int it = 0; it < o.iters; ++it) {
+      hipLaunchKernelGGL((k_kmeans_assign<true, false>), dim3(nch, H, B), dim3(kAsgTok), sm, st, v, S, k,
+                         ws.hdr, ws.cent, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
+      VC_LAUNCH_CHECK();
+      hipLaunchKernelGGL(k_kmeans_update, dim3(BH), dim3(256), 0, st, k, ws.cent, ws.csum, ws.ccount);
+      VC_LAUNCH_CHECK();
+    }
+    hipLaunchKernelGGL((k_kmeans_assign<false, true>), dim3(nch, H, B), dim3(kAsgTok), sm, st, v, S, k, ws.hdr,
+                       ws.cent, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
+    VC_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_cluster_scan, dim3(BH), dim3(64), 0, st, S, k, ws.chunk_hist, ws.chunk_off);
+    VC_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_cluster_scatter, dim3(nch, H, B), dim3(kAsgTok), 0, st, S, k, ws.assign, ws.chunk_off,
+                       ws.perm);
+    VC_LAUNCH_CHECK();
+  } else {
+    hipLaunchKernelGGL(k_identity_perm, dim3((S + 255) / 256, H, B), dim3(256), 0, st, S, ws.assign, ws.perm);
+    VC_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(k_v_block_stats, gblk, dim3(128), 0, st, v, S, o.smooth, ws.perm, ws.v_mean, ws.hdr);
+  VC_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_v_quant_pack, gblk, dim3(256), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.v8, ws.v_meanp);
+  VC_LAUNCH_CHECK();
+  if (ws.nrep > 0) {
+    const dim3 grep(ws.nrep_pad / kBlock, H, B);
+    hipLaunchKernelGGL(k_repair_norm, gblk, dim3(128), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.rep_norm);
+    VC_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_repair_select, dim3(BH), dim3(256), 0, st, S, ws.nrep, ws.nrep_pad, ws.rep_norm,
+                       ws.rep_pos, ws.hdr);
+    VC_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_repair_eamax, grep, dim3(128), 0, st, v, S, ws.nrep_pad, ws.perm, ws.v_mean, ws.rep_pos,
+                       ws.hdr);
+    VC_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_repair_epack, grep, dim3(256), 0, st, v, S, ws.nrep_pad, ws.perm, ws.v_mean, ws.rep_pos,
+                       ws.hdr, ws.rep_e8);
+    VC_LAUNCH_CHECK();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& kt, int B, int S, int H, const WsPtrs& ws,
+                             hipStream_t st) {
+  const int nblk = (S + kBlock - 1) / kBlock;
+  const dim3 gblk(nblk, H, B);
+  hipLaunchKernelGGL((k_quant_rows<false>), gblk, dim3(256), 0, st, q, S, ws.perm, ws.q8, ws.q_scale);
+  VC_LAUNCH_CHECK();
+  hipLaunchKernelGGL((k_quant_rows<true>), gblk, dim3(256), 0, st, kt, S, ws.perm, ws.k8, ws.k_scale);
+  VC_LAUNCH_CHECK();
+  if (ws.nrep > 0) {
+    hipLaunchKernelGGL(k_repair_kpack, dim3(ws.nrep_pad / kBlock, H, B), dim3(256), 0, st, S, ws.nrep_pad,
+                       ws.rep_pos, ws.k8, ws.k_scale, ws.rep_k8, ws.rep_ks);
+    VC_LAUNCH_CHECK();
+  }
+  return hipSuccess;
+}
+
+}  // namespace vc

@@ -1,0 +1,191 @@
+/*
+ * vc.h -- C ABI of the MI355X (gfx950) VC-Attention forward library (libvc.so).
+ *
+ * VC-Attention is FP8 (OCP E4M3) non-causal multi-head attention with two
+ * additions, both defined in "VC-Attention: Value Smoothing and Softmax
+ * Casting for Low-bit Attention", section "Abstract (arXiv)":
+ *   - V-Smooth: value tokens of each (batch, head) are reordered by a light
+ *     online clustering so each 128-token block holds similar tokens; only
+ *     the residual after the block mean is quantised, and the mean is added
+ *     back from the online-softmax row sum;
+ *   - ExpCast-FP8: log-domain scores become E4M3 probability codes with one
+ *     fused multiply-add.
+ * The call shape ([B,S,H,128] or [S,H,128] FP16/BF16 in, BF16 out, head
+ * dimension 128, non-causal, per-block Q/K and per-head V scales, an optional
+ * V residual repair with a budget) follows "Open VC Attention", section
+ * "Описание" (Description).
+ *
+ * Three calls make up one forward pass, all ordered on the caller's stream:
+ *   vc_prepare_v     clustering, permutation, block means, E4M3 residual
+ *   vc_prepare_qk    per-block E4M3 quantisation of Q and of K gathered
+ *                    through the permutation of vc_prepare_v
+ *   vc_attention_fwd the fused FP8 attention kernel (any number of times on
+ *                    one prepared workspace)
+ *
+ * Memory and ownership: every pointer marked "device" is HIP device memory
+ * owned by the caller; the library never allocates or frees device memory
+ * and keeps no state between calls.  All intermediate results live in one
+ * caller-provided workspace whose size and internal offsets come from
+ * vc_workspace_layout (a host-only computation).  Descriptors and option
+ * structs are host memory, read during the call only.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  The library enqueues kernels and never synchronises; kernel
+ * faults surface at the caller's next synchronisation.
+ *
+ * Errors: every call validates its host-side arguments before it enqueues
+ * any work; on failure it returns a non-zero vc_status, enqueues nothing,
+ * and vc_last_error() returns a message (thread-local, valid until the next
+ * call on the same thread).  VC_ERR_DEVICE means a HIP call or a kernel
+ * launch failed; work already enqueued by that call may have run.
+ *
+ * Results are bit-deterministic for identical inputs and options.
+ * Non-finite inputs are undefined behaviour.
+ */
+#ifndef VC_ATTN_VC_H
+#define VC_ATTN_VC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VC_OK = 0,
+  VC_ERR_ARG = 1,          /* null pointer, bad size, bad stride or option   */
+  VC_ERR_UNSUPPORTED = 2,  /* D != 128, unsupported dtype or k, not gfx950   */
+  VC_ERR_WORKSPACE = 3,    /* workspace smaller than vc_workspace_layout's   */
+  VC_ERR_DEVICE = 4        /* HIP runtime or kernel launch failure           */
+} vc_status;
+
+typedef enum { VC_F16 = 0, VC_BF16 = 1 } vc_dtype;
+
+/* A [B,S,H,D] tensor view.  Element (b,s,h,d) is at
+ * base + b*sB + s*sS + h*sH + d (strides in elements; D is contiguous).
+ * D must be 128.  An [S,H,128] tensor is the view with B=1.
+ * Base pointers and strides*2 bytes must be 16-byte aligned. */
+typedef struct {
+  int32_t B, S, H, D;
+  int32_t dtype;           /* vc_dtype */
+  int32_t reserved;
+  int64_t sB, sS, sH;
+} vc_desc;
+
+/* V-Smooth options. */
+typedef struct {
+  int32_t smooth;          /* 1: k-means reorder + block-mean subtraction;
+                              0: identity order, no mean (plain per-head FP8 V) */
+  int32_t k;               /* clusters per (b,h): 1 <= k <= min(S, 64)         */
+  int32_t iters;           /* Lloyd iterations after the seeded init: 0..64     */
+  int32_t reserved;
+  uint64_t seed;           /* init offset: splitmix64(seed ^ (b*H+h))           */
+  float repair_budget;     /* beta in [0,1): ceil(beta*S) repaired tokens per
+                              (b,h); 0 disables repair                          */
+  float reserved2;
+} vc_v_opts;
+
+/* Attention options. */
+typedef struct {
+  float sm_scale;          /* softmax scale > 0; 0 selects fp32(1/sqrt(128))   */
+  int32_t reserved;
+} vc_attn_opts;
+
+/* Byte offsets of the workspace regions (all 256-byte aligned).  Per (b,h)
+ * index bh = b*H + h; nblk = ceil(S/128); Sp = 128*nblk; nrep = ceil(beta*S);
+ * nrep_pad = 128*ceil(nrep/128).
+ *   q8      u8  [BH][nblk] tiles of 16384 B: Q codes, original token order
+ *   q_scale f32 [BH][nblk]
+ *   k8      u8  [BH][nblk] tiles: K codes, PERMUTED order (row p = token perm[p])
+ *   k_scale f32 [BH][nblk]
+ *   v8      u8  [BH][nblk] tiles: residual codes, permuted order, transposed
+ *   v_mean  f32 [BH][nblk][128] block means mu_b
+ *   v_meanp f32 [BH][nblk][128] mu_b / s_v
+ *   hdr     per-(b,h) scalars, vc_head_hdr [BH]
+ *   assign  i32 [BH][S] cluster id of each ORIGINAL token
+ *   perm    i32 [BH][S] original token at permuted position p
+ *   rep_pos i32 [BH][nrep_pad] repaired permuted positions, ascending; pad -1
+ *   rep_k8  u8  [BH][nrep_pad/128] tiles: K codes of the repaired positions
+ *   rep_ks  f32 [BH][nrep_pad] K block scale of each repaired position
+ *   rep_e8  u8  [BH][nrep_pad/128] tiles: E4M3 residual error, transposed
+ *   scratch     internal (k-means state, sort counters, repair scores)
+ * Tile formats (16384 B, 128 rows x 128 columns of codes):
+ *   row tile (q8, k8, rep_k8): the byte for (row r, column d) is at
+ *     ((((r/16)*2 + (d%32)/16)*64 + (r%16) + 16*(d/32)) * 16) + d%16
+ *   transposed tile (v8, rep_e8): the byte for (key j, channel d) is at
+ *     ((((d/16)*2 + i/16)*64 + (d%16) + 16*g) * 16) + i%16,
+ *     with g = (j%16)/4 and i = 4*(j/16) + j%4.
+ */
+typedef struct {
+  size_t total;
+  size_t q8, q_scale, k8, k_scale, v8, v_mean, v_meanp, hdr;
+  size_t assign, perm, rep_pos, rep_k8, rep_ks, rep_e8, scratch;
+  int32_t nblk, nrep, nrep_pad, reserved;
+} vc_ws_layout;
+
+/* Per-(b,h) scalars in the workspace's hdr region. */
+typedef struct {
+  float v_scale;           /* s_v = a_R/448 (1 if a_R == 0)                     */
+  float v_inv;             /* 448/a_R (1 if a_R == 0)                           */
+  uint32_t v_amax_bits;    /* max|v| (float bits) over the head                 */
+  uint32_t r_amax_bits;    /* a_R = max|R| (float bits) over the head           */
+  int32_t shift;           /* k-means sketch scaling exponent                   */
+  int32_t nrep;            /* repaired tokens for this head                     */
+  float rep_scale;         /* s_e = a_e/448 (1 if a_e == 0)                     */
+  uint32_t e_amax_bits;    /* a_e (float bits)                                  */
+} vc_head_hdr;
+
+/* Host only: workspace size and offsets for a V descriptor and options.
+ * Only B, S, H (and k, repair_budget) matter.  Returns VC_ERR_ARG or
+ * VC_ERR_UNSUPPORTED on invalid shapes/options. */
+vc_status vc_workspace_layout(const vc_desc* vd, const vc_v_opts* opts, vc_ws_layout* out);
+
+/* V-Smooth prepare ("VC-Attention: Value Smoothing and Softmax Casting for
+ * Low-bit Attention", Abstract; "Nunchux AI lanza VC-Attention kernel ..."
+ * paragraph 2: k-means per batch and head, mean of each 128-token block
+ * subtracted, E4M3 residual; "Open VC Attention", Description: per-head V
+ * scale, residual repair with a budget).
+ *   vd, v   : V view (device), fp16/bf16, D == 128
+ *   opts    : V-Smooth options (host)
+ *   ws      : workspace (device), ws_bytes >= layout.total
+ * Writes assign, perm, v8, v_mean, v_meanp, hdr and the repair set. */
+vc_status vc_prepare_v(const vc_desc* vd, const void* v, const vc_v_opts* opts,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Q/K prepare ("Open VC Attention", Description: per-block Q/K scales).
+ * Q is quantised in its original order; K is gathered through perm (written
+ * by vc_prepare_v on the same workspace, earlier on the same stream) so that
+ * keys and values stay paired.  Per 128-token block: scale = amax/448,
+ * code = E4M3(x * (448/amax)).  qd and kd must agree on B, S, H, D. */
+vc_status vc_prepare_qk(const vc_desc* qd, const void* q, const vc_desc* kd, const void* k,
+                        const vc_v_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/* Fused attention ("VC-Attention: Value Smoothing and Softmax Casting for
+ * Low-bit Attention", Abstract; "Hugging Face Introduces VC-Attention ...",
+ * Technical Breakthroughs and Core Innovations).  For every query and every
+ * 128-key tile in ascending order: FP8 MFMA scores, integer log2 running
+ * maximum, ExpCast E4M3 probability codes, row sum, exact power-of-two
+ * rescale, FP8 MFMA P.V, block-mean restore; then the repair tiles; output
+ * out = (s_v*O + s_e*O_rep)/l rounded to bf16.
+ *   od      : output view (device memory `out`), dtype must be VC_BF16, same
+ *             B, S, H as the prepared inputs; rows stay in the original
+ *             query order
+ *   opts    : the V options the workspace was prepared with
+ *   aopts   : may be NULL (defaults)
+ *   ws      : a workspace prepared by vc_prepare_v and vc_prepare_qk */
+vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts,
+                           const vc_attn_opts* aopts, const void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Static strings; never NULL. */
+const char* vc_status_string(vc_status s);
+const char* vc_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* vc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VC_ATTN_VC_H */

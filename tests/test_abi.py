@@ -1,0 +1,193 @@
+"""C-ABI checks that need no GPU: exports, struct layout, host-side validation.
+
+Every call here fails validation before the library touches the device, so
+these run on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import bit_attention_video_vc_amd as vc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(vc.lib_path), reason="libvc.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(vc_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(vc.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = vc.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", vc.lib_path], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+    assert vc.lib().vc_version().decode().count(".") == 2
+
+
+def test_struct_layouts_match_c_compiler():
+    structs = {"vc_desc": vc.VcDesc, "vc_v_opts": vc.VcVOpts, "vc_attn_opts": vc.VcAttnOpts,
+               "vc_ws_layout": vc.VcWsLayout, "vc_head_hdr": vc.VcHeadHdr}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "vc.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("  return 0; }")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write("\n".join(lines))
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    for line in out.splitlines():
+        cname, field, val = line.split()
+        py = structs[cname]
+        got = ctypes.sizeof(py) if field == "sizeof" else getattr(py, field).offset
+        assert got == int(val), (cname, field, got, val)
+
+
+def _desc(B=1, S=256, H=2, D=128, dtype=vc.VC_BF16, sS=None):
+    sH = 128
+    sS = H * 128 if sS is None else sS
+    return vc.VcDesc(B, S, H, D, dtype, 0, S * sS, sS, sH)
+
+
+def _status(fn, *args):
+    return getattr(vc.lib(), fn)(*args)
+
+
+def _layout(d, o):
+    out = vc.VcWsLayout()
+    return _status("vc_workspace_layout", ctypes.byref(d), ctypes.byref(o), ctypes.byref(out)), out
+
+
+def test_layout_regions_are_disjoint_and_sized():
+    d = _desc(B=2, S=300, H=3)
+    o = vc.v_opts(True, 4, 2, 0, 0.05)
+    st, L = _layout(d, o)
+    assert st == vc.VC_OK
+    BH, nblk = 6, 3
+    # ceil(beta*S) with beta's fp32 value: fp32(0.05) = 0.0500000007..., so 300 tokens -> 16
+    assert L.nblk == nblk and L.nrep == 16 and L.nrep_pad == 128
+    need = {"q8": BH * nblk * 16384, "q_scale": 4 * BH * nblk, "k8": BH * nblk * 16384, "k_scale": 4 * BH * nblk,
+            "v8": BH * nblk * 16384, "v_mean": 4 * BH * nblk * 128, "v_meanp": 4 * BH * nblk * 128,
+            "hdr": 32 * BH, "assign": 4 * BH * 300, "perm": 4 * BH * 300, "rep_pos": 4 * BH * 128,
+            "rep_k8": BH * 128 * 128, "rep_ks": 4 * BH * 128, "rep_e8": BH * 128 * 128}
+    spans = sorted((getattr(L, k), getattr(L, k) + v, k) for k, v in need.items())
+    for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
+        assert a1 <= b0, (ka, kb)
+    assert spans[-1][1] <= L.scratch < L.total
+    assert all(getattr(L, k) % 256 == 0 for k in need)
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(D=64), vc.VC_ERR_UNSUPPORTED),
+    (dict(S=0), vc.VC_ERR_ARG),
+    (dict(B=0), vc.VC_ERR_ARG),
+    (dict(H=0), vc.VC_ERR_ARG),
+    (dict(dtype=7), vc.VC_ERR_UNSUPPORTED),
+    (dict(sS=129), vc.VC_ERR_ARG),
+])
+def test_layout_rejects_bad_descriptors(mut, code):
+    d = _desc(**mut)
+    st, _ = _layout(d, vc.v_opts(True, 2, 1))
+    assert st == code
+    assert vc.lib().vc_last_error().decode()
+
+
+@pytest.mark.parametrize("opts,code", [
+    (vc.v_opts(True, 0, 1), vc.VC_ERR_ARG),
+    (vc.v_opts(True, 300, 1), vc.VC_ERR_ARG),        # k > S
+    (vc.v_opts(True, 65, 1), vc.VC_ERR_UNSUPPORTED),
+    (vc.v_opts(True, 4, -1), vc.VC_ERR_ARG),
+    (vc.v_opts(True, 4, 1, 0, 1.0), vc.VC_ERR_ARG),
+    (vc.v_opts(True, 4, 1, 0, -0.1), vc.VC_ERR_ARG),
+    (vc.v_opts(True, 4, 1, 0, float("nan")), vc.VC_ERR_ARG),
+])
+def test_layout_rejects_bad_options(opts, code):
+    st, _ = _layout(_desc(S=256), opts)
+    assert st == code
+
+
+def test_smooth_off_ignores_k():
+    st, _ = _layout(_desc(S=256), vc.v_opts(False, 0, -5))
+    assert st == vc.VC_OK
+
+
+FAKE = ctypes.c_void_p(0x100000)          # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+def test_prepare_v_validation_paths():
+    d = _desc(S=256)
+    o = vc.v_opts(True, 4, 1)
+    _, L = _layout(d, o)
+    L_ = vc.lib()
+    st = L_.vc_prepare_v(ctypes.byref(d), None, ctypes.byref(o), FAKE, L.total, None)
+    assert st == vc.VC_ERR_ARG
+    st = L_.vc_prepare_v(ctypes.byref(d), MISALIGNED, ctypes.byref(o), FAKE, L.total, None)
+    assert st == vc.VC_ERR_ARG and "aligned" in L_.vc_last_error().decode()
+    st = L_.vc_prepare_v(ctypes.byref(d), FAKE, ctypes.byref(o), FAKE, L.total - 1, None)
+    assert st == vc.VC_ERR_WORKSPACE
+    st = L_.vc_prepare_v(ctypes.byref(d), FAKE, ctypes.byref(o), None, L.total, None)
+    assert st == vc.VC_ERR_ARG
+    st = L_.vc_prepare_v(ctypes.byref(d), FAKE, ctypes.byref(o), ctypes.c_void_p(0x100010), L.total, None)
+    assert st == vc.VC_ERR_ARG                    # workspace not 256-byte aligned
+    st = L_.vc_prepare_v(None, FAKE, ctypes.byref(o), FAKE, L.total, None)
+    assert st == vc.VC_ERR_ARG
+
+
+def test_prepare_qk_validation_paths():
+    d = _desc(S=256)
+    d2 = _desc(S=255)
+    o = vc.v_opts(True, 4, 1)
+    _, L = _layout(d, o)
+    L_ = vc.lib()
+    assert L_.vc_prepare_qk(ctypes.byref(d), FAKE, ctypes.byref(d2), FAKE, ctypes.byref(o), FAKE, L.total,
+                            None) == vc.VC_ERR_ARG
+    assert L_.vc_prepare_qk(ctypes.byref(d), FAKE, ctypes.byref(d), None, ctypes.byref(o), FAKE, L.total,
+                            None) == vc.VC_ERR_ARG
+    assert L_.vc_prepare_qk(ctypes.byref(d), FAKE, ctypes.byref(d), FAKE, ctypes.byref(o), FAKE, 10,
+                            None) == vc.VC_ERR_WORKSPACE
+
+
+def test_attention_fwd_validation_paths():
+    d = _desc(S=256)
+    o = vc.v_opts(True, 4, 1)
+    _, L = _layout(d, o)
+    L_ = vc.lib()
+    a = vc.VcAttnOpts(0.0, 0)
+    f16 = _desc(S=256, dtype=vc.VC_F16)
+    assert L_.vc_attention_fwd(ctypes.byref(f16), FAKE, ctypes.byref(o), ctypes.byref(a), FAKE, L.total,
+                               None) == vc.VC_ERR_UNSUPPORTED
+    bad = vc.VcAttnOpts(-1.0, 0)
+    assert L_.vc_attention_fwd(ctypes.byref(d), FAKE, ctypes.byref(o), ctypes.byref(bad), FAKE, L.total,
+                               None) == vc.VC_ERR_ARG
+    inf = vc.VcAttnOpts(float("inf"), 0)
+    assert L_.vc_attention_fwd(ctypes.byref(d), FAKE, ctypes.byref(o), ctypes.byref(inf), FAKE, L.total,
+                               None) == vc.VC_ERR_ARG
+    assert L_.vc_attention_fwd(ctypes.byref(d), FAKE, ctypes.byref(o), ctypes.byref(a), FAKE, 0,
+                               None) == vc.VC_ERR_WORKSPACE
+
+
+def test_status_strings():
+    L_ = vc.lib()
+    assert L_.vc_status_string(vc.VC_OK) == b"VC_OK"
+    assert L_.vc_status_string(vc.VC_ERR_WORKSPACE) == b"VC_ERR_WORKSPACE"
+    assert L_.vc_status_string(99) == b"VC_ERR_UNKNOWN"
