@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--seq", type=int, default=None, help="override S")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for scaling HBM byte counters) and exit")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_fwd_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -93,6 +95,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes device to device")
+        return 0
     kw = {}
     if args.heads is not None:
         kw["H"] = args.heads

@@ -32,6 +32,12 @@ HIP_FLAGS = [
 ]
 
 
+# Extra flags per source.  The attention kernel is NaN-free by construction
+# (finite inputs, no infinities used as sentinels), so fmaxf needs no
+# IEEE-mode canonicalisation of MFMA results.
+PER_FILE_FLAGS = {"vc_attn.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -41,17 +47,29 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    objs = []
+    for src in srcs:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *compile_flags, *PER_FILE_FLAGS.get(os.path.basename(src), []), *inc, "-c", src, "-o", obj]
+        _run(cmd, verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp, *srcs]
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd))
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libvc.so")
-    os.replace(tmp, LIB)
-    return LIB
 
 
 if __name__ == "__main__":

@@ -64,6 +64,18 @@ __device__ __forceinline__ v8i ld_op_global(const uint8_t* base, int sub, int la
   return r;
 }
 
+// Copy one 16 KB tile from global memory straight into LDS: each of the 4
+// instructions moves 16 bytes per lane; the LDS destination of lane i is
+// base + 16*i, so the tile lands in the same linear order.
+__device__ __forceinline__ void tile_to_lds(const uint8_t* src, uint8_t* dst, int tid) {
+  const int w = tid >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(src + (j * kAttnThreads + tid) * 16),   // global source
+        (__attribute__((address_space(3))) void*)(dst + j * 4096 + w * 1024), 16, 0, 0);         // LDS base
+}
+
 // ExpCast of one 16x16 accumulator (4 keys per lane) into one packed dword.
 __device__ __forceinline__ uint32_t expcast4(const v4f& s, float s8, float c) {
   uint32_t w = 0;
@@ -76,9 +88,228 @@ __device__ __forceinline__ uint32_t expcast4(const v4f& s, float s8, float c) {
 
 __device__ __forceinline__ float max4(const v4f& s) { return fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])); }
 
+// Large finite stand-in for -infinity (the kernel is built without NaN/IEEE
+// canonicalisation, so it avoids infinities altogether).
+constexpr float kNegBig = -3.0e38f;
+
+// Per-wave online-softmax state for two 16-query sub-tiles.
+struct SoftState {
+  float M[2];      // integer log2 running maximum (kNegBig before the first tile)
+  float l[2];      // running row sum
+};
+
+// Score tile of one 128-key block against this wave's two query sub-tiles.
+// K operands are read from LDS two sub-tiles ahead of their MFMAs.  When
+// vt is given, the first two V operands of the P.V product that follows are
+// read during the last steps (they sit in another buffer).
+__device__ __forceinline__ void score_tile(const uint8_t* ktile, int lane, const v8i (&qop)[2], v4f (&sc)[8][2],
+                                           const uint8_t* vt = nullptr, v8i* vop = nullptr) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  v8i kop[2];
+  kop[0] = ld_op_lds(ktile, 0, lane);
+  kop[1] = ld_op_lds(ktile, 1, lane);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const v8i cur = kop[t & 1];
+    sc[t][0] = mfma_fp8(cur, qop[0], zero);
+    sc[t][1] = mfma_fp8(cur, qop[1], zero);
+    if (t + 2 < 8) {
+      kop[t & 1] = ld_op_lds(ktile, t + 2, lane);
+    } else if (vt != nullptr) {
+      vop[t - 6] = ld_op_lds(vt, t - 6, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Mask keys >= kval in a ragged last tile (lane group g holds keys 16t+4g+i).
+__device__ __forceinline__ void mask_tile(v4f (&sc)[8][2], int g, int kval) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (16 * t + 4 * g + i >= kval) sc[t][0][i] = sc[t][1][i] = kNegBig;
+}
+
+// Integer running max, rescale factor and ExpCast codes for one tile.
+__device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma, SoftState& st, float (&alpha)[2],
+                                             v8i (&P)[2]) {
+  const float s8 = 8.0f * sigma;
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    float mx = max4(sc[0][qi]);
+#pragma unroll
+    for (int t = 1; t < 8; ++t) mx = fmaxf(mx, max4(sc[t][qi]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(st.M[qi], ceilf(mx * sigma));
+    alpha[qi] = st.M[qi] == kNegBig ? 0.0f : ldexpf(1.0f, static_cast<int>(fmaxf(st.M[qi] - mn, -160.0f)));
+    st.M[qi] = mn;
+    const float c = 120.0f - 8.0f * mn;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) P[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, c));
+  }
+}
+
+// Loop-invariant inputs of one workgroup's tile loop.
+struct TileCtx {
+  const uint8_t* kbase;     // this head's K8 tiles
+  const uint8_t* vbase;     // this head's V8 tiles
+  const float* mbase;       // this head's mu/s_v, restore-operand order
+  const float* __restrict__ ks;   // this head's K block scales (read-only: scalar loads)
+  float sqs, sm_scale;
+  int nblk, kval_last, tid, lane, g, l16;
+};
+
+// Per-wave accumulators carried across tiles.
+struct TileAcc {
+  v4f O[8][2];     // O^T: lane holds channels 16dt+4g+i of query l16 (+16 per sub-tile)
+  v8i P[2];        // E4M3 codes of the current tile (P^T operand)
+  float rb[2];     // restore batch: lane group g holds the row sum of tile 4*batch+g
+  float mu[8];     // restore operand: lane group g holds mu/s_v of tile 4*batch+g
+  float ks_next;   // K scale of tile kb+1 (loaded during step kb-1)
+  SoftState st;
+};
+
+// mu/s_v of tile t for the restore operand: lanes of group t%4 keep channel
+// 16*dt + l16 at mu[dt]; the other lanes keep what they hold.
+__device__ __forceinline__ void load_mu_row(const float* mbase, int t, int nblk, int g, int l16, float (&mu)[8]) {
+  if (t < nblk && g == (t & 3)) {
+    const float4* mp = reinterpret_cast<const float4*>(mbase + static_cast<int64_t>(t) * kD + l16 * 8);
+    const float4 m0 = mp[0], m1 = mp[1];
+    mu[0] = m0.x; mu[1] = m0.y; mu[2] = m0.z; mu[3] = m0.w;
+    mu[4] = m1.x; mu[5] = m1.y; mu[6] = m1.z; mu[7] = m1.w;
+  }
+}
+
+__device__ __forceinline__ bool flush_step(int kb, int nblk) { return (kb & 3) == 3 || kb + 1 >= nblk; }
+
+// One tile step kb: scores of tile kb+1 (K in kcur), P.V of tile kb (V in
+// vcur) interleaved with tile kb+1's softmax, block-mean restore, rescale,
+// and the loads of K(kb+2) into kfree and V(kb+1) into vfree.  The four LDS
+// buffers are distinct arrays, so these loads overlap with the reads of this
+// step; they are waited for at the closing barrier.
+__device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
+                                          const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2],
+                                          const uint8_t* ones_lds, TileAcc& acc) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int nblk = c.nblk, lane = c.lane, g = c.g;
+  const bool has_next = kb + 1 < nblk;
+  // No vector load issued in this step is consumed in it (the vector-memory
+  // counter retires in order, so such a wait would also wait for the next
+  // tile): the next tile's restore row and K scale are loaded at the end of
+  // the step and retired by the closing barrier.
+  const bool flush = flush_step(kb, nblk);
+  const float ks_next = acc.ks_next;
+  if (kb + 2 < nblk) tile_to_lds(c.kbase + static_cast<int64_t>(kb + 2) * kTileBytes, kfree, c.tid);
+  if (has_next) tile_to_lds(c.vbase + static_cast<int64_t>(kb + 1) * kTileBytes, vfree, c.tid);
+
+  v8i Pn[2];
+  float alpha[2] = {1.0f, 1.0f};
+  if (has_next) {
+    v4f sc[8][2];
+    v8i vop[2];
+    score_tile(kcur, lane, qop, sc, vcur, vop);
+    if (kb + 2 == nblk && c.kval_last < kBlock) mask_tile(sc, g, c.kval_last);
+    const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
+    const float s8 = 8.0f * sigma;
+    // P.V of tile kb on the matrix core, hand-interleaved with tile kb+1's
+    // softmax on the VALU: step dt issues V^T sub-tile dt's two MFMAs with a
+    // fixed slice of the max / ExpCast work between them.
+    float mx[2], cq[2];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const v8i vc = vop[dt & 1];
+      acc.O[dt][0] = mfma_fp8(vc, acc.P[0], acc.O[dt][0]);
+      if (dt < 2) {
+        mx[dt] = fmaxf(fmaxf(max4(sc[0][dt]), max4(sc[1][dt])), fmaxf(max4(sc[2][dt]), max4(sc[3][dt])));
+      } else {
+        const int c0 = 2 * (dt - 2);
+        Pn[c0 & 1][c0 >> 1] = static_cast<int>(expcast4(sc[c0 >> 1][c0 & 1], s8, cq[c0 & 1]));
+        if (dt >= 6) {
+          const int c2 = 12 + 2 * (dt - 6);
+          Pn[c2 & 1][c2 >> 1] = static_cast<int>(expcast4(sc[c2 >> 1][c2 & 1], s8, cq[c2 & 1]));
+        }
+      }
+      acc.O[dt][1] = mfma_fp8(vc, acc.P[1], acc.O[dt][1]);
+      if (dt < 2) {
+        mx[dt] = fmaxf(mx[dt], fmaxf(fmaxf(max4(sc[4][dt]), max4(sc[5][dt])), fmaxf(max4(sc[6][dt]), max4(sc[7][dt]))));
+        mx[dt] = fmaxf(mx[dt], __shfl_xor(mx[dt], 16, 64));
+        mx[dt] = fmaxf(mx[dt], __shfl_xor(mx[dt], 32, 64));
+        if (dt == 1) {
+#pragma unroll
+          for (int qi = 0; qi < 2; ++qi) {
+            const float mn = fmaxf(acc.st.M[qi], ceilf(mx[qi] * sigma));
+            alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn, -160.0f)));
+            acc.st.M[qi] = mn;
+            cq[qi] = 120.0f - 8.0f * mn;
+          }
+        }
+      } else {
+        const int c1 = 2 * (dt - 2) + 1;
+        Pn[c1 & 1][c1 >> 1] = static_cast<int>(expcast4(sc[c1 >> 1][c1 & 1], s8, cq[c1 & 1]));
+        if (dt >= 6) {
+          const int c3 = 13 + 2 * (dt - 6);
+          Pn[c3 & 1][c3 >> 1] = static_cast<int>(expcast4(sc[c3 >> 1][c3 & 1], s8, cq[c3 & 1]));
+        }
+      }
+      if (dt + 2 < 8) vop[dt & 1] = ld_op_lds(vcur, dt + 2, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const v8i vop = ld_op_lds(vcur, dt, lane);
+      acc.O[dt][0] = mfma_fp8(vop, acc.P[0], acc.O[dt][0]);
+      acc.O[dt][1] = mfma_fp8(vop, acc.P[1], acc.O[dt][1]);
+    }
+  }
+
+  // flush the restore batch after its last tile (or the last tile overall):
+  // O^T += (mu/s_v)^T (16 d x 4 tiles) . rb  with v_mfma_f32_16x16x4_f32
+  if (flush) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      acc.O[dt][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(acc.mu[dt], acc.rb[0], acc.O[dt][0], 0, 0, 0);
+      acc.O[dt][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(acc.mu[dt], acc.rb[1], acc.O[dt][1], 0, 0, 0);
+    }
+    acc.rb[0] = acc.rb[1] = 0.0f;
+  }
+  // restore row of tile kb+1 (after this step's flush has used the slot) and
+  // the K scale of tile kb+2
+  load_mu_row(c.mbase, kb + 1, nblk, g, c.l16, acc.mu);
+  if (kb + 2 < nblk) acc.ks_next = c.ks[kb + 2];
+
+  if (has_next) {
+    if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        acc.st.l[qi] *= alpha[qi];
+        acc.rb[qi] *= alpha[qi];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc.O[dt][qi] *= alpha[qi];
+      }
+    }
+    const int gnext = (kb + 1) & 3;
+    const v8i ones = ld_op_lds(ones_lds, 0, lane);
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      const float r = mfma_fp8(ones, Pn[qi], zero)[0];
+      acc.st.l[qi] += r;
+      acc.rb[qi] = g == gnext ? r : acc.rb[qi];
+      acc.P[qi] = Pn[qi];
+    }
+  }
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
-  __shared__ __align__(16) uint8_t kv[2][2][kTileBytes];   // [buffer][K, V]
-  __shared__ __align__(16) float mus[2][kD];
+  // four distinct arrays: a load into one provably does not alias reads of another
+  __shared__ __align__(16) uint8_t kbuf0[kTileBytes];
+  __shared__ __align__(16) uint8_t kbuf1[kTileBytes];
+  __shared__ __align__(16) uint8_t vbuf0[kTileBytes];
+  __shared__ __align__(16) uint8_t vbuf1[kTileBytes];
+  __shared__ __align__(16) uint8_t ones_lds[2048];   // E4M3 1.0 operand for the row sums
 
   // XCD-aware order: hardware deals workgroup ids round-robin over 8 XCDs;
   // give XCD x a contiguous range of (head, query-block) work items.
@@ -94,148 +325,70 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
   const int g = lane >> 4, l16 = lane & 15;
   const int S = a.S;
 
-  // Q^T operands for this wave's two 16-query sub-tiles (kept in registers)
+  TileCtx c;
+  c.kbase = a.k8 + static_cast<int64_t>(bh) * nblk * kTileBytes;
+  c.vbase = a.v8 + static_cast<int64_t>(bh) * nblk * kTileBytes;
+  c.mbase = a.v_meanp + static_cast<int64_t>(bh) * nblk * kD;
+  c.ks = a.k_scale + static_cast<int64_t>(bh) * nblk;
+  c.sqs = a.q_scale[static_cast<int64_t>(bh) * nblk + qb];
+  c.sm_scale = a.sm_scale;
+  c.nblk = nblk;
+  c.kval_last = S - (nblk - 1) * kBlock;          // real keys in the last tile
+  c.tid = tid;
+  c.lane = lane;
+  c.g = g;
+  c.l16 = l16;
+  const float sqs = c.sqs;
+
   const uint8_t* qtile = a.q8 + (static_cast<int64_t>(bh) * nblk + qb) * kTileBytes;
   v8i qop[2];
   qop[0] = ld_op_global(qtile, 2 * w, lane);
   qop[1] = ld_op_global(qtile, 2 * w + 1, lane);
-  const float s_q = a.q_scale[static_cast<int64_t>(bh) * nblk + qb];
-  const float* ks = a.k_scale + static_cast<int64_t>(bh) * nblk;
 
-  v8i ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0
+  for (int i = tid; i < 2048 / 4; i += kAttnThreads) reinterpret_cast<uint32_t*>(ones_lds)[i] = 0x38383838u;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  float M[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.0f, 0.0f};
-  v4f O[8][2];
+  TileAcc acc;
+  acc.st.M[0] = acc.st.M[1] = kNegBig;
+  acc.st.l[0] = acc.st.l[1] = 0.0f;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt][0] = O[dt][1] = zero;
+  for (int dt = 0; dt < 8; ++dt) acc.O[dt][0] = acc.O[dt][1] = zero;
+  acc.rb[0] = acc.rb[1] = 0.0f;
 
-  const uint8_t* kbase = a.k8 + static_cast<int64_t>(bh) * nblk * kTileBytes;
-  const uint8_t* vbase = a.v8 + static_cast<int64_t>(bh) * nblk * kTileBytes;
-  const float* mbase = a.v_meanp + static_cast<int64_t>(bh) * nblk * kD;
-
-  // staging registers for the next K/V tile and its block means
-  uint4 stk0, stk1, stk2, stk3, stv0, stv1, stv2, stv3;
-  float4 stm = make_float4(0, 0, 0, 0);
-#define VC_GLOAD(kb_)                                                                               \
-  do {                                                                                              \
-    const uint4* ksrc_ = reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kb_) * kTileBytes); \
-    const uint4* vsrc_ = reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(kb_) * kTileBytes); \
-    stk0 = ksrc_[tid];                                                                              \
-    stk1 = ksrc_[tid + kAttnThreads];                                                               \
-    stk2 = ksrc_[tid + 2 * kAttnThreads];                                                           \
-    stk3 = ksrc_[tid + 3 * kAttnThreads];                                                           \
-    stv0 = vsrc_[tid];                                                                              \
-    stv1 = vsrc_[tid + kAttnThreads];                                                               \
-    stv2 = vsrc_[tid + 2 * kAttnThreads];                                                           \
-    stv3 = vsrc_[tid + 3 * kAttnThreads];                                                           \
-    if (tid < kD / 4) stm = reinterpret_cast<const float4*>(mbase + static_cast<int64_t>(kb_) * kD)[tid]; \
-  } while (0)
-#define VC_LSTORE(buf_)                                                                             \
-  do {                                                                                              \
-    uint4* kd_ = reinterpret_cast<uint4*>(kv[buf_][0]);                                             \
-    uint4* vd_ = reinterpret_cast<uint4*>(kv[buf_][1]);                                             \
-    kd_[tid] = stk0;                                                                                \
-    kd_[tid + kAttnThreads] = stk1;                                                                 \
-    kd_[tid + 2 * kAttnThreads] = stk2;                                                             \
-    kd_[tid + 3 * kAttnThreads] = stk3;                                                             \
-    vd_[tid] = stv0;                                                                                \
-    vd_[tid + kAttnThreads] = stv1;                                                                 \
-    vd_[tid + 2 * kAttnThreads] = stv2;                                                             \
-    vd_[tid + 3 * kAttnThreads] = stv3;                                                             \
-    if (tid < kD / 4) reinterpret_cast<float4*>(mus[buf_])[tid] = stm;                              \
-  } while (0)
-
-  VC_GLOAD(0);
-  VC_LSTORE(0);
+  // ---- prologue: K(0), V(0), K(1) into LDS; scores and codes of tile 0 ----
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc.mu[i] = 0.0f;
+  load_mu_row(c.mbase, 0, nblk, g, l16, acc.mu);
+  acc.ks_next = nblk > 1 ? c.ks[1] : 1.0f;
+  tile_to_lds(c.kbase, kbuf0, tid);
+  tile_to_lds(c.vbase, vbuf0, tid);
+  if (nblk > 1) tile_to_lds(c.kbase + kTileBytes, kbuf1, tid);
   __syncthreads();
-
-  for (int kb = 0; kb < nblk; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nblk) VC_GLOAD(kb + 1);
-
-    // ---- scores S^T = K . Q^T (16 MFMAs) ----
+  {
     v4f sc[8][2];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const v8i kop = ld_op_lds(kv[buf][0], t, lane);
-      sc[t][0] = mfma_fp8(kop, qop[0], zero);
-      sc[t][1] = mfma_fp8(kop, qop[1], zero);
-    }
-    if ((kb + 1) * kBlock > S) {            // ragged last tile: mask padded keys
-      const int kval = S - kb * kBlock;
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * t + 4 * g + i >= kval) sc[t][0][i] = sc[t][1][i] = -INFINITY;
-    }
-    const float sigma = ((s_q * ks[kb]) * a.sm_scale) * kLog2e;
-    const float s8 = 8.0f * sigma;
-
-    // ---- integer running max, rescale, ExpCast ----
-    v8i P[2];
+    score_tile(kbuf0, lane, qop, sc);
+    if (nblk == 1 && c.kval_last < kBlock) mask_tile(sc, g, c.kval_last);
     float alpha[2];
+    softmax_tile(sc, ((sqs * c.ks[0]) * a.sm_scale) * kLog2e, acc.st, alpha, acc.P);
+    const v8i ones = ld_op_lds(ones_lds, 0, lane);
 #pragma unroll
     for (int qi = 0; qi < 2; ++qi) {
-      float mx = max4(sc[0][qi]);
-#pragma unroll
-      for (int t = 1; t < 8; ++t) mx = fmaxf(mx, max4(sc[t][qi]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(M[qi], ceilf(mx * sigma));
-      alpha[qi] = M[qi] == -INFINITY ? 0.0f : ldexpf(1.0f, static_cast<int>(fmaxf(M[qi] - mn, -160.0f)));
-      M[qi] = mn;
-      const float c = 120.0f - 8.0f * mn;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) P[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, c));
+      const float r = mfma_fp8(ones, acc.P[qi], zero)[0];
+      acc.st.l[qi] = r;
+      acc.rb[qi] = g == 0 ? r : 0.0f;
     }
-    if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
-#pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
-        l[qi] *= alpha[qi];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) O[dt][qi] *= alpha[qi];
-      }
-    }
+  }
+  __syncthreads();   // kbuf0 (K(0)) is refilled with K(2) in the first step
 
-    // ---- row sums on the matrix core: ones(16x128) . P^T ----
-    float r[2];
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
-      const v4f rs = mfma_fp8(ones, P[qi], zero);
-      r[qi] = rs[0];
-      l[qi] += r[qi];
-    }
-
-    // ---- O^T += V^T . P^T (16 MFMAs) and block-mean restore ----
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const v8i vop = ld_op_lds(kv[buf][1], dt, lane);
-      O[dt][0] = mfma_fp8(vop, P[0], O[dt][0]);
-      O[dt][1] = mfma_fp8(vop, P[1], O[dt][1]);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const float4 mu = *reinterpret_cast<const float4*>(&mus[buf][16 * dt + 4 * g]);
-#pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
-        O[dt][qi][0] = fmaf(r[qi], mu.x, O[dt][qi][0]);
-        O[dt][qi][1] = fmaf(r[qi], mu.y, O[dt][qi][1]);
-        O[dt][qi][2] = fmaf(r[qi], mu.z, O[dt][qi][2]);
-        O[dt][qi][3] = fmaf(r[qi], mu.w, O[dt][qi][3]);
-      }
-    }
-
-    if (kb + 1 < nblk) VC_LSTORE(buf ^ 1);
-    __syncthreads();
+  // Even steps read K(kb+1) from kbuf1 and V(kb) from vbuf0, and refill kbuf0
+  // and vbuf1; odd steps the other way round.
+  for (int kb = 0; kb < nblk; kb += 2) {
+    tile_step(c, kb, kbuf1, kbuf0, vbuf0, vbuf1, qop, ones_lds, acc);
+    if (kb + 1 < nblk) tile_step(c, kb + 1, kbuf0, kbuf1, vbuf1, vbuf0, qop, ones_lds, acc);
   }
 
-#undef VC_GLOAD
-#undef VC_LSTORE
+  SoftState& st = acc.st;
+  v4f (&O)[8][2] = acc.O;
   const vc_head_hdr hd = a.hdr[bh];
 
   // ---- residual repair tiles (codes against the final maximum) ----
@@ -245,9 +398,8 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
     const uint8_t* rk = a.rep_k8 + static_cast<int64_t>(bh) * a.nrep_pad * kD;
     const uint8_t* re = a.rep_e8 + static_cast<int64_t>(bh) * a.nrep_pad * kD;
     const float* rks = a.rep_ks + static_cast<int64_t>(bh) * a.nrep_pad;
-    const float sq = s_q * a.sm_scale;
     for (int rt = 0; rt < a.nrep_pad / kBlock; ++rt) {
-      v8i P[2];
+      v8i Pr[2];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const v8i kop = ld_op_global(rk + static_cast<int64_t>(rt) * kTileBytes, t, lane);
@@ -257,22 +409,21 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = rt * kBlock + 16 * t + 4 * g + i;
-          const float sig = ((s_q * rks[j]) * a.sm_scale) * kLog2e;
+          const float sig = ((sqs * rks[j]) * a.sm_scale) * kLog2e;
           const float s8j = j < nrep ? 8.0f * sig : 0.0f;
-          const float c0 = j < nrep ? 120.0f - 8.0f * M[0] : -1.0f;
-          const float c1 = j < nrep ? 120.0f - 8.0f * M[1] : -1.0f;
+          const float c0 = j < nrep ? 120.0f - 8.0f * st.M[0] : -1.0f;
+          const float c1 = j < nrep ? 120.0f - 8.0f * st.M[1] : -1.0f;
           w0 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[i], s8j, c0), i, w0);
           w1 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[i], s8j, c1), i, w1);
         }
-        P[0][t] = static_cast<int>(w0);
-        P[1][t] = static_cast<int>(w1);
+        Pr[0][t] = static_cast<int>(w0);
+        Pr[1][t] = static_cast<int>(w1);
       }
-      (void)sq;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const v8i eop = ld_op_global(re + static_cast<int64_t>(rt) * kTileBytes, dt, lane);
-        const v4f o0 = mfma_fp8(eop, P[0], zero);
-        const v4f o1 = mfma_fp8(eop, P[1], zero);
+        const v4f o0 = mfma_fp8(eop, Pr[0], zero);
+        const v4f o1 = mfma_fp8(eop, Pr[1], zero);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           O[dt][0][i] = fmaf(fe, o0[i], O[dt][0][i]);
@@ -287,7 +438,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
   for (int qi = 0; qi < 2; ++qi) {
     const int q = qb * kBlock + 16 * (2 * w + qi) + l16;
     if (q < S) {
-      const float f = hd.v_scale / l[qi];
+      const float f = hd.v_scale / st.l[qi];
       uint16_t* orow = a.out + b * a.osB + static_cast<int64_t>(q) * a.osS + h * a.osH;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {

@@ -17,7 +17,7 @@ constexpr int kD = 128;          // head dimension
 constexpr int kBlock = 128;      // tokens per quantisation block / KV tile
 constexpr int kTileBytes = kBlock * kD;
 constexpr int kMaxK = 64;        // clusters per head
-constexpr int kAsgTok = 128;     // tokens per k-means assignment / sort block
+constexpr int kAsgTok = 1024;    // tokens per k-means assignment / sort chunk
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));

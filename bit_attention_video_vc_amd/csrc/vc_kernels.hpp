@@ -48,7 +48,5 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
 hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& k, int B, int S, int H, const WsPtrs& ws,
                              hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int BH, hipStream_t st);
-hipError_t init_kernel_attributes();
-size_t kmeans_assign_smem(int k);
 
 }  // namespace vc

@@ -13,8 +13,8 @@
 // The clustering runs on an integer sketch of V (V scaled by an exact power
 // of two and rounded to [-255, 255]); every distance, sum and count is an
 // exact integer, so assignments and the permutation do not depend on
-// summation order.  All kernels are HBM-bound streaming passes except the
-// distance loop of k_kmeans_assign.
+// summation order.  All kernels are HBM-bound streaming passes; the k-means
+// distances run on the bf16 matrix core (exact for these integers).
 #include "vc_common.hpp"
 #include "vc_kernels.hpp"
 
@@ -74,126 +74,136 @@ __global__ void __launch_bounds__(128) k_kmeans_init(TensorArg v, int S, int H, 
   if (d < k) ccount[bh * k + d] = 0;
 }
 
-// One Lloyd assignment pass over 128 tokens per block.
+// One Lloyd assignment pass over kAsgTok (1024) tokens per workgroup.
 //   ACCUM: add the block's per-cluster sketch sums and counts to csum/ccount.
 //   FINAL: write assign[] and the block's cluster histogram (for the sort).
-// grid (ceil(S/128), H, B), 128 threads (one token per thread in the
-// distance loop).  Scores |c|^2 - 2 x.c are exact integers (|x|,|c| <= 255,
-// 128 terms: below 2^24 per dot product), ties go to the lowest cluster.
-constexpr int kTokPitch = kD + 8;   // int16 row pitch (272 B): staggers LDS banks
+// Distances run on the matrix core: scores^T = C . X^T with
+// v_mfma_f32_16x16x32_bf16, centroids as the A operand (held in registers
+// for the whole block), 16 tokens as the B operand.  Sketch values and
+// centroids are integers in [-255, 255], exact in bf16; every dot product
+// is an integer below 2^24, so the fp32 accumulation is exact in any order.
+// Lane l then holds the scores of centroids 16ct + 4(l/16) + i for token
+// l%16: an in-lane argmin over its centroids and a 4-lane combine give the
+// cluster, ties to the lowest index.  grid (ceil(S/1024), H, B), 256 threads.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+constexpr int kSumPitch = kD + 1;   // padded LDS pitch of the per-cluster sums
+
+__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 template <bool ACCUM, bool FINAL>
-__global__ void __launch_bounds__(kAsgTok) k_kmeans_assign(TensorArg v, int S, int k, const vc_head_hdr* hdr,
-                                                           const int32_t* cent, int32_t* csum, int32_t* ccount,
-                                                           int32_t* assign, int32_t* chunk_hist) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  int16_t* tok = reinterpret_cast<int16_t*>(smem);                               // [128][136]
-  float* cl = reinterpret_cast<float*>(smem + kAsgTok * kTokPitch * 2);          // [k][128]
-  int32_t* part = reinterpret_cast<int32_t*>(cl + k * kD);                       // [k][128]
-  int32_t* cnorm = part + k * kD;                                                // [k]
-  int32_t* cnt = cnorm + kMaxK;                                                  // [k]
-  int32_t* asg = cnt + kMaxK;                                                    // [128]
-
+__global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k, const vc_head_hdr* hdr,
+                                                       const int32_t* cent, int32_t* csum, int32_t* ccount,
+                                                       int32_t* assign, int32_t* chunk_hist) {
+  __shared__ int32_t sums[ACCUM ? kMaxK * kSumPitch : 1];
+  __shared__ int32_t cnorm_s[kMaxK];
+  __shared__ int32_t cnt[kMaxK];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
-  const int s0 = blockIdx.x * kAsgTok;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int shift = hdr[bh].shift;
   const int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
-
-  for (int i = tid; i < k * kD; i += kAsgTok) {
-    cl[i] = static_cast<float>(cg[i]);
-    if (ACCUM) part[i] = 0;
-  }
+  if (ACCUM)
+    for (int i = tid; i < k * kSumPitch; i += 256) sums[i] = 0;
   if (tid < kMaxK) cnt[tid] = 0;
-  // stage the block's sketch rows: 16 threads per token row, 8 channels each
-  for (int i = tid; i < kAsgTok * 16; i += kAsgTok) {
-    const int r = i >> 4, c8 = (i & 15) * 8;
-    const int s = s0 + r;
-    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (s < S) load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tok[r * kTokPitch + c8 + j] = static_cast<int16_t>(sketch1(x[j], shift));
-  }
-  __syncthreads();
   if (tid < k) {
     int32_t n2 = 0;
     for (int d = 0; d < kD; ++d) {
-      const int32_t c = static_cast<int32_t>(cl[tid * kD + d]);
+      const int32_t c = cg[tid * kD + d];
       n2 += c * c;
     }
-    cnorm[tid] = n2;
+    cnorm_s[tid] = n2;
+  }
+  const int nct = (k + 15) >> 4;
+  v8bf ca[4][4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int c = 16 * ct + l16;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        ca[ct][kk][i] = static_cast<__bf16>(c < k ? static_cast<float>(cg[c * kD + 32 * kk + 8 * g + i]) : 0.0f);
   }
   __syncthreads();
-
-  const int s = s0 + tid;
-  int best_c = 0;
-  if (s < S) {
-    float x[kD];
+  int32_t cn[4][4];
 #pragma unroll
-    for (int d = 0; d < kD; ++d) x[d] = static_cast<float>(tok[tid * kTokPitch + d]);
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * ct + 4 * g + i;
+      cn[ct][i] = c < k ? cnorm_s[c] : 0x7FFFFFFF;
+    }
+
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int s0 = blockIdx.x * kAsgTok;
+  for (int tt = 0; tt < kAsgTok / 64; ++tt) {
+    const int tok = s0 + tt * 64 + w * 16 + l16;
+    const bool valid = tok < S;
+    v8bf xb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (valid) load8(v.p, b * v.sB + tok * v.sS + h * v.sH + 32 * kk + 8 * g, v.dtype, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xb[kk][i] = static_cast<__bf16>(sketch1(x[i], shift));
+    }
+    v4f acc[4] = {zero, zero, zero, zero};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (ct < nct) acc[ct] = mfma_bf16(ca[ct][kk], xb[kk], acc[ct]);
     int32_t best = 0x7FFFFFFF;
-    for (int c0 = 0; c0 < k; c0 += 4) {
-      float acc[4] = {0, 0, 0, 0};
-      const int nc = k - c0 < 4 ? k - c0 : 4;
-#pragma unroll 8
-      for (int d = 0; d < kD; d += 4) {
+    int bc = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int cj = c0 + (j < nc ? j : 0);
-          const float4 cv = *reinterpret_cast<const float4*>(&cl[cj * kD + d]);
-          acc[j] = fmaf(x[d], cv.x, acc[j]);
-          acc[j] = fmaf(x[d + 1], cv.y, acc[j]);
-          acc[j] = fmaf(x[d + 2], cv.z, acc[j]);
-          acc[j] = fmaf(x[d + 3], cv.w, acc[j]);
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (ct < nct && cn[ct][i] != 0x7FFFFFFF) {
+          const int32_t sc = cn[ct][i] - 2 * static_cast<int32_t>(acc[ct][i]);
+          if (sc < best) {
+            best = sc;
+            bc = 16 * ct + 4 * g + i;
+          }
         }
       }
-      for (int j = 0; j < nc; ++j) {
-        const int32_t sc = cnorm[c0 + j] - 2 * static_cast<int32_t>(acc[j]);
-        if (sc < best) {
-          best = sc;
-          best_c = c0 + j;
-        }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const int32_t ob = __shfl_xor(best, off, 64);
+      const int oc = __shfl_xor(bc, off, 64);
+      if (ob < best || (ob == best && oc < bc)) {
+        best = ob;
+        bc = oc;
       }
     }
-    asg[tid] = best_c;
-    atomicAdd(&cnt[best_c], 1);
-    if (FINAL) assign[static_cast<int64_t>(bh) * S + s] = best_c;
-  } else {
-    asg[tid] = -1;
+    if (valid) {
+      if (g == 0) {
+        atomicAdd(&cnt[bc], 1);
+        if (FINAL) assign[static_cast<int64_t>(bh) * S + tok] = bc;
+      }
+      if (ACCUM) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            atomicAdd(&sums[bc * kSumPitch + 32 * kk + 8 * g + i], static_cast<int32_t>(static_cast<float>(xb[kk][i])));
+      }
+    }
   }
   __syncthreads();
-
   if (ACCUM) {
-    // thread owns channel d; walk the block's tokens in order
-    const int d = tid;
-    for (int r = 0; r < kAsgTok; ++r) {
-      const int c = asg[r];
-      if (c >= 0) part[c * kD + d] += tok[r * kTokPitch + d];
-    }
-    __syncthreads();
     int32_t* gs = csum + static_cast<int64_t>(bh) * k * kD;
-    for (int i = tid; i < k * kD; i += kAsgTok)
-      if (part[i] != 0) atomicAdd(&gs[i], part[i]);
+    for (int i = tid; i < k * kD; i += 256) {
+      const int32_t val = sums[(i / kD) * kSumPitch + (i % kD)];
+      if (val != 0) atomicAdd(&gs[i], val);
+    }
     if (tid < k && cnt[tid] != 0) atomicAdd(&ccount[bh * k + tid], cnt[tid]);
   }
   if (FINAL && tid < k) {
     const int nchunk = (S + kAsgTok - 1) / kAsgTok;
     chunk_hist[(static_cast<int64_t>(bh) * nchunk + blockIdx.x) * k + tid] = cnt[tid];
   }
-}
-
-size_t kmeans_assign_smem(int k) {
-  return static_cast<size_t>(kAsgTok) * kTokPitch * 2 + static_cast<size_t>(k) * kD * 4 * 2 +
-         (2 * kMaxK + kAsgTok) * 4;
-}
-
-hipError_t init_kernel_attributes() {
-  const int bytes = static_cast<int>(kmeans_assign_smem(kMaxK));
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_kmeans_assign<true, false>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(k_kmeans_assign<false, true>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 // New centroid = floor((2*sum + n) / (2n)) (mean rounded half up); empty
@@ -242,34 +252,44 @@ __global__ void __launch_bounds__(64) k_cluster_scan(int S, int k, const int32_t
 }
 
 // Stable counting-sort scatter: perm[pos] = token, ordered by (cluster, token).
-// grid (ceil(S/128), H, B), 128 threads (2 waves).
-__global__ void __launch_bounds__(kAsgTok) k_cluster_scatter(int S, int k, const int32_t* assign,
-                                                             const int32_t* chunk_off, int32_t* perm) {
-  __shared__ int32_t wcount[kAsgTok / 64][kMaxK];
+// One 1024-token chunk per workgroup, walked in token order in four passes
+// of 256; ranks within a wave come from ballots.  grid (ceil(S/1024), H, B),
+// 256 threads.
+__global__ void __launch_bounds__(256) k_cluster_scatter(int S, int k, const int32_t* assign,
+                                                         const int32_t* chunk_off, int32_t* perm) {
+  __shared__ int32_t wcount[4][kMaxK];
+  __shared__ int32_t run[kMaxK];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < (kAsgTok / 64) * kMaxK; i += kAsgTok) (&wcount[0][0])[i] = 0;
-  __syncthreads();
-  const int s = blockIdx.x * kAsgTok + tid;
-  const bool valid = s < S;
-  const int c = valid ? assign[static_cast<int64_t>(bh) * S + s] : -1;
+  const int nchunk = (S + kAsgTok - 1) / kAsgTok;
+  const int32_t* off = chunk_off + (static_cast<int64_t>(bh) * nchunk + blockIdx.x) * k;
+  if (tid < kMaxK) run[tid] = 0;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint64_t rem = __ballot(valid);
-  int rank = 0;
-  while (rem) {
-    const int leader = __ffsll(static_cast<unsigned long long>(rem)) - 1;
-    const int cl = __builtin_amdgcn_readlane(c, leader);
-    const uint64_t m = __ballot(valid && c == cl);
-    if (valid && c == cl) rank = __popcll(m & lt);
-    if (lane == 0) wcount[w][cl] = __popcll(m);
-    rem &= ~m;
-  }
-  __syncthreads();
-  if (valid) {
-    const int nchunk = (S + kAsgTok - 1) / kAsgTok;
-    int pos = chunk_off[(static_cast<int64_t>(bh) * nchunk + blockIdx.x) * k + c] + rank;
-    for (int j = 0; j < w; ++j) pos += wcount[j][c];
-    perm[static_cast<int64_t>(bh) * S + pos] = s;
+  for (int it = 0; it < kAsgTok / 256; ++it) {
+    for (int i = tid; i < 4 * kMaxK; i += 256) (&wcount[0][0])[i] = 0;
+    __syncthreads();
+    const int s = blockIdx.x * kAsgTok + it * 256 + tid;
+    const bool valid = s < S;
+    const int c = valid ? assign[static_cast<int64_t>(bh) * S + s] : -1;
+    uint64_t rem = __ballot(valid);
+    int rank = 0;
+    while (rem) {
+      const int leader = __ffsll(static_cast<unsigned long long>(rem)) - 1;
+      const int cl = __builtin_amdgcn_readlane(c, leader);
+      const uint64_t m = __ballot(valid && c == cl);
+      if (valid && c == cl) rank = __popcll(m & lt);
+      if (lane == 0) wcount[w][cl] = __popcll(m);
+      rem &= ~m;
+    }
+    __syncthreads();
+    if (valid) {
+      int pos = off[c] + run[c] + rank;
+      for (int j = 0; j < w; ++j) pos += wcount[j][c];
+      perm[static_cast<int64_t>(bh) * S + pos] = s;
+    }
+    __syncthreads();
+    if (tid < k) run[tid] += wcount[0][tid] + wcount[1][tid] + wcount[2][tid] + wcount[3][tid];
+    __syncthreads();
   }
 }
 
@@ -350,7 +370,8 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
   if (threadIdx.x < kD) {
     const float m = v_mean[(static_cast<int64_t>(bh) * nblk + blk) * kD + threadIdx.x];
     mu[threadIdx.x] = m;
-    v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kD + threadIdx.x] = m / s_v;
+    // restore-operand order: (d % 16) * 8 + d / 16 within the tile's 128 floats
+    v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kD + (threadIdx.x & 15) * 8 + (threadIdx.x >> 4)] = m / s_v;
   }
   if (blk == 0 && threadIdx.x == 0) {
     hdr[bh].v_scale = s_v;
@@ -635,20 +656,19 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
     hipLaunchKernelGGL(k_kmeans_init, dim3(BH), dim3(128), 0, st, v, S, H, k, o.seed, ws.hdr, ws.cent, ws.csum,
                        ws.ccount);
     VC_LAUNCH_CHECK();
-    const size_t sm = kmeans_assign_smem(k);
     for (int it = 0; it < o.iters; ++it) {
-      hipLaunchKernelGGL((k_kmeans_assign<true, false>), dim3(nch, H, B), dim3(kAsgTok), sm, st, v, S, k,
-                         ws.hdr, ws.cent, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
+      hipLaunchKernelGGL((k_kmeans_assign<true, false>), dim3(nch, H, B), dim3(256), 0, st, v, S, k, ws.hdr,
+                         ws.cent, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
       VC_LAUNCH_CHECK();
       hipLaunchKernelGGL(k_kmeans_update, dim3(BH), dim3(256), 0, st, k, ws.cent, ws.csum, ws.ccount);
       VC_LAUNCH_CHECK();
     }
-    hipLaunchKernelGGL((k_kmeans_assign<false, true>), dim3(nch, H, B), dim3(kAsgTok), sm, st, v, S, k, ws.hdr,
+    hipLaunchKernelGGL((k_kmeans_assign<false, true>), dim3(nch, H, B), dim3(256), 0, st, v, S, k, ws.hdr,
                        ws.cent, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
     VC_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_cluster_scan, dim3(BH), dim3(64), 0, st, S, k, ws.chunk_hist, ws.chunk_off);
     VC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_cluster_scatter, dim3(nch, H, B), dim3(kAsgTok), 0, st, S, k, ws.assign, ws.chunk_off,
+    hipLaunchKernelGGL(k_cluster_scatter, dim3(nch, H, B), dim3(256), 0, st, S, k, ws.assign, ws.chunk_off,
                        ws.perm);
     VC_LAUNCH_CHECK();
   } else {

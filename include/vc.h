@@ -101,7 +101,7 @@ typedef struct {
  *   k_scale f32 [BH][nblk]
  *   v8      u8  [BH][nblk] tiles: residual codes, permuted order, transposed
  *   v_mean  f32 [BH][nblk][128] block means mu_b
- *   v_meanp f32 [BH][nblk][128] mu_b / s_v
+ *   v_meanp f32 [BH][nblk][128] mu_b / s_v, channel d stored at (d%16)*8 + d/16
  *   hdr     per-(b,h) scalars, vc_head_hdr [BH]
  *   assign  i32 [BH][S] cluster id of each ORIGINAL token
  *   perm    i32 [BH][S] original token at permuted position p
