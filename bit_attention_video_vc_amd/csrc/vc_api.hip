@@ -96,7 +96,7 @@ vc_status make_plan(const vc_desc* vd, const vc_v_opts* o, Plan* p) {
   L.k_scale = take(sizeof(float) * per_blk);
   L.v8 = take(tiles);
   L.v_mean = take(sizeof(float) * per_blk * vc::kD);
-  L.v_meanp = take(sizeof(float) * per_blk * vc::kD);
+  L.v_meanp = take(sizeof(float) * per_blk * vc::kMuStride);
   L.hdr = take(sizeof(vc_head_hdr) * BH);
   L.assign = take(sizeof(int32_t) * BH * p->S);
   L.perm = take(sizeof(int32_t) * BH * p->S);
@@ -273,7 +273,7 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   float sm = aopts ? aopts->sm_scale : 0.0f;
   if (!(sm >= 0.0f) || std::isinf(sm)) return fail(VC_ERR_ARG, "sm_scale must be finite and >= 0");
   if (sm == 0.0f) sm = static_cast<float>(1.0 / std::sqrt(128.0));
-  const int64_t total = static_cast<int64_t>(p.B) * p.H * p.nblk;
+  const int64_t total = static_cast<int64_t>(p.B) * p.H * ((p.nblk + 1) / 2);   // one workgroup per query-block pair
   if (total > (int64_t)1 << 31) return fail(VC_ERR_UNSUPPORTED, "too many query blocks");
   if ((s = check_device()) != VC_OK) return s;
   const vc::WsPtrs w = ws_ptrs(p, const_cast<void*>(ws));

@@ -37,7 +37,8 @@
 
 namespace vc {
 
-constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = 64 * kAttnWaves;   // 512: two 128-query blocks per workgroup
 constexpr float kLog2e = 1.44269504088896340736f;
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -64,16 +65,44 @@ __device__ __forceinline__ v8i ld_op_global(const uint8_t* base, int sub, int la
   return r;
 }
 
-// Copy one 16 KB tile from global memory straight into LDS: each of the 4
-// instructions moves 16 bytes per lane; the LDS destination of lane i is
-// base + 16*i, so the tile lands in the same linear order.
-__device__ __forceinline__ void tile_to_lds(const uint8_t* src, uint8_t* dst, int tid) {
-  const int w = tid >> 6;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(src + (j * kAttnThreads + tid) * 16),   // global source
-        (__attribute__((address_space(3))) void*)(dst + j * 4096 + w * 1024), 16, 0, 0);         // LDS base
+// Tiles go from global memory straight into LDS with buffer loads (the
+// buffer form: the compiler tracks these copies on the vector-memory counter
+// only, so waits for LDS reads issued after a copy stay partial).  Every
+// lane moves 16 bytes to LDS address M0 + 16*lane; a per-head buffer
+// resource bounds every copy (an offset past it reads zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: raw 32-bit untyped access (the CDNA3/CDNA4 setting)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0,
+                                           0, 0);
+}
+constexpr int kDmaPerTile = kTileBytes / (16 * kAttnThreads);   // copy instructions per 16 KB tile
+// LDS ring depth for K and for V tiles; copies run kStages-1 tiles ahead.
+constexpr int kStages = 4;
+constexpr int kDmaPerStep = 2 * kDmaPerTile + 1;                  // K tile, V tile, mu row + scale
+constexpr uint32_t kMuRowBytes = kMuStride * 4;                  // 528
+// A V buffer: the V tile, then its v_meanp row (mu/s_v at [0,512), the K
+// scale of the next score tile at 512) and room for the zero-filled lanes
+// 33..63 of the row copy.
+constexpr int kVBufBytes = kTileBytes + 1024;
+
+// End of a tile step: every wave waits until only the copies of its last
+// kStages-2 steps (the last (kStages-2)*kDmaPerStep vector-memory
+// instructions it issued) may still be in flight -- so the copies issued
+// kStages-2 steps earlier have landed -- and until its LDS reads have
+// returned; then the workgroup barrier.  The copies of a step are always its
+// last vector-memory instructions.
+__device__ __forceinline__ void step_barrier() {
+  // s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14.
+  // Written as a builtin so the compiler's own wait insertion knows that
+  // every older copy has landed after this point.
+  constexpr int kVm = (kStages - 2) * kDmaPerStep;
+  static_assert(kVm < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((kVm & 15) | (7 << 4) | (0 << 8) | ((kVm >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
 }
 
 // ExpCast of one 16x16 accumulator (4 keys per lane) into one packed dword.
@@ -99,36 +128,69 @@ struct SoftState {
 };
 
 // Score tile of one 128-key block against this wave's two query sub-tiles.
-// K operands are read from LDS two sub-tiles ahead of their MFMAs.  When
-// vt is given, the first two V operands of the P.V product that follows are
-// read during the last steps (they sit in another buffer).
-__device__ __forceinline__ void score_tile(const uint8_t* ktile, int lane, const v8i (&qop)[2], v4f (&sc)[8][2],
-                                           const uint8_t* vt = nullptr, v8i* vop = nullptr) {
+// The block-mean restore of the tile whose P.V follows (O^T += mu'_b . r_b,
+// 64 FMAs, mu' from the LDS row next to that tile's V codes) fills the VALU
+// slots under these MFMAs.  K operands and mu values are read from LDS two
+// sub-tiles ahead of their use (mu first, so that waiting for the older pair
+// leaves the newer one in flight); the first two V operands of the P.V that
+// follows are read in the last two sub-tiles.
+template <typename Copies>
+__device__ __forceinline__ void score_tile_restore(const uint8_t* ktile, int lane, int g, const v8i (&qop)[2],
+                                                   v4f (&sc)[8][2], const uint8_t* vt, v8i (&vop)[2],
+                                                   v4f (&O)[8][2], const float (&r)[2], const Copies& cp) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float* mrow = reinterpret_cast<const float*>(vt + kTileBytes);
   v8i kop[2];
+  float4 mu[2];
+  mu[0] = *reinterpret_cast<const float4*>(mrow + 4 * g);
   kop[0] = ld_op_lds(ktile, 0, lane);
+  mu[1] = *reinterpret_cast<const float4*>(mrow + 16 + 4 * g);
   kop[1] = ld_op_lds(ktile, 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const v8i cur = kop[t & 1];
+    const float4 m = mu[t & 1];
     sc[t][0] = mfma_fp8(cur, qop[0], zero);
+    O[t][0][0] = fmaf(r[0], m.x, O[t][0][0]);
+    O[t][0][1] = fmaf(r[0], m.y, O[t][0][1]);
+    O[t][0][2] = fmaf(r[0], m.z, O[t][0][2]);
+    O[t][0][3] = fmaf(r[0], m.w, O[t][0][3]);
     sc[t][1] = mfma_fp8(cur, qop[1], zero);
+    O[t][1][0] = fmaf(r[1], m.x, O[t][1][0]);
+    O[t][1][1] = fmaf(r[1], m.y, O[t][1][1]);
+    O[t][1][2] = fmaf(r[1], m.z, O[t][1][2]);
+    O[t][1][3] = fmaf(r[1], m.w, O[t][1][3]);
     if (t + 2 < 8) {
+      mu[t & 1] = *reinterpret_cast<const float4*>(mrow + 16 * (t + 2) + 4 * g);
       kop[t & 1] = ld_op_lds(ktile, t + 2, lane);
-    } else if (vt != nullptr) {
-      vop[t - 6] = ld_op_lds(vt, t - 6, lane);
+    } else {
+      vop[t & 1] = ld_op_lds(vt, t - 6, lane);
     }
+    if (t & 1) cp.issue(t >> 1);   // copy parts 0..3
     __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Score tile without restore (tile 0 in the prologue).
+__device__ __forceinline__ void score_tile(const uint8_t* ktile, int lane, const v8i (&qop)[2], v4f (&sc)[8][2]) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const v8i kop = ld_op_lds(ktile, t, lane);
+    sc[t][0] = mfma_fp8(kop, qop[0], zero);
+    sc[t][1] = mfma_fp8(kop, qop[1], zero);
   }
 }
 
 // Mask keys >= kval in a ragged last tile (lane group g holds keys 16t+4g+i).
 __device__ __forceinline__ void mask_tile(v4f (&sc)[8][2], int g, int kval) {
+  const int kr = kval - 4 * g;   // compare 16t+i against it: no per-key registers
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (16 * t + 4 * g + i >= kval) sc[t][0][i] = sc[t][1][i] = kNegBig;
+      if (16 * t + i >= kr) sc[t][0][i] = sc[t][1][i] = kNegBig;
 }
 
 // Integer running max, rescale factor and ExpCast codes for one tile.
@@ -140,8 +202,7 @@ __device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma,
     float mx = max4(sc[0][qi]);
 #pragma unroll
     for (int t = 1; t < 8; ++t) mx = fmaxf(mx, max4(sc[t][qi]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_over_rows(mx);
     const float mn = fmaxf(st.M[qi], ceilf(mx * sigma));
     alpha[qi] = st.M[qi] == kNegBig ? 0.0f : ldexpf(1.0f, static_cast<int>(fmaxf(st.M[qi] - mn, -160.0f)));
     st.M[qi] = mn;
@@ -153,10 +214,8 @@ __device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma,
 
 // Loop-invariant inputs of one workgroup's tile loop.
 struct TileCtx {
-  const uint8_t* kbase;     // this head's K8 tiles
-  const uint8_t* vbase;     // this head's V8 tiles
-  const float* mbase;       // this head's mu/s_v, restore-operand order
-  const float* __restrict__ ks;   // this head's K block scales (read-only: scalar loads)
+  __amdgpu_buffer_rsrc_t kr, vr, mr;   // this head's K8 tiles, V8 tiles, v_meanp rows
+  const float* ks;          // this head's K block scales
   float sqs, sm_scale;
   int nblk, kval_last, tid, lane, g, l16;
 };
@@ -165,52 +224,74 @@ struct TileCtx {
 struct TileAcc {
   v4f O[8][2];     // O^T: lane holds channels 16dt+4g+i of query l16 (+16 per sub-tile)
   v8i P[2];        // E4M3 codes of the current tile (P^T operand)
-  float rb[2];     // restore batch: lane group g holds the row sum of tile 4*batch+g
-  float mu[8];     // restore operand: lane group g holds mu/s_v of tile 4*batch+g
-  float ks_next;   // K scale of tile kb+1 (loaded during step kb-1)
+  float r[2];      // row sum of the current tile (for its block-mean restore)
   SoftState st;
 };
 
-// mu/s_v of tile t for the restore operand: lanes of group t%4 keep channel
-// 16*dt + l16 at mu[dt]; the other lanes keep what they hold.
-__device__ __forceinline__ void load_mu_row(const float* mbase, int t, int nblk, int g, int l16, float (&mu)[8]) {
-  if (t < nblk && g == (t & 3)) {
-    const float4* mp = reinterpret_cast<const float4*>(mbase + static_cast<int64_t>(t) * kD + l16 * 8);
-    const float4 m0 = mp[0], m1 = mp[1];
-    mu[0] = m0.x; mu[1] = m0.y; mu[2] = m0.z; mu[3] = m0.w;
-    mu[4] = m1.x; mu[5] = m1.y; mu[6] = m1.z; mu[7] = m1.w;
+// The copies of one step: K(tk) into kfree, V(tv) with its v_meanp row into
+// vfree -- exactly kDmaPerStep copy instructions, issued one at a time
+// (part 0: the row, parts 1..kDmaPerTile: K, then V) at points spread over
+// the step, so that the workgroup's copies do not all queue at once.
+struct StepCopies {
+  const TileCtx& c;
+  uint32_t koff, voff, moff;
+  uint8_t* kdst;
+  uint8_t* vdst;
+  __device__ __forceinline__ StepCopies(const TileCtx& ctx, int tk, int tv, uint8_t* kfree, uint8_t* vfree)
+      : c(ctx) {
+    koff = static_cast<uint32_t>(tk) * kTileBytes + static_cast<uint32_t>(c.tid) * 16;
+    voff = static_cast<uint32_t>(tv) * kTileBytes + static_cast<uint32_t>(c.tid) * 16;
+    // lanes 0..32 move the 528-byte row; the others read past the buffer (zeros)
+    moff = c.lane * 16 < static_cast<int>(kMuRowBytes) ? static_cast<uint32_t>(tv) * kMuRowBytes + c.lane * 16
+                                                         : static_cast<uint32_t>(c.nblk) * kMuRowBytes;
+    kdst = kfree;
+    vdst = vfree;
   }
-}
+  __device__ __forceinline__ void issue(int part) const {
+    const int w = c.tid >> 6;
+    if (part == 0) {
+      copy16_to_lds(c.mr, moff, vdst + kTileBytes);
+    } else if (part <= kDmaPerTile) {
+      const int j = part - 1;
+      copy16_to_lds(c.kr, koff + j * (16 * kAttnThreads), kdst + j * (16 * kAttnThreads) + w * 1024);
+    } else {
+      const int j = part - 1 - kDmaPerTile;
+      copy16_to_lds(c.vr, voff + j * (16 * kAttnThreads), vdst + j * (16 * kAttnThreads) + w * 1024);
+    }
+  }
+  __device__ __forceinline__ void issue_all() const {
+#pragma unroll
+    for (int p = 0; p < kDmaPerStep; ++p) issue(p);
+  }
+};
 
-__device__ __forceinline__ bool flush_step(int kb, int nblk) { return (kb & 3) == 3 || kb + 1 >= nblk; }
-
-// One tile step kb: scores of tile kb+1 (K in kcur), P.V of tile kb (V in
-// vcur) interleaved with tile kb+1's softmax, block-mean restore, rescale,
-// and the loads of K(kb+2) into kfree and V(kb+1) into vfree.  The four LDS
-// buffers are distinct arrays, so these loads overlap with the reads of this
-// step; they are waited for at the closing barrier.
+// One tile step kb: scores of tile kb+1 (K in kcur) with tile kb's
+// block-mean restore under them, then P.V of tile kb (V in vcur)
+// interleaved with tile kb+1's softmax, then rescale and row sum.  Copies
+// run two steps ahead: this step copies K(kb+3) into kfree and V(kb+2) into
+// vfree (triple-buffered, distinct LDS arrays, so the copies overlap the
+// reads of this step and the next), as its last vector-memory instructions
+// (see step_barrier).  Tile indices past the last tile are clamped to it and
+// a score tile past the end is masked out entirely, which leaves the state
+// unchanged (alpha = 1, codes and row sum 0): every step runs the same code.
 __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
                                           const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2],
                                           const uint8_t* ones_lds, TileAcc& acc) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int nblk = c.nblk, lane = c.lane, g = c.g;
-  const bool has_next = kb + 1 < nblk;
-  // No vector load issued in this step is consumed in it (the vector-memory
-  // counter retires in order, so such a wait would also wait for the next
-  // tile): the next tile's restore row and K scale are loaded at the end of
-  // the step and retired by the closing barrier.
-  const bool flush = flush_step(kb, nblk);
-  const float ks_next = acc.ks_next;
-  if (kb + 2 < nblk) tile_to_lds(c.kbase + static_cast<int64_t>(kb + 2) * kTileBytes, kfree, c.tid);
-  if (has_next) tile_to_lds(c.vbase + static_cast<int64_t>(kb + 1) * kTileBytes, vfree, c.tid);
+  const int nblk = c.nblk, last = nblk - 1, lane = c.lane, g = c.g;
+  const int tn = kb + 1 < last ? kb + 1 : last;   // score tile (clamped)
+  const float ks_next = *reinterpret_cast<const float*>(vcur + kTileBytes + 4 * kD);
+  const StepCopies cp(c, kb + kStages < last ? kb + kStages : last,
+                      kb + kStages - 1 < last ? kb + kStages - 1 : last, kfree, vfree);
+  static_assert(kDmaPerStep == 5, "copy parts 0-3 go under the scores, part 4 under P.V");
 
   v8i Pn[2];
-  float alpha[2] = {1.0f, 1.0f};
-  if (has_next) {
+  float alpha[2];
+  {
     v4f sc[8][2];
     v8i vop[2];
-    score_tile(kcur, lane, qop, sc, vcur, vop);
-    if (kb + 2 == nblk && c.kval_last < kBlock) mask_tile(sc, g, c.kval_last);
+    score_tile_restore(kcur, lane, g, qop, sc, vcur, vop, acc.O, acc.r, cp);
+    if (kb + 2 >= nblk) mask_tile(sc, g, kb + 2 == nblk ? c.kval_last : 0);
     const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
     const float s8 = 8.0f * sigma;
     // P.V of tile kb on the matrix core, hand-interleaved with tile kb+1's
@@ -234,8 +315,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
       acc.O[dt][1] = mfma_fp8(vc, acc.P[1], acc.O[dt][1]);
       if (dt < 2) {
         mx[dt] = fmaxf(mx[dt], fmaxf(fmaxf(max4(sc[4][dt]), max4(sc[5][dt])), fmaxf(max4(sc[6][dt]), max4(sc[7][dt]))));
-        mx[dt] = fmaxf(mx[dt], __shfl_xor(mx[dt], 16, 64));
-        mx[dt] = fmaxf(mx[dt], __shfl_xor(mx[dt], 32, 64));
+        mx[dt] = max_over_rows(mx[dt]);
         if (dt == 1) {
 #pragma unroll
           for (int qi = 0; qi < 2; ++qi) {
@@ -254,83 +334,74 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
         }
       }
       if (dt + 2 < 8) vop[dt & 1] = ld_op_lds(vcur, dt + 2, lane);
+      if (dt == 3) cp.issue(4);
       __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const v8i vop = ld_op_lds(vcur, dt, lane);
-      acc.O[dt][0] = mfma_fp8(vop, acc.P[0], acc.O[dt][0]);
-      acc.O[dt][1] = mfma_fp8(vop, acc.P[1], acc.O[dt][1]);
-    }
   }
 
-  // flush the restore batch after its last tile (or the last tile overall):
-  // O^T += (mu/s_v)^T (16 d x 4 tiles) . rb  with v_mfma_f32_16x16x4_f32
-  if (flush) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      acc.O[dt][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(acc.mu[dt], acc.rb[0], acc.O[dt][0], 0, 0, 0);
-      acc.O[dt][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(acc.mu[dt], acc.rb[1], acc.O[dt][1], 0, 0, 0);
-    }
-    acc.rb[0] = acc.rb[1] = 0.0f;
-  }
-  // restore row of tile kb+1 (after this step's flush has used the slot) and
-  // the K scale of tile kb+2
-  load_mu_row(c.mbase, kb + 1, nblk, g, c.l16, acc.mu);
-  if (kb + 2 < nblk) acc.ks_next = c.ks[kb + 2];
-
-  if (has_next) {
-    if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
-#pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
-        acc.st.l[qi] *= alpha[qi];
-        acc.rb[qi] *= alpha[qi];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc.O[dt][qi] *= alpha[qi];
-      }
-    }
-    const int gnext = (kb + 1) & 3;
-    const v8i ones = ld_op_lds(ones_lds, 0, lane);
+  if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
 #pragma unroll
     for (int qi = 0; qi < 2; ++qi) {
-      const float r = mfma_fp8(ones, Pn[qi], zero)[0];
-      acc.st.l[qi] += r;
-      acc.rb[qi] = g == gnext ? r : acc.rb[qi];
-      acc.P[qi] = Pn[qi];
+      acc.st.l[qi] *= alpha[qi];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc.O[dt][qi] *= alpha[qi];
     }
   }
-  __syncthreads();
+  const v8i ones = ld_op_lds(ones_lds, 0, lane);
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const float r = mfma_fp8(ones, Pn[qi], zero)[0];
+    acc.st.l[qi] += r;
+    acc.r[qi] = r;
+    acc.P[qi] = Pn[qi];
+  }
+  step_barrier();
 }
 
-__global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
-  // four distinct arrays: a load into one provably does not alias reads of another
+__global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
+  // six distinct arrays (K and V triple-buffered): a copy into one provably
+  // does not alias reads of another
+  static_assert(kStages == 4, "buffer declarations below");
   __shared__ __align__(16) uint8_t kbuf0[kTileBytes];
   __shared__ __align__(16) uint8_t kbuf1[kTileBytes];
-  __shared__ __align__(16) uint8_t vbuf0[kTileBytes];
-  __shared__ __align__(16) uint8_t vbuf1[kTileBytes];
+  __shared__ __align__(16) uint8_t kbuf2[kTileBytes];
+  __shared__ __align__(16) uint8_t kbuf3[kTileBytes];
+  __shared__ __align__(16) uint8_t vbuf0[kVBufBytes];   // V codes + the tile's mu row
+  __shared__ __align__(16) uint8_t vbuf1[kVBufBytes];
+  __shared__ __align__(16) uint8_t vbuf2[kVBufBytes];
+  __shared__ __align__(16) uint8_t vbuf3[kVBufBytes];
+  uint8_t* const kring[kStages] = {kbuf0, kbuf1, kbuf2, kbuf3};
+  uint8_t* const vring[kStages] = {vbuf0, vbuf1, vbuf2, vbuf3};
   __shared__ __align__(16) uint8_t ones_lds[2048];   // E4M3 1.0 operand for the row sums
 
   // XCD-aware order: hardware deals workgroup ids round-robin over 8 XCDs;
-  // give XCD x a contiguous range of (head, query-block) work items.
+  // give XCD x a contiguous range of (head, query-block pair) work items.
   const int total = a.total_wg;
   const int wg = blockIdx.x, xcd = wg & 7, idx = wg >> 3;
   const int per = total >> 3, rem = total & 7;
   const int logical = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
   const int nblk = a.nblk;
-  const int bh = logical / nblk, qb = logical - bh * nblk;
+  const int npair = (nblk + 1) >> 1;
+  const int bh = logical / npair, qp = logical - bh * npair;
   const int b = bh / a.H, h = bh - b * a.H;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int S = a.S;
+  // waves 0-3 own query block 2*qp, waves 4-7 block 2*qp+1 (a missing second
+  // block of an odd count is computed on a copy of the first and not stored)
+  const int qb = 2 * qp + (w >> 2);
+  const bool q_valid = qb < nblk;
+  const int qbl = q_valid ? qb : nblk - 1;
+  const int wq = w & 3;                           // 32-query slice within the block
 
   TileCtx c;
-  c.kbase = a.k8 + static_cast<int64_t>(bh) * nblk * kTileBytes;
-  c.vbase = a.v8 + static_cast<int64_t>(bh) * nblk * kTileBytes;
-  c.mbase = a.v_meanp + static_cast<int64_t>(bh) * nblk * kD;
+  // nblk <= 2^17 (S <= 2^24), so a head's tiles span less than 4 GB
+  c.kr = head_rsrc(a.k8 + static_cast<int64_t>(bh) * nblk * kTileBytes, static_cast<uint32_t>(nblk) * kTileBytes);
+  c.vr = head_rsrc(a.v8 + static_cast<int64_t>(bh) * nblk * kTileBytes, static_cast<uint32_t>(nblk) * kTileBytes);
+  c.mr = head_rsrc(a.v_meanp + static_cast<int64_t>(bh) * nblk * kMuStride, static_cast<uint32_t>(nblk) * kMuRowBytes);
   c.ks = a.k_scale + static_cast<int64_t>(bh) * nblk;
-  c.sqs = a.q_scale[static_cast<int64_t>(bh) * nblk + qb];
+  c.sqs = a.q_scale[static_cast<int64_t>(bh) * nblk + qbl];
   c.sm_scale = a.sm_scale;
   c.nblk = nblk;
   c.kval_last = S - (nblk - 1) * kBlock;          // real keys in the last tile
@@ -340,10 +411,10 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
   c.l16 = l16;
   const float sqs = c.sqs;
 
-  const uint8_t* qtile = a.q8 + (static_cast<int64_t>(bh) * nblk + qb) * kTileBytes;
+  const uint8_t* qtile = a.q8 + (static_cast<int64_t>(bh) * nblk + qbl) * kTileBytes;
   v8i qop[2];
-  qop[0] = ld_op_global(qtile, 2 * w, lane);
-  qop[1] = ld_op_global(qtile, 2 * w + 1, lane);
+  qop[0] = ld_op_global(qtile, 2 * wq, lane);
+  qop[1] = ld_op_global(qtile, 2 * wq + 1, lane);
 
   for (int i = tid; i < 2048 / 4; i += kAttnThreads) reinterpret_cast<uint32_t*>(ones_lds)[i] = 0x38383838u;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -353,16 +424,21 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
   acc.st.l[0] = acc.st.l[1] = 0.0f;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc.O[dt][0] = acc.O[dt][1] = zero;
-  acc.rb[0] = acc.rb[1] = 0.0f;
 
-  // ---- prologue: K(0), V(0), K(1) into LDS; scores and codes of tile 0 ----
+  // ---- prologue: K(0..2), V(0..1) with their mu rows into LDS; scores and
+  // codes of tile 0 ----
+  const int last = nblk - 1;
+  // tiles 0..kStages-2: K, and V with its mu row and the scales of the tile
+  // after it; then K(kStages-1)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc.mu[i] = 0.0f;
-  load_mu_row(c.mbase, 0, nblk, g, l16, acc.mu);
-  acc.ks_next = nblk > 1 ? c.ks[1] : 1.0f;
-  tile_to_lds(c.kbase, kbuf0, tid);
-  tile_to_lds(c.vbase, vbuf0, tid);
-  if (nblk > 1) tile_to_lds(c.kbase + kTileBytes, kbuf1, tid);
+  for (int j = 0; j + 1 < kStages; ++j)
+    StepCopies(c, j < last ? j : last, j < last ? j : last, kring[j], vring[j]).issue_all();
+  {
+    const StepCopies cp(c, kStages - 1 < last ? kStages - 1 : last, 0, kring[kStages - 1], vring[0]);
+#pragma unroll
+    for (int p = 1; p <= kDmaPerTile; ++p) cp.issue(p);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   {
     v4f sc[8][2];
@@ -375,17 +451,29 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
     for (int qi = 0; qi < 2; ++qi) {
       const float r = mfma_fp8(ones, acc.P[qi], zero)[0];
       acc.st.l[qi] = r;
-      acc.rb[qi] = g == 0 ? r : 0.0f;
+      acc.r[qi] = r;
     }
   }
-  __syncthreads();   // kbuf0 (K(0)) is refilled with K(2) in the first step
+  __syncthreads();   // kring[0] (K(0)) is refilled in the first step
 
-  // Even steps read K(kb+1) from kbuf1 and V(kb) from vbuf0, and refill kbuf0
-  // and vbuf1; odd steps the other way round.
-  for (int kb = 0; kb < nblk; kb += 2) {
-    tile_step(c, kb, kbuf1, kbuf0, vbuf0, vbuf1, qop, ones_lds, acc);
-    if (kb + 1 < nblk) tile_step(c, kb + 1, kbuf0, kbuf1, vbuf1, vbuf0, qop, ones_lds, acc);
+  // Step kb reads K(kb+1) from kring[(kb+1)%S] and V(kb) from vring[kb%S]
+  // (S = kStages), and refills kring[kb%S] with K(kb+S) and
+  // vring[(kb+S-1)%S] with V(kb+S-1).  The loop is unrolled S times so that
+  // every buffer is a fixed array.
+  int kb = 0;
+  for (; kb + kStages <= nblk; kb += kStages) {
+#pragma unroll
+    for (int j = 0; j < kStages; ++j)
+      tile_step(c, kb + j, kring[(j + 1) % kStages], kring[j], vring[j], vring[(j + kStages - 1) % kStages], qop,
+                ones_lds, acc);
   }
+#pragma unroll
+  for (int j = 0; j + 1 < kStages; ++j)
+    if (kb + j < nblk)
+      tile_step(c, kb + j, kring[(j + 1) % kStages], kring[j], vring[j], vring[(j + kStages - 1) % kStages], qop,
+                ones_lds, acc);
+  // drain the copies still in flight before the workgroup retires
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   SoftState& st = acc.st;
   v4f (&O)[8][2] = acc.O;
@@ -436,8 +524,8 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_vc_attn_fwd(AttnArgs a) {
   // ---- epilogue: out = bf16(s_v * O / l), original query order ----
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
-    const int q = qb * kBlock + 16 * (2 * w + qi) + l16;
-    if (q < S) {
+    const int q = qb * kBlock + 16 * (2 * wq + qi) + l16;
+    if (q_valid && q < S) {
       const float f = hd.v_scale / st.l[qi];
       uint16_t* orow = a.out + b * a.osB + static_cast<int64_t>(q) * a.osS + h * a.osH;
 #pragma unroll

@@ -17,6 +17,9 @@ constexpr int kD = 128;          // head dimension
 constexpr int kBlock = 128;      // tokens per quantisation block / KV tile
 constexpr int kTileBytes = kBlock * kD;
 constexpr int kMaxK = 64;        // clusters per head
+// A v_meanp row: mu_b/s_v (128 floats), the K scale of block min(b+1, last),
+// three zeros -- 528 bytes, copied into LDS next to the V tile in one go.
+constexpr int kMuStride = kD + 4;
 constexpr int kAsgTok = 1024;    // tokens per k-means assignment / sort chunk
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -100,6 +103,15 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap instructions (VALU, no LDS round trip).
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Max over a block of blockDim.x threads (multiple of 64); `red` holds >= 16 floats.

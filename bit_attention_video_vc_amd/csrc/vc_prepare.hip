@@ -370,8 +370,9 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
   if (threadIdx.x < kD) {
     const float m = v_mean[(static_cast<int64_t>(bh) * nblk + blk) * kD + threadIdx.x];
     mu[threadIdx.x] = m;
-    // restore-operand order: (d % 16) * 8 + d / 16 within the tile's 128 floats
-    v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kD + (threadIdx.x & 15) * 8 + (threadIdx.x >> 4)] = m / s_v;
+    v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kMuStride + threadIdx.x] = m / s_v;
+  } else if (threadIdx.x > kD && threadIdx.x < kMuStride) {
+    v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kMuStride + threadIdx.x] = 0.0f;   // slot kD: vc_prepare_qk
   }
   if (blk == 0 && threadIdx.x == 0) {
     hdr[bh].v_scale = s_v;
@@ -401,7 +402,7 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
 // grid (nblk, H, B), 256 threads; 4 (row, 16-channel) tasks per thread.
 template <bool GATHER>
 __global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const int32_t* perm, uint8_t* out8,
-                                                    float* scale) {
+                                                    float* scale, float* v_meanp) {
   __shared__ float red[16];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
   float val[4][16];
@@ -441,7 +442,15 @@ __global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const in
     }
     *reinterpret_cast<uint4*>(tile + row_tile_off(r, c16)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  if (threadIdx.x == 0) scale[static_cast<int64_t>(bh) * nblk + blk] = sc;
+  if (threadIdx.x == 0) {
+    scale[static_cast<int64_t>(bh) * nblk + blk] = sc;
+    if (GATHER) {
+      // K scales also go into the v_meanp rows: row b carries the scale of
+      // block min(b+1, nblk-1), the score tile that follows it.
+      if (blk > 0) v_meanp[(static_cast<int64_t>(bh) * nblk + blk - 1) * kMuStride + kD] = sc;
+      if (blk == nblk - 1) v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kMuStride + kD] = sc;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -700,9 +709,9 @@ hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& kt, int B, int
                              hipStream_t st) {
   const int nblk = (S + kBlock - 1) / kBlock;
   const dim3 gblk(nblk, H, B);
-  hipLaunchKernelGGL((k_quant_rows<false>), gblk, dim3(256), 0, st, q, S, ws.perm, ws.q8, ws.q_scale);
+  hipLaunchKernelGGL((k_quant_rows<false>), gblk, dim3(256), 0, st, q, S, ws.perm, ws.q8, ws.q_scale, nullptr);
   VC_LAUNCH_CHECK();
-  hipLaunchKernelGGL((k_quant_rows<true>), gblk, dim3(256), 0, st, kt, S, ws.perm, ws.k8, ws.k_scale);
+  hipLaunchKernelGGL((k_quant_rows<true>), gblk, dim3(256), 0, st, kt, S, ws.perm, ws.k8, ws.k_scale, ws.v_meanp);
   VC_LAUNCH_CHECK();
   if (ws.nrep > 0) {
     hipLaunchKernelGGL(k_repair_kpack, dim3(ws.nrep_pad / kBlock, H, B), dim3(256), 0, st, S, ws.nrep_pad,

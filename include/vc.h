@@ -101,7 +101,9 @@ typedef struct {
  *   k_scale f32 [BH][nblk]
  *   v8      u8  [BH][nblk] tiles: residual codes, permuted order, transposed
  *   v_mean  f32 [BH][nblk][128] block means mu_b
- *   v_meanp f32 [BH][nblk][128] mu_b / s_v, channel d stored at (d%16)*8 + d/16
+ *   v_meanp f32 [BH][nblk][132] mu_b / s_v (128 values), then the K scale
+ *               of block min(b+1, nblk-1) (written by vc_prepare_qk), then
+ *               three zeros
  *   hdr     per-(b,h) scalars, vc_head_hdr [BH]
  *   assign  i32 [BH][S] cluster id of each ORIGINAL token
  *   perm    i32 [BH][S] original token at permuted position p
