@@ -91,17 +91,19 @@ constexpr int kVBufBytes = kTileBytes + 1024;
 
 // End of a tile step: every wave waits until only the copies of its last
 // kStages-2 steps (the last (kStages-2)*kDmaPerStep vector-memory
-// instructions it issued) may still be in flight -- so the copies issued
-// kStages-2 steps earlier have landed -- and until its LDS reads have
-// returned; then the workgroup barrier.  The copies of a step are always its
-// last vector-memory instructions.
-__device__ __forceinline__ void step_barrier() {
+// instructions it issued; one fewer per step for waves other than wave 0,
+// which alone copies the v_meanp row) may still be in flight -- so the
+// copies issued kStages-2 steps earlier have landed -- and until its LDS
+// reads have returned; then the workgroup barrier.  The copies of a step are
+// always its last vector-memory instructions.
+__device__ __forceinline__ void step_barrier(int w) {
   // s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14.
   // Written as a builtin so the compiler's own wait insertion knows that
   // every older copy has landed after this point.
   constexpr int kVm = (kStages - 2) * kDmaPerStep;
-  static_assert(kVm < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((kVm & 15) | (7 << 4) | (0 << 8) | ((kVm >> 4) << 14));
+  constexpr int kVm1 = (kStages - 2) * (kDmaPerStep - 1);
+  if (w == 0) __builtin_amdgcn_s_waitcnt((kVm & 15) | (7 << 4) | (0 << 8) | ((kVm >> 4) << 14));
+  else __builtin_amdgcn_s_waitcnt((kVm1 & 15) | (7 << 4) | (0 << 8) | ((kVm1 >> 4) << 14));
   __builtin_amdgcn_s_barrier();
 }
 
@@ -116,6 +118,8 @@ __device__ __forceinline__ uint32_t expcast4(const v4f& s, float s8, float c) {
 }
 
 __device__ __forceinline__ float max4(const v4f& s) { return fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])); }
+// running max over 4 more values as two 3-input maxima
+__device__ __forceinline__ float max_acc4(float m, const v4f& s) { return fmaxf(fmaxf(fmaxf(fmaxf(m, s[0]), s[1]), s[2]), s[3]); }
 
 // Large finite stand-in for -infinity (the kernel is built without NaN/IEEE
 // canonicalisation, so it avoids infinities altogether).
@@ -229,9 +233,10 @@ struct TileAcc {
 };
 
 // The copies of one step: K(tk) into kfree, V(tv) with its v_meanp row into
-// vfree -- exactly kDmaPerStep copy instructions, issued one at a time
-// (part 0: the row, parts 1..kDmaPerTile: K, then V) at points spread over
-// the step, so that the workgroup's copies do not all queue at once.
+// vfree -- kDmaPerStep copy instructions in wave 0, one fewer in the others
+// (part 0, the row, is copied by wave 0 alone; parts 1..kDmaPerTile: K,
+// then V), issued one at a time at points spread over the step, so that the
+// workgroup's copies do not all queue at once.
 struct StepCopies {
   const TileCtx& c;
   uint32_t koff, voff, moff;
@@ -250,7 +255,7 @@ struct StepCopies {
   __device__ __forceinline__ void issue(int part) const {
     const int w = c.tid >> 6;
     if (part == 0) {
-      copy16_to_lds(c.mr, moff, vdst + kTileBytes);
+      if (w == 0) copy16_to_lds(c.mr, moff, vdst + kTileBytes);
     } else if (part <= kDmaPerTile) {
       const int j = part - 1;
       copy16_to_lds(c.kr, koff + j * (16 * kAttnThreads), kdst + j * (16 * kAttnThreads) + w * 1024);
@@ -303,7 +308,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
       const v8i vc = vop[dt & 1];
       acc.O[dt][0] = mfma_fp8(vc, acc.P[0], acc.O[dt][0]);
       if (dt < 2) {
-        mx[dt] = fmaxf(fmaxf(max4(sc[0][dt]), max4(sc[1][dt])), fmaxf(max4(sc[2][dt]), max4(sc[3][dt])));
+        mx[dt] = max_acc4(max_acc4(max_acc4(max4(sc[0][dt]), sc[1][dt]), sc[2][dt]), sc[3][dt]);
       } else {
         const int c0 = 2 * (dt - 2);
         Pn[c0 & 1][c0 >> 1] = static_cast<int>(expcast4(sc[c0 >> 1][c0 & 1], s8, cq[c0 & 1]));
@@ -314,7 +319,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
       }
       acc.O[dt][1] = mfma_fp8(vc, acc.P[1], acc.O[dt][1]);
       if (dt < 2) {
-        mx[dt] = fmaxf(mx[dt], fmaxf(fmaxf(max4(sc[4][dt]), max4(sc[5][dt])), fmaxf(max4(sc[6][dt]), max4(sc[7][dt]))));
+        mx[dt] = max_acc4(max_acc4(max_acc4(max_acc4(mx[dt], sc[4][dt]), sc[5][dt]), sc[6][dt]), sc[7][dt]);
         mx[dt] = max_over_rows(mx[dt]);
         if (dt == 1) {
 #pragma unroll
@@ -355,7 +360,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
     acc.r[qi] = r;
     acc.P[qi] = Pn[qi];
   }
-  step_barrier();
+  step_barrier(c.tid >> 6);
 }
 
 __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
