@@ -55,7 +55,7 @@ class VcAttnOpts(ctypes.Structure):
 
 class VcWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "total", "q8", "q_scale", "k8", "k_scale", "v8", "v_mean", "v_meanp", "hdr",
+        "total", "q8", "q_scale", "k8", "k_scale", "v8", "v_mean", "v_muop", "hdr",
         "assign", "perm", "rep_pos", "rep_k8", "rep_ks", "rep_e8", "scratch")] + \
         [("nblk", ctypes.c_int32), ("nrep", ctypes.c_int32), ("nrep_pad", ctypes.c_int32),
          ("reserved", ctypes.c_int32)]

@@ -96,7 +96,7 @@ vc_status make_plan(const vc_desc* vd, const vc_v_opts* o, Plan* p) {
   L.k_scale = take(sizeof(float) * per_blk);
   L.v8 = take(tiles);
   L.v_mean = take(sizeof(float) * per_blk * vc::kD);
-  L.v_meanp = take(sizeof(float) * per_blk * vc::kMuStride);
+  L.v_muop = take(static_cast<size_t>(BH) * vc::muop_rows(p->nblk) * vc::kMuOpRowBytes);
   L.hdr = take(sizeof(vc_head_hdr) * BH);
   L.assign = take(sizeof(int32_t) * BH * p->S);
   L.perm = take(sizeof(int32_t) * BH * p->S);
@@ -140,7 +140,7 @@ vc::WsPtrs ws_ptrs(const Plan& p, void* ws) {
   w.q_scale = reinterpret_cast<float*>(base + L.q_scale);
   w.k_scale = reinterpret_cast<float*>(base + L.k_scale);
   w.v_mean = reinterpret_cast<float*>(base + L.v_mean);
-  w.v_meanp = reinterpret_cast<float*>(base + L.v_meanp);
+  w.v_muop = base + L.v_muop;
   w.rep_ks = reinterpret_cast<float*>(base + L.rep_ks);
   w.hdr = reinterpret_cast<vc_head_hdr*>(base + L.hdr);
   w.assign = reinterpret_cast<int32_t*>(base + L.assign);
@@ -283,7 +283,7 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   a.k8 = w.k8;
   a.k_scale = w.k_scale;
   a.v8 = w.v8;
-  a.v_meanp = w.v_meanp;
+  a.v_muop = w.v_muop;
   a.hdr = w.hdr;
   a.rep_k8 = w.rep_k8;
   a.rep_ks = w.rep_ks;

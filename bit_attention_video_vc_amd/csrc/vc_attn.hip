@@ -20,16 +20,21 @@
 // M, not added to l) and out = bf16(s_v * (O + (s_e/s_v) O_rep) / l).
 //
 // Layout and schedule:
-//   * one workgroup = 4 waves = one 128-query block of one (b,h); wave w owns
-//     queries 32w..32w+31 as two 16-query sub-tiles;
+//   * one workgroup = 8 waves = two 128-query blocks of one (b,h); wave w
+//     owns 32 queries of block w/4 as two 16-query sub-tiles;
 //   * transposed products: S^T = K.Q^T with v_mfma_f32_16x16x128_f8f6f4, so
 //     each lane holds one query column; row max and row sum stay in-lane
-//     apart from one 4-lane combine;
+//     apart from one cross-row combine;
 //   * the S^T accumulator bytes (keys 16t+4g+i for lane group g) are exactly
 //     the B-operand slots of O^T = V^T.P^T, so P never leaves registers; the
 //     prepare stage stores V8 in that slot order;
-//   * K and V tiles (16 KB each) are staged in LDS, double buffered, loaded
-//     with 16-byte coalesced global loads, one barrier per tile;
+//   * K and V tiles (16 KB each) stream through a 4-deep LDS ring, copied
+//     straight from global memory into LDS three tiles ahead, one barrier
+//     per tile;
+//   * the block-mean restore r_b * mu_b/s_v is deferred: each tile's row sum
+//     is kept (and rescaled with O), and every 16 tiles the sums meet the
+//     prepared mu/s_v operands in 16x16x16 bf16 MFMAs (high/low bf16 parts,
+//     three products), instead of 64 fp32 FMAs per tile on the VALU;
 //   * workgroup ids are remapped so each XCD runs consecutive query blocks of
 //     the same head: its 4 MB L2 then serves the K/V stream to all of them.
 #include "vc_common.hpp"
@@ -82,28 +87,34 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 constexpr int kDmaPerTile = kTileBytes / (16 * kAttnThreads);   // copy instructions per 16 KB tile
 // LDS ring depth for K and for V tiles; copies run kStages-1 tiles ahead.
 constexpr int kStages = 4;
-constexpr int kDmaPerStep = 2 * kDmaPerTile + 1;                  // K tile, V tile, mu row + scale
-constexpr uint32_t kMuRowBytes = kMuStride * 4;                  // 528
-// A V buffer: the V tile, then its v_meanp row (mu/s_v at [0,512), the K
-// scale of the next score tile at 512) and room for the zero-filled lanes
-// 33..63 of the row copy.
-constexpr int kVBufBytes = kTileBytes + 1024;
+// Copy instructions per step: every wave copies its share of one K and one
+// V tile; wave 0 also copies the K tile's scale and one restore-operand row.
+constexpr int kDmaPerStep = 2 * kDmaPerTile;
+constexpr int kDmaPerStep0 = kDmaPerStep + 2;
+// A K buffer: the K tile, then its scale, written by every lane of a 4-byte
+// copy (256 bytes).
+constexpr int kKBufBytes = kTileBytes + 256;
+// A restore-operand group buffer: 16 rows of 512 bytes plus the landing room
+// of lanes 32..63 of the last row's copy (they carry the next row).
+constexpr int kGrpBytes = kMuOpGroup * kMuOpRowBytes + kMuOpRowBytes;
 
-// End of a tile step: every wave waits until only the copies of its last
-// kStages-2 steps (the last (kStages-2)*kDmaPerStep vector-memory
-// instructions it issued; one fewer per step for waves other than wave 0,
-// which alone copies the v_meanp row) may still be in flight -- so the
-// copies issued kStages-2 steps earlier have landed -- and until its LDS
+// End of a tile step: every wave waits until at most the (kStages-2) *
+// kDmaPerStep newest of its copies may still be in flight, and until its LDS
 // reads have returned; then the workgroup barrier.  The copies of a step are
-// always its last vector-memory instructions.
-__device__ __forceinline__ void step_barrier(int w) {
+// always its last vector-memory instructions, so for waves 1..7 (kDmaPerStep
+// copies per step) this means every copy issued kStages-2 or more steps
+// earlier has landed.  Wave 0 issues kDmaPerStep0 per step, so the same count
+// also completes all but the last two copies of the step before; its two
+// extra copies (a K scale and a restore-operand row) are read kStages-1
+// steps after issue at the earliest, and so have landed too.  One count for
+// all waves keeps the compiler's own wait analysis exact.
+__device__ __forceinline__ void step_barrier() {
   // s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14.
   // Written as a builtin so the compiler's own wait insertion knows that
   // every older copy has landed after this point.
   constexpr int kVm = (kStages - 2) * kDmaPerStep;
-  constexpr int kVm1 = (kStages - 2) * (kDmaPerStep - 1);
-  if (w == 0) __builtin_amdgcn_s_waitcnt((kVm & 15) | (7 << 4) | (0 << 8) | ((kVm >> 4) << 14));
-  else __builtin_amdgcn_s_waitcnt((kVm1 & 15) | (7 << 4) | (0 << 8) | ((kVm1 >> 4) << 14));
+  static_assert(kVm < 64 && kDmaPerStep0 - kDmaPerStep <= kDmaPerStep, "vmcnt field; wave 0 bound");
+  __builtin_amdgcn_s_waitcnt((kVm & 15) | (7 << 4) | (0 << 8) | ((kVm >> 4) << 14));
   __builtin_amdgcn_s_barrier();
 }
 
@@ -132,45 +143,25 @@ struct SoftState {
 };
 
 // Score tile of one 128-key block against this wave's two query sub-tiles.
-// The block-mean restore of the tile whose P.V follows (O^T += mu'_b . r_b,
-// 64 FMAs, mu' from the LDS row next to that tile's V codes) fills the VALU
-// slots under these MFMAs.  K operands and mu values are read from LDS two
-// sub-tiles ahead of their use (mu first, so that waiting for the older pair
-// leaves the newer one in flight); the first two V operands of the P.V that
-// follows are read in the last two sub-tiles.
+// K operands are read from LDS two sub-tiles ahead of their MFMAs; the first
+// two V operands of the P.V that follows are read in the last two
+// sub-tiles.  Copy parts go out between the MFMAs.
 template <typename Copies>
-__device__ __forceinline__ void score_tile_restore(const uint8_t* ktile, int lane, int g, const v8i (&qop)[2],
-                                                   v4f (&sc)[8][2], const uint8_t* vt, v8i (&vop)[2],
-                                                   v4f (&O)[8][2], const float (&r)[2], const Copies& cp) {
+__device__ __forceinline__ void score_tile_pipe(const uint8_t* ktile, int lane, const v8i (&qop)[2],
+                                                v4f (&sc)[8][2], const uint8_t* vt, v8i (&vop)[2],
+                                                const Copies& cp) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  const float* mrow = reinterpret_cast<const float*>(vt + kTileBytes);
   v8i kop[2];
-  float4 mu[2];
-  mu[0] = *reinterpret_cast<const float4*>(mrow + 4 * g);
   kop[0] = ld_op_lds(ktile, 0, lane);
-  mu[1] = *reinterpret_cast<const float4*>(mrow + 16 + 4 * g);
   kop[1] = ld_op_lds(ktile, 1, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const v8i cur = kop[t & 1];
-    const float4 m = mu[t & 1];
     sc[t][0] = mfma_fp8(cur, qop[0], zero);
-    O[t][0][0] = fmaf(r[0], m.x, O[t][0][0]);
-    O[t][0][1] = fmaf(r[0], m.y, O[t][0][1]);
-    O[t][0][2] = fmaf(r[0], m.z, O[t][0][2]);
-    O[t][0][3] = fmaf(r[0], m.w, O[t][0][3]);
     sc[t][1] = mfma_fp8(cur, qop[1], zero);
-    O[t][1][0] = fmaf(r[1], m.x, O[t][1][0]);
-    O[t][1][1] = fmaf(r[1], m.y, O[t][1][1]);
-    O[t][1][2] = fmaf(r[1], m.z, O[t][1][2]);
-    O[t][1][3] = fmaf(r[1], m.w, O[t][1][3]);
-    if (t + 2 < 8) {
-      mu[t & 1] = *reinterpret_cast<const float4*>(mrow + 16 * (t + 2) + 4 * g);
-      kop[t & 1] = ld_op_lds(ktile, t + 2, lane);
-    } else {
-      vop[t & 1] = ld_op_lds(vt, t - 6, lane);
-    }
+    if (t + 2 < 8) kop[t & 1] = ld_op_lds(ktile, t + 2, lane);
+    else vop[t & 1] = ld_op_lds(vt, t - 6, lane);
     if (t & 1) cp.issue(t >> 1);   // copy parts 0..3
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -218,10 +209,13 @@ __device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma,
 
 // Loop-invariant inputs of one workgroup's tile loop.
 struct TileCtx {
-  __amdgpu_buffer_rsrc_t kr, vr, mr;   // this head's K8 tiles, V8 tiles, v_meanp rows
+  __amdgpu_buffer_rsrc_t kr, vr, sr, mr;   // this head's K8 tiles, V8 tiles, K scales, restore operands
   const float* ks;          // this head's K block scales
+  const uint8_t* muop;      // this head's restore operands
+  uint8_t* grp0;            // LDS group buffers for the restore operands
+  uint8_t* grp1;            // (even and odd groups)
   float sqs, sm_scale;
-  int nblk, kval_last, tid, lane, g, l16;
+  int nblk, kval_last, tid, lane, g, l16, w;
 };
 
 // Per-wave accumulators carried across tiles.
@@ -229,73 +223,155 @@ struct TileAcc {
   v4f O[8][2];     // O^T: lane holds channels 16dt+4g+i of query l16 (+16 per sub-tile)
   v8i P[2];        // E4M3 codes of the current tile (P^T operand)
   float r[2];      // row sum of the current tile (for its block-mean restore)
+  float rr[4][2];  // deferred restore weights: lane group g, slot j holds the
+                   // row sum of tile 16G+4g+j of the current group G
   SoftState st;
 };
 
-// The copies of one step: K(tk) into kfree, V(tv) with its v_meanp row into
-// vfree -- kDmaPerStep copy instructions in wave 0, one fewer in the others
-// (part 0, the row, is copied by wave 0 alone; parts 1..kDmaPerTile: K,
-// then V), issued one at a time at points spread over the step, so that the
-// workgroup's copies do not all queue at once.
+// The copies of one step: K(tk) with its scale into kfree, V(tv) into vfree,
+// and restore-operand row `row` into its group buffer -- parts 1..kDmaPerTile
+// K, then V (every wave), part 0 the scale and part 2*kDmaPerTile+1 the row
+// (wave 0 only) -- issued one at a time at points spread over the step, so
+// that the workgroup's copies do not all queue at once.
 struct StepCopies {
   const TileCtx& c;
-  uint32_t koff, voff, moff;
+  uint32_t koff, voff, soff, roff;
   uint8_t* kdst;
   uint8_t* vdst;
-  __device__ __forceinline__ StepCopies(const TileCtx& ctx, int tk, int tv, uint8_t* kfree, uint8_t* vfree)
+  uint8_t* rdst;
+  __device__ __forceinline__ StepCopies(const TileCtx& ctx, int tk, int tv, int row, uint8_t* kfree, uint8_t* vfree)
       : c(ctx) {
     koff = static_cast<uint32_t>(tk) * kTileBytes + static_cast<uint32_t>(c.tid) * 16;
     voff = static_cast<uint32_t>(tv) * kTileBytes + static_cast<uint32_t>(c.tid) * 16;
-    // lanes 0..32 move the 528-byte row; the others read past the buffer (zeros)
-    moff = c.lane * 16 < static_cast<int>(kMuRowBytes) ? static_cast<uint32_t>(tv) * kMuRowBytes + c.lane * 16
-                                                         : static_cast<uint32_t>(c.nblk) * kMuRowBytes;
+    soff = static_cast<uint32_t>(tk) * 4;
+    roff = static_cast<uint32_t>(row) * kMuOpRowBytes + c.lane * 16;
     kdst = kfree;
     vdst = vfree;
+    rdst = ((row / kMuOpGroup) & 1 ? c.grp1 : c.grp0) + (row % kMuOpGroup) * kMuOpRowBytes;
   }
   __device__ __forceinline__ void issue(int part) const {
-    const int w = c.tid >> 6;
+    const int w = c.w;
     if (part == 0) {
-      if (w == 0) copy16_to_lds(c.mr, moff, vdst + kTileBytes);
+      if (w == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.sr, (__attribute__((address_space(3))) void*)(kdst + kTileBytes),
+                                                 4, soff, 0, 0, 0);
     } else if (part <= kDmaPerTile) {
       const int j = part - 1;
       copy16_to_lds(c.kr, koff + j * (16 * kAttnThreads), kdst + j * (16 * kAttnThreads) + w * 1024);
-    } else {
+    } else if (part <= 2 * kDmaPerTile) {
       const int j = part - 1 - kDmaPerTile;
       copy16_to_lds(c.vr, voff + j * (16 * kAttnThreads), vdst + j * (16 * kAttnThreads) + w * 1024);
+    } else {
+      if (w == 0) copy16_to_lds(c.mr, roff, rdst);
     }
   }
   __device__ __forceinline__ void issue_all() const {
 #pragma unroll
-    for (int p = 0; p < kDmaPerStep; ++p) issue(p);
+    for (int p = 0; p < 2 * kDmaPerTile + 2; ++p) issue(p);
   }
 };
 
-// One tile step kb: scores of tile kb+1 (K in kcur) with tile kb's
-// block-mean restore under them, then P.V of tile kb (V in vcur)
-// interleaved with tile kb+1's softmax, then rescale and row sum.  Copies
-// run two steps ahead: this step copies K(kb+3) into kfree and V(kb+2) into
-// vfree (triple-buffered, distinct LDS arrays, so the copies overlap the
-// reads of this step and the next), as its last vector-memory instructions
-// (see step_barrier).  Tile indices past the last tile are clamped to it and
-// a score tile past the end is masked out entirely, which leaves the state
-// unchanged (alpha = 1, codes and row sum 0): every step runs the same code.
+// Deferred block-mean restore of one group of 16 tiles:
+// O^T[dt][qi] += A_dt . B_qi over the group's tiles, A = mu/s_v (bf16 high
+// and low parts, 16 channels x 16 tiles), B = the row-sum weights (16 tiles
+// x 16 queries) split the same way; hi*hi + hi*lo + lo*hi.  A comes from
+// `ops` (lane-ordered rows, 8 bytes per lane).
+__device__ __forceinline__ v4s bf16x4_hi_lo(const float (&x)[4], v4s& lo) {
+  v4s hi;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h = f32_to_bf16_bits(x[j]);
+    hi[j] = static_cast<short>(h);
+    lo[j] = static_cast<short>(f32_to_bf16_bits(x[j] - __uint_as_float(h << 16)));
+  }
+  return hi;
+}
+__device__ __forceinline__ void restore_mfma(const v4s (&A)[8][2], const float (&rr)[4][2], v4f (&O)[8][2]) {
+  v4s bh[2], bl[2];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const float x[4] = {rr[0][qi], rr[1][qi], rr[2][qi], rr[3][qi]};
+    bh[qi] = bf16x4_hi_lo(x, bl[qi]);
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) O[dt][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[dt][0], bh[qi], O[dt][qi], 0, 0, 0);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) O[dt][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[dt][0], bl[qi], O[dt][qi], 0, 0, 0);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) O[dt][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[dt][1], bh[qi], O[dt][qi], 0, 0, 0);
+}
+
+// Restore operands of a group from its LDS buffer.  The buffer is filled by
+// copies whose completion the step barriers establish, which the compiler's
+// wait insertion cannot see through a runtime-selected buffer; the reads are
+// therefore written as one asm block that waits for its own results.
+__device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane, v4s (&A)[8][2]) {
+  const uint32_t addr =
+      static_cast<uint32_t>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)grp)) + lane * 8;
+  asm volatile(
+      "ds_read_b64 %0, %16 offset:0\n\t"
+      "ds_read_b64 %1, %16 offset:512\n\t"
+      "ds_read_b64 %2, %16 offset:1024\n\t"
+      "ds_read_b64 %3, %16 offset:1536\n\t"
+      "ds_read_b64 %4, %16 offset:2048\n\t"
+      "ds_read_b64 %5, %16 offset:2560\n\t"
+      "ds_read_b64 %6, %16 offset:3072\n\t"
+      "ds_read_b64 %7, %16 offset:3584\n\t"
+      "ds_read_b64 %8, %16 offset:4096\n\t"
+      "ds_read_b64 %9, %16 offset:4608\n\t"
+      "ds_read_b64 %10, %16 offset:5120\n\t"
+      "ds_read_b64 %11, %16 offset:5632\n\t"
+      "ds_read_b64 %12, %16 offset:6144\n\t"
+      "ds_read_b64 %13, %16 offset:6656\n\t"
+      "ds_read_b64 %14, %16 offset:7168\n\t"
+      "ds_read_b64 %15, %16 offset:7680\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(A[0][0]), "=v"(A[0][1]), "=v"(A[1][0]), "=v"(A[1][1]), "=v"(A[2][0]), "=v"(A[2][1]), "=v"(A[3][0]),
+        "=v"(A[3][1]), "=v"(A[4][0]), "=v"(A[4][1]), "=v"(A[5][0]), "=v"(A[5][1]), "=v"(A[6][0]), "=v"(A[6][1]),
+        "=v"(A[7][0]), "=v"(A[7][1])
+      : "v"(addr)
+      : "memory");
+}
+
+// One tile step kb (J = kb mod 4): scores of tile kb+1 (K in kcur), then
+// P.V of tile kb (V in vcur) interleaved with tile kb+1's softmax, then
+// rescale and row sum; tile kb's row sum joins the deferred restore weights,
+// and after the last tile of a group of 16 the group's restore runs.  Copies
+// run three steps ahead: this step copies K(kb+4) into kfree, V(kb+3) into
+// vfree and restore-operand row kb+3 (distinct LDS arrays, so the copies
+// overlap the reads of this step and the next two), as its last
+// vector-memory instructions (see step_barrier).  Tile indices past the last
+// tile are clamped to it and a score tile past the end is masked out
+// entirely, which leaves the state unchanged (alpha = 1, codes and row sum
+// 0): every step runs the same code.
+template <int J>
 __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
                                           const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2],
                                           const uint8_t* ones_lds, TileAcc& acc) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const int nblk = c.nblk, last = nblk - 1, lane = c.lane, g = c.g;
-  const int tn = kb + 1 < last ? kb + 1 : last;   // score tile (clamped)
-  const float ks_next = *reinterpret_cast<const float*>(vcur + kTileBytes + 4 * kD);
-  const StepCopies cp(c, kb + kStages < last ? kb + kStages : last,
-                      kb + kStages - 1 < last ? kb + kStages - 1 : last, kfree, vfree);
-  static_assert(kDmaPerStep == 5, "copy parts 0-3 go under the scores, part 4 under P.V");
+  const float ks_next = *reinterpret_cast<const float*>(kcur + kTileBytes);
+  const StepCopies cp(c, kb + kStages < last ? kb + kStages : last, kb + kStages - 1 < last ? kb + kStages - 1 : last,
+                      kb + kStages - 1, kfree, vfree);
+  static_assert(2 * kDmaPerTile + 2 == 6, "copy parts 0-3 go under the scores, 4-5 under P.V");
+  // tile kb's row sum becomes restore weight (tile kb%16 of its group)
+  if (g == ((kb >> 2) & 3)) {
+    acc.rr[J][0] = acc.r[0];
+    acc.rr[J][1] = acc.r[1];
+  }
 
   v8i Pn[2];
   float alpha[2];
   {
     v4f sc[8][2];
     v8i vop[2];
-    score_tile_restore(kcur, lane, g, qop, sc, vcur, vop, acc.O, acc.r, cp);
+    score_tile_pipe(kcur, lane, qop, sc, vcur, vop, cp);
     if (kb + 2 >= nblk) mask_tile(sc, g, kb + 2 == nblk ? c.kval_last : 0);
     const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
     const float s8 = 8.0f * sigma;
@@ -339,7 +415,8 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
         }
       }
       if (dt + 2 < 8) vop[dt & 1] = ld_op_lds(vcur, dt + 2, lane);
-      if (dt == 3) cp.issue(4);
+      if (dt == 2) cp.issue(4);
+      if (dt == 5) cp.issue(5);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -350,6 +427,8 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
       acc.st.l[qi] *= alpha[qi];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) acc.O[dt][qi] *= alpha[qi];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc.rr[j][qi] *= alpha[qi];
     }
   }
   const v8i ones = ld_op_lds(ones_lds, 0, lane);
@@ -360,21 +439,30 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
     acc.r[qi] = r;
     acc.P[qi] = Pn[qi];
   }
-  step_barrier(c.tid >> 6);
+  if ((kb & (kMuOpGroup - 1)) == kMuOpGroup - 1) {
+    // the group's operand rows were copied by steps kb-18 .. kb-3, which
+    // the barrier of step kb-1 has made visible
+    v4s A[8][2];
+    restore_ops_lds((kb / kMuOpGroup) & 1 ? c.grp1 : c.grp0, lane, A);
+    restore_mfma(A, acc.rr, acc.O);
+  }
+  step_barrier();
 }
 
 __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
-  // six distinct arrays (K and V triple-buffered): a copy into one provably
-  // does not alias reads of another
+  // distinct arrays for the ring slots: a copy into one provably does not
+  // alias reads of another
   static_assert(kStages == 4, "buffer declarations below");
-  __shared__ __align__(16) uint8_t kbuf0[kTileBytes];
-  __shared__ __align__(16) uint8_t kbuf1[kTileBytes];
-  __shared__ __align__(16) uint8_t kbuf2[kTileBytes];
-  __shared__ __align__(16) uint8_t kbuf3[kTileBytes];
-  __shared__ __align__(16) uint8_t vbuf0[kVBufBytes];   // V codes + the tile's mu row
-  __shared__ __align__(16) uint8_t vbuf1[kVBufBytes];
-  __shared__ __align__(16) uint8_t vbuf2[kVBufBytes];
-  __shared__ __align__(16) uint8_t vbuf3[kVBufBytes];
+  __shared__ __align__(16) uint8_t kbuf0[kKBufBytes];   // K codes + the tile's scale
+  __shared__ __align__(16) uint8_t kbuf1[kKBufBytes];
+  __shared__ __align__(16) uint8_t kbuf2[kKBufBytes];
+  __shared__ __align__(16) uint8_t kbuf3[kKBufBytes];
+  __shared__ __align__(16) uint8_t vbuf0[kTileBytes];
+  __shared__ __align__(16) uint8_t vbuf1[kTileBytes];
+  __shared__ __align__(16) uint8_t vbuf2[kTileBytes];
+  __shared__ __align__(16) uint8_t vbuf3[kTileBytes];
+  __shared__ __align__(16) uint8_t grp0[kGrpBytes];     // restore operands, even groups
+  __shared__ __align__(16) uint8_t grp1[kGrpBytes];     // odd groups
   uint8_t* const kring[kStages] = {kbuf0, kbuf1, kbuf2, kbuf3};
   uint8_t* const vring[kStages] = {vbuf0, vbuf1, vbuf2, vbuf3};
   __shared__ __align__(16) uint8_t ones_lds[2048];   // E4M3 1.0 operand for the row sums
@@ -390,7 +478,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   const int bh = logical / npair, qp = logical - bh * npair;
   const int b = bh / a.H, h = bh - b * a.H;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // wave index made provably wave-uniform (scalar branches on it)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int S = a.S;
   // waves 0-3 own query block 2*qp, waves 4-7 block 2*qp+1 (a missing second
@@ -404,13 +493,19 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   // nblk <= 2^17 (S <= 2^24), so a head's tiles span less than 4 GB
   c.kr = head_rsrc(a.k8 + static_cast<int64_t>(bh) * nblk * kTileBytes, static_cast<uint32_t>(nblk) * kTileBytes);
   c.vr = head_rsrc(a.v8 + static_cast<int64_t>(bh) * nblk * kTileBytes, static_cast<uint32_t>(nblk) * kTileBytes);
-  c.mr = head_rsrc(a.v_meanp + static_cast<int64_t>(bh) * nblk * kMuStride, static_cast<uint32_t>(nblk) * kMuRowBytes);
+  const int nrows = muop_rows(nblk);
+  c.muop = a.v_muop + static_cast<int64_t>(bh) * nrows * kMuOpRowBytes;
+  c.mr = head_rsrc(c.muop, static_cast<uint32_t>(nrows) * kMuOpRowBytes);
   c.ks = a.k_scale + static_cast<int64_t>(bh) * nblk;
+  c.sr = head_rsrc(c.ks, static_cast<uint32_t>(nblk) * 4);
+  c.grp0 = grp0;
+  c.grp1 = grp1;
   c.sqs = a.q_scale[static_cast<int64_t>(bh) * nblk + qbl];
   c.sm_scale = a.sm_scale;
   c.nblk = nblk;
   c.kval_last = S - (nblk - 1) * kBlock;          // real keys in the last tile
   c.tid = tid;
+  c.w = w;
   c.lane = lane;
   c.g = g;
   c.l16 = l16;
@@ -429,19 +524,19 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   acc.st.l[0] = acc.st.l[1] = 0.0f;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc.O[dt][0] = acc.O[dt][1] = zero;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc.rr[j][0] = acc.rr[j][1] = 0.0f;
 
-  // ---- prologue: K(0..2), V(0..1) with their mu rows into LDS; scores and
-  // codes of tile 0 ----
+  // ---- prologue: K(0..3) with scales, V(0..2) and restore-operand rows
+  // 0..2 into LDS; scores and codes of tile 0 ----
   const int last = nblk - 1;
-  // tiles 0..kStages-2: K, and V with its mu row and the scales of the tile
-  // after it; then K(kStages-1)
 #pragma unroll
   for (int j = 0; j + 1 < kStages; ++j)
-    StepCopies(c, j < last ? j : last, j < last ? j : last, kring[j], vring[j]).issue_all();
+    StepCopies(c, j < last ? j : last, j < last ? j : last, j, kring[j], vring[j]).issue_all();
   {
-    const StepCopies cp(c, kStages - 1 < last ? kStages - 1 : last, 0, kring[kStages - 1], vring[0]);
+    const StepCopies cp(c, kStages - 1 < last ? kStages - 1 : last, 0, 0, kring[kStages - 1], vring[0]);
 #pragma unroll
-    for (int p = 1; p <= kDmaPerTile; ++p) cp.issue(p);
+    for (int p = 0; p <= kDmaPerTile; ++p) cp.issue(p);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -465,20 +560,32 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   // (S = kStages), and refills kring[kb%S] with K(kb+S) and
   // vring[(kb+S-1)%S] with V(kb+S-1).  The loop is unrolled S times so that
   // every buffer is a fixed array.
+  static_assert(kStages == 4, "tile_step<J> takes J = kb mod 4");
   int kb = 0;
   for (; kb + kStages <= nblk; kb += kStages) {
-#pragma unroll
-    for (int j = 0; j < kStages; ++j)
-      tile_step(c, kb + j, kring[(j + 1) % kStages], kring[j], vring[j], vring[(j + kStages - 1) % kStages], qop,
-                ones_lds, acc);
+    tile_step<0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, ones_lds, acc);
+    tile_step<1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, ones_lds, acc);
+    tile_step<2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, ones_lds, acc);
+    tile_step<3>(c, kb + 3, kbuf0, kbuf3, vbuf3, vbuf2, qop, ones_lds, acc);
   }
-#pragma unroll
-  for (int j = 0; j + 1 < kStages; ++j)
-    if (kb + j < nblk)
-      tile_step(c, kb + j, kring[(j + 1) % kStages], kring[j], vring[j], vring[(j + kStages - 1) % kStages], qop,
-                ones_lds, acc);
+  if (kb < nblk) tile_step<0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, ones_lds, acc);
+  if (kb + 1 < nblk) tile_step<1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, ones_lds, acc);
+  if (kb + 2 < nblk) tile_step<2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, ones_lds, acc);
   // drain the copies still in flight before the workgroup retires
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // restore of the last, partial group (its operand rows may not all have
+  // been copied; read them from global memory).  Weight slots of tiles past
+  // the last hold stale sums but meet zero operands.
+  if ((last & (kMuOpGroup - 1)) != kMuOpGroup - 1) {
+    const uint8_t* rows = c.muop + static_cast<int64_t>(last / kMuOpGroup) * kMuOpGroup * kMuOpRowBytes + lane * 8;
+    v4s A[8][2];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl) A[dt][hl] = *reinterpret_cast<const v4s*>(rows + (2 * dt + hl) * kMuOpRowBytes);
+    restore_mfma(A, acc.rr, acc.O);
+  }
 
   SoftState& st = acc.st;
   v4f (&O)[8][2] = acc.O;

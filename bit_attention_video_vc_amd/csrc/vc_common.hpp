@@ -17,13 +17,22 @@ constexpr int kD = 128;          // head dimension
 constexpr int kBlock = 128;      // tokens per quantisation block / KV tile
 constexpr int kTileBytes = kBlock * kD;
 constexpr int kMaxK = 64;        // clusters per head
-// A v_meanp row: mu_b/s_v (128 floats), the K scale of block min(b+1, last),
-// three zeros -- 528 bytes, copied into LDS next to the V tile in one go.
-constexpr int kMuStride = kD + 4;
+// Block-mean restore operands (v_muop): per head, rows of 512 bytes; group
+// G = 16 consecutive blocks; row 16G + 2*dt + h holds the A operand of a
+// 16x16x16 bf16 MFMA for channels 16dt..16dt+15 and blocks 16G..16G+15 --
+// lane l's 8 bytes are 4 bf16 values for channel 16dt + l%16 and blocks
+// 16G + 4*(l/16) + j, j = 0..3 -- of the high (h = 0) or low (h = 1) bf16
+// part of mu_b/s_v.  Blocks past the last are zero; a head has
+// muop_rows(nblk) rows (room for the attention kernel to read three rows
+// past the last block).
+constexpr int kMuOpRowBytes = 512;
+constexpr int kMuOpGroup = 16;
+__host__ __device__ inline int muop_rows(int nblk) { return kMuOpGroup * ((nblk + 3 + kMuOpGroup - 1) / kMuOpGroup); }
 constexpr int kAsgTok = 1024;    // tokens per k-means assignment / sort chunk
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 // ---- input loads ------------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

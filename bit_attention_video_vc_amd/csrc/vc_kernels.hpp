@@ -17,8 +17,8 @@ struct TensorArg {
 
 // Typed pointers into one workspace.
 struct WsPtrs {
-  uint8_t *q8, *k8, *v8, *rep_k8, *rep_e8;
-  float *q_scale, *k_scale, *v_mean, *v_meanp, *rep_ks;
+  uint8_t *q8, *k8, *v8, *rep_k8, *rep_e8, *v_muop;
+  float *q_scale, *k_scale, *v_mean, *rep_ks;
   vc_head_hdr* hdr;
   int32_t *assign, *perm, *rep_pos;
   int32_t *cent, *csum, *ccount, *chunk_hist, *chunk_off;
@@ -32,7 +32,7 @@ struct AttnArgs {
   const uint8_t* k8;
   const float* k_scale;
   const uint8_t* v8;
-  const float* v_meanp;
+  const uint8_t* v_muop;
   const vc_head_hdr* hdr;
   const uint8_t* rep_k8;
   const float* rep_ks;

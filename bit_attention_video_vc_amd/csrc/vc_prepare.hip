@@ -361,18 +361,25 @@ __device__ __forceinline__ void store_tr_tile(const uint8_t* codes /*[128][128] 
 // E4M3 residual codes, written as transposed tiles; mu' = mu / s_v.
 // grid (nblk, H, B), 256 threads.
 __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const int32_t* perm, const float* v_mean,
-                                                      vc_head_hdr* hdr, uint8_t* v8, float* v_meanp) {
+                                                      vc_head_hdr* hdr, uint8_t* v8, uint8_t* v_muop) {
   __shared__ __align__(16) uint8_t codes[kTileBytes];
   __shared__ float mu[kD];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
   float s_v, inv;
   v_scales(hdr[bh], &s_v, &inv);
   if (threadIdx.x < kD) {
-    const float m = v_mean[(static_cast<int64_t>(bh) * nblk + blk) * kD + threadIdx.x];
-    mu[threadIdx.x] = m;
-    v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kMuStride + threadIdx.x] = m / s_v;
-  } else if (threadIdx.x > kD && threadIdx.x < kMuStride) {
-    v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kMuStride + threadIdx.x] = 0.0f;   // slot kD: vc_prepare_qk
+    const int ch = threadIdx.x;
+    const float m = v_mean[(static_cast<int64_t>(bh) * nblk + blk) * kD + ch];
+    mu[ch] = m;
+    // restore operand: mu/s_v split into bf16 high and low parts
+    const float mp = m / s_v;
+    const uint16_t hi = static_cast<uint16_t>(f32_to_bf16_bits(mp));
+    const uint16_t lo = static_cast<uint16_t>(f32_to_bf16_bits(mp - __uint_as_float(static_cast<uint32_t>(hi) << 16)));
+    const int p = blk % kMuOpGroup, row = (blk - p) + 2 * (ch >> 4);
+    const int off = ((p >> 2) * 16 + (ch & 15)) * 8 + (p & 3) * 2;
+    uint8_t* base = v_muop + static_cast<int64_t>(bh) * muop_rows(nblk) * kMuOpRowBytes;
+    *reinterpret_cast<uint16_t*>(base + static_cast<int64_t>(row) * kMuOpRowBytes + off) = hi;
+    *reinterpret_cast<uint16_t*>(base + static_cast<int64_t>(row + 1) * kMuOpRowBytes + off) = lo;
   }
   if (blk == 0 && threadIdx.x == 0) {
     hdr[bh].v_scale = s_v;
@@ -402,7 +409,7 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
 // grid (nblk, H, B), 256 threads; 4 (row, 16-channel) tasks per thread.
 template <bool GATHER>
 __global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const int32_t* perm, uint8_t* out8,
-                                                    float* scale, float* v_meanp) {
+                                                    float* scale) {
   __shared__ float red[16];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
   float val[4][16];
@@ -444,12 +451,6 @@ __global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const in
   }
   if (threadIdx.x == 0) {
     scale[static_cast<int64_t>(bh) * nblk + blk] = sc;
-    if (GATHER) {
-      // K scales also go into the v_meanp rows: row b carries the scale of
-      // block min(b+1, nblk-1), the score tile that follows it.
-      if (blk > 0) v_meanp[(static_cast<int64_t>(bh) * nblk + blk - 1) * kMuStride + kD] = sc;
-      if (blk == nblk - 1) v_meanp[(static_cast<int64_t>(bh) * nblk + blk) * kMuStride + kD] = sc;
-    }
   }
 }
 
@@ -686,7 +687,11 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
   }
   hipLaunchKernelGGL(k_v_block_stats, gblk, dim3(128), 0, st, v, S, o.smooth, ws.perm, ws.v_mean, ws.hdr);
   VC_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_v_quant_pack, gblk, dim3(256), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.v8, ws.v_meanp);
+  // restore operands: zero first (blocks past the last stay zero)
+  hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws.v_muop), 0u,
+                     static_cast<int64_t>(BH) * muop_rows(nblk) * (kMuOpRowBytes / 4));
+  VC_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_v_quant_pack, gblk, dim3(256), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.v8, ws.v_muop);
   VC_LAUNCH_CHECK();
   if (ws.nrep > 0) {
     const dim3 grep(ws.nrep_pad / kBlock, H, B);
@@ -709,9 +714,9 @@ hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& kt, int B, int
                              hipStream_t st) {
   const int nblk = (S + kBlock - 1) / kBlock;
   const dim3 gblk(nblk, H, B);
-  hipLaunchKernelGGL((k_quant_rows<false>), gblk, dim3(256), 0, st, q, S, ws.perm, ws.q8, ws.q_scale, nullptr);
+  hipLaunchKernelGGL((k_quant_rows<false>), gblk, dim3(256), 0, st, q, S, ws.perm, ws.q8, ws.q_scale);
   VC_LAUNCH_CHECK();
-  hipLaunchKernelGGL((k_quant_rows<true>), gblk, dim3(256), 0, st, kt, S, ws.perm, ws.k8, ws.k_scale, ws.v_meanp);
+  hipLaunchKernelGGL((k_quant_rows<true>), gblk, dim3(256), 0, st, kt, S, ws.perm, ws.k8, ws.k_scale);
   VC_LAUNCH_CHECK();
   if (ws.nrep > 0) {
     hipLaunchKernelGGL(k_repair_kpack, dim3(ws.nrep_pad / kBlock, H, B), dim3(256), 0, st, S, ws.nrep_pad,

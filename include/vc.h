@@ -101,9 +101,11 @@ typedef struct {
  *   k_scale f32 [BH][nblk]
  *   v8      u8  [BH][nblk] tiles: residual codes, permuted order, transposed
  *   v_mean  f32 [BH][nblk][128] block means mu_b
- *   v_meanp f32 [BH][nblk][132] mu_b / s_v (128 values), then the K scale
- *               of block min(b+1, nblk-1) (written by vc_prepare_qk), then
- *               three zeros
+ *   v_muop  u8  [BH][R][512] mu_b / s_v as bf16 high and low parts, laid
+ *               out as matrix-core operands; R = 16*ceil((nblk+3)/16); row
+ *               16G + 2*dt + h, lane l (8 bytes at 8*l): 4 bf16 values for
+ *               channel 16*dt + l%16 and blocks 16G + 4*(l/16) + j, j=0..3,
+ *               of the high (h=0) or low (h=1) part; zero past the last block
  *   hdr     per-(b,h) scalars, vc_head_hdr [BH]
  *   assign  i32 [BH][S] cluster id of each ORIGINAL token
  *   perm    i32 [BH][S] original token at permuted position p
@@ -121,7 +123,7 @@ typedef struct {
  */
 typedef struct {
   size_t total;
-  size_t q8, q_scale, k8, k_scale, v8, v_mean, v_meanp, hdr;
+  size_t q8, q_scale, k8, k_scale, v8, v_mean, v_muop, hdr;
   size_t assign, perm, rep_pos, rep_k8, rep_ks, rep_e8, scratch;
   int32_t nblk, nrep, nrep_pad, reserved;
 } vc_ws_layout;
@@ -151,7 +153,7 @@ vc_status vc_workspace_layout(const vc_desc* vd, const vc_v_opts* opts, vc_ws_la
  *   vd, v   : V view (device), fp16/bf16, D == 128
  *   opts    : V-Smooth options (host)
  *   ws      : workspace (device), ws_bytes >= layout.total
- * Writes assign, perm, v8, v_mean, v_meanp, hdr and the repair set. */
+ * Writes assign, perm, v8, v_mean, v_muop, hdr and the repair set. */
 vc_status vc_prepare_v(const vc_desc* vd, const void* v, const vc_v_opts* opts,
                        void* ws, size_t ws_bytes, void* stream);
 

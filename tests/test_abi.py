@@ -86,7 +86,7 @@ def test_layout_regions_are_disjoint_and_sized():
     # ceil(beta*S) with beta's fp32 value: fp32(0.05) = 0.0500000007..., so 300 tokens -> 16
     assert L.nblk == nblk and L.nrep == 16 and L.nrep_pad == 128
     need = {"q8": BH * nblk * 16384, "q_scale": 4 * BH * nblk, "k8": BH * nblk * 16384, "k_scale": 4 * BH * nblk,
-            "v8": BH * nblk * 16384, "v_mean": 4 * BH * nblk * 128, "v_meanp": 4 * BH * nblk * 132,
+            "v8": BH * nblk * 16384, "v_mean": 4 * BH * nblk * 128, "v_muop": BH * 16 * ((nblk + 3 + 15) // 16) * 512,
             "hdr": 32 * BH, "assign": 4 * BH * 300, "perm": 4 * BH * 300, "rep_pos": 4 * BH * 128,
             "rep_k8": BH * 128 * 128, "rep_ks": 4 * BH * 128, "rep_e8": BH * 128 * 128}
     spans = sorted((getattr(L, k), getattr(L, k) + v, k) for k, v in need.items())
