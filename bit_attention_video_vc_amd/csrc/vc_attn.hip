@@ -142,27 +142,64 @@ struct SoftState {
   float l[2];      // running row sum
 };
 
-// Score tile of one 128-key block against this wave's two query sub-tiles.
-// K operands are read from LDS two sub-tiles ahead of their MFMAs; the first
-// two V operands of the P.V that follows are read in the last two
-// sub-tiles.  Copy parts go out between the MFMAs.
+// Score phase of a step: the 16 MFMAs of score tile kb+1 against this
+// wave's two query sub-tiles, with the ExpCast of each 16-key sub-tile one
+// sub-tile behind its MFMAs -- speculatively, against the running maximum
+// before this tile (cq = 120 - 8*M) -- and the running max of the raw
+// scores.  If the tile raises the maximum the caller recomputes the codes
+// from sc, so the result is the same as computing the maximum first.  K
+// operands are read from LDS two sub-tiles ahead; copy parts 1..4 go out
+// between the MFMAs.
 template <typename Copies>
-__device__ __forceinline__ void score_tile_pipe(const uint8_t* ktile, int lane, const v8i (&qop)[2],
-                                                v4f (&sc)[8][2], const uint8_t* vt, v8i (&vop)[2],
-                                                const Copies& cp) {
+__device__ __forceinline__ void score_phase(const uint8_t* ktile, int lane, const v8i (&qop)[2], float s8,
+                                            const float (&cq)[2], v4f (&sc)[8][2], v8i (&Pn)[2], float (&mx)[2],
+                                            const Copies& cp) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   v8i kop[2];
   kop[0] = ld_op_lds(ktile, 0, lane);
   kop[1] = ld_op_lds(ktile, 1, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const v8i cur = kop[t & 1];
-    sc[t][0] = mfma_fp8(cur, qop[0], zero);
-    sc[t][1] = mfma_fp8(cur, qop[1], zero);
+  for (int t = 0; t < 9; ++t) {
+    if (t < 8) {
+      const v8i cur = kop[t & 1];
+      sc[t][0] = mfma_fp8(cur, qop[0], zero);
+      sc[t][1] = mfma_fp8(cur, qop[1], zero);
+    }
+    if (t >= 1) {
+      const int u = t - 1;
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        mx[qi] = u == 0 ? max4(sc[0][qi]) : max_acc4(mx[qi], sc[u][qi]);
+        Pn[qi][u] = static_cast<int>(expcast4(sc[u][qi], s8, cq[qi]));
+        // pin the speculative codes here, under the MFMAs (the compiler
+        // would otherwise sink them past the recompute branch)
+        asm volatile("" : "+v"(Pn[qi][u]));
+      }
+    }
     if (t + 2 < 8) kop[t & 1] = ld_op_lds(ktile, t + 2, lane);
-    else vop[t & 1] = ld_op_lds(vt, t - 6, lane);
-    if (t & 1) cp.issue(t >> 1);   // copy parts 0..3
+    if (t < 8 && (t & 1)) cp.issue(1 + (t >> 1));   // copy parts 1..4
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// P.V phase of a step: O^T += V^T . P^T for tile kb (16 MFMAs), V operands
+// read two sub-tiles ahead; copy parts 0 and 5 go out between the MFMAs.
+template <typename Copies>
+__device__ __forceinline__ void pv_phase(const uint8_t* vt, int lane, const v8i (&P)[2], v4f (&O)[8][2],
+                                         const Copies& cp) {
+  v8i vop[2];
+  vop[0] = ld_op_lds(vt, 0, lane);
+  vop[1] = ld_op_lds(vt, 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const v8i vc = vop[dt & 1];
+    O[dt][0] = mfma_fp8(vc, P[0], O[dt][0]);
+    O[dt][1] = mfma_fp8(vc, P[1], O[dt][1]);
+    if (dt + 2 < 8) vop[dt & 1] = ld_op_lds(vt, dt + 2, lane);
+    if (dt == 2) cp.issue(0);
+    if (dt == 5) cp.issue(5);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -339,17 +376,19 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane, v4
       : "memory");
 }
 
-// One tile step kb (J = kb mod 4): scores of tile kb+1 (K in kcur), then
-// P.V of tile kb (V in vcur) interleaved with tile kb+1's softmax, then
-// rescale and row sum; tile kb's row sum joins the deferred restore weights,
-// and after the last tile of a group of 16 the group's restore runs.  Copies
-// run three steps ahead: this step copies K(kb+4) into kfree, V(kb+3) into
-// vfree and restore-operand row kb+3 (distinct LDS arrays, so the copies
-// overlap the reads of this step and the next two), as its last
-// vector-memory instructions (see step_barrier).  Tile indices past the last
-// tile are clamped to it and a score tile past the end is masked out
-// entirely, which leaves the state unchanged (alpha = 1, codes and row sum
-// 0): every step runs the same code.
+// One tile step kb (J = kb mod 4): the score phase of tile kb+1 (K in
+// kcur), the maximum check (codes recomputed if the tile raised the maximum
+// or is ragged), the P.V phase of tile kb (V in vcur), the rescale of O, l
+// and the restore weights, and the row sum.  (Running the independent P.V
+// phase first in half of the waves measured slower.)  Tile kb's row sum joins the deferred restore weights, and after the
+// last tile of a group of 16 the group's restore runs.  Copies run three
+// steps ahead: this step copies K(kb+4) into kfree, V(kb+3) into vfree and
+// restore-operand row kb+3 (distinct LDS arrays, so the copies overlap the
+// reads of this step and the next two), as its last vector-memory
+// instructions (see step_barrier).  Tile indices past the last tile are
+// clamped to it and a score tile past the end is masked out entirely, which
+// leaves the state unchanged (alpha = 1, codes and row sum 0): every step
+// runs the same code.
 template <int J>
 __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
                                           const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2],
@@ -359,69 +398,56 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
   const float ks_next = *reinterpret_cast<const float*>(kcur + kTileBytes);
   const StepCopies cp(c, kb + kStages < last ? kb + kStages : last, kb + kStages - 1 < last ? kb + kStages - 1 : last,
                       kb + kStages - 1, kfree, vfree);
-  static_assert(2 * kDmaPerTile + 2 == 6, "copy parts 0-3 go under the scores, 4-5 under P.V");
+  static_assert(2 * kDmaPerTile + 2 == 6, "copy parts 1-4 go under the scores, 0 and 5 under P.V");
   // tile kb's row sum becomes restore weight (tile kb%16 of its group)
   if (g == ((kb >> 2) & 3)) {
     acc.rr[J][0] = acc.r[0];
     acc.rr[J][1] = acc.r[1];
   }
-
+  const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
+  const float s8 = 8.0f * sigma;
   v8i Pn[2];
   float alpha[2];
+  bool changed;
   {
     v4f sc[8][2];
-    v8i vop[2];
-    score_tile_pipe(kcur, lane, qop, sc, vcur, vop, cp);
-    if (kb + 2 >= nblk) mask_tile(sc, g, kb + 2 == nblk ? c.kval_last : 0);
-    const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
-    const float s8 = 8.0f * sigma;
-    // P.V of tile kb on the matrix core, hand-interleaved with tile kb+1's
-    // softmax on the VALU: step dt issues V^T sub-tile dt's two MFMAs with a
-    // fixed slice of the max / ExpCast work between them.
-    float mx[2], cq[2];
+    float mx[2];
+    const float cq[2] = {120.0f - 8.0f * acc.st.M[0], 120.0f - 8.0f * acc.st.M[1]};
+    score_phase(kcur, lane, qop, s8, cq, sc, Pn, mx, cp);
+    const bool ragged = kb + 2 >= nblk;
+    if (ragged) {
+      mask_tile(sc, g, kb + 2 == nblk ? c.kval_last : 0);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const v8i vc = vop[dt & 1];
-      acc.O[dt][0] = mfma_fp8(vc, acc.P[0], acc.O[dt][0]);
-      if (dt < 2) {
-        mx[dt] = max_acc4(max_acc4(max_acc4(max4(sc[0][dt]), sc[1][dt]), sc[2][dt]), sc[3][dt]);
-      } else {
-        const int c0 = 2 * (dt - 2);
-        Pn[c0 & 1][c0 >> 1] = static_cast<int>(expcast4(sc[c0 >> 1][c0 & 1], s8, cq[c0 & 1]));
-        if (dt >= 6) {
-          const int c2 = 12 + 2 * (dt - 6);
-          Pn[c2 & 1][c2 >> 1] = static_cast<int>(expcast4(sc[c2 >> 1][c2 & 1], s8, cq[c2 & 1]));
-        }
-      }
-      acc.O[dt][1] = mfma_fp8(vc, acc.P[1], acc.O[dt][1]);
-      if (dt < 2) {
-        mx[dt] = max_acc4(max_acc4(max_acc4(max_acc4(mx[dt], sc[4][dt]), sc[5][dt]), sc[6][dt]), sc[7][dt]);
-        mx[dt] = max_over_rows(mx[dt]);
-        if (dt == 1) {
+      for (int qi = 0; qi < 2; ++qi) {
+        mx[qi] = max4(sc[0][qi]);
 #pragma unroll
-          for (int qi = 0; qi < 2; ++qi) {
-            const float mn = fmaxf(acc.st.M[qi], ceilf(mx[qi] * sigma));
-            alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn, -160.0f)));
-            acc.st.M[qi] = mn;
-            cq[qi] = 120.0f - 8.0f * mn;
-          }
-        }
-      } else {
-        const int c1 = 2 * (dt - 2) + 1;
-        Pn[c1 & 1][c1 >> 1] = static_cast<int>(expcast4(sc[c1 >> 1][c1 & 1], s8, cq[c1 & 1]));
-        if (dt >= 6) {
-          const int c3 = 13 + 2 * (dt - 6);
-          Pn[c3 & 1][c3 >> 1] = static_cast<int>(expcast4(sc[c3 >> 1][c3 & 1], s8, cq[c3 & 1]));
-        }
+        for (int t = 1; t < 8; ++t) mx[qi] = max_acc4(mx[qi], sc[t][qi]);
       }
-      if (dt + 2 < 8) vop[dt & 1] = ld_op_lds(vcur, dt + 2, lane);
-      if (dt == 2) cp.issue(4);
-      if (dt == 5) cp.issue(5);
-      __builtin_amdgcn_sched_barrier(0);
+    }
+    float mn[2];
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      mx[qi] = max_over_rows(mx[qi]);
+      mn[qi] = fmaxf(acc.st.M[qi], ceilf(mx[qi] * sigma));
+    }
+    changed = __any(mn[0] != acc.st.M[0] || mn[1] != acc.st.M[1]);
+    if (changed || ragged) {
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        const float cn = 120.0f - 8.0f * mn[qi];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) Pn[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, cn));
+      }
+    }
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn[qi], -160.0f)));
+      acc.st.M[qi] = mn[qi];
     }
   }
+  pv_phase(vcur, lane, acc.P, acc.O, cp);
 
-  if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+  if (changed) {
 #pragma unroll
     for (int qi = 0; qi < 2; ++qi) {
       acc.st.l[qi] *= alpha[qi];
