@@ -114,14 +114,18 @@ def _ar1(g: torch.Generator, B: int, S: int, H: int, D: int, rho: float) -> torc
     import numpy as np
     from scipy.signal import lfilter
 
-    eps = torch.randn(B, S, H, D, generator=g).numpy().astype(np.float64)
+    eps = torch.randn(B, S, H, D, generator=g)
+    # filter along a contiguous last axis ([B,H,D,S]); the recurrence per
+    # series is the same whatever the memory layout (torch does the copies:
+    # they run on all cores)
+    e = eps.permute(0, 2, 3, 1).contiguous().double().numpy()
     c = math.sqrt(1.0 - rho * rho)
-    out = np.empty_like(eps)
-    out[:, 0] = eps[:, 0]
+    out = np.empty_like(e)
+    out[..., 0] = e[..., 0]
     if S > 1:
-        zi = (rho * eps[:, 0])[:, None]                     # filter state [B,1,H,D]
-        out[:, 1:], _ = lfilter([c], [1.0, -rho], eps[:, 1:], axis=1, zi=zi)
-    return torch.from_numpy(out.astype(np.float32))
+        zi = (rho * e[..., 0])[..., None]                   # filter state [B,H,D,1]
+        out[..., 1:], _ = lfilter([c], [1.0, -rho], e[..., 1:], axis=-1, zi=zi)
+    return torch.from_numpy(out).float().permute(0, 3, 1, 2).contiguous()
 
 
 def generate(w: Workload, device: str | torch.device = "cpu"):

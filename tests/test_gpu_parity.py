@@ -50,6 +50,29 @@ ROW_IDX = _row_tile_index()
 TR_IDX = _tr_tile_index()
 
 
+def muop_rows(nblk):
+    return 16 * ((nblk + 3 + 15) // 16)
+
+
+def decode_muop(raw: np.ndarray, nblk: int):
+    """Restore-operand rows -> (hi, lo) bf16 parts as float32 [nblk_pad, 128].
+
+    Row 16G + 2*dt + h, lane l (8 bytes at 8*l): 4 bf16 values for channel
+    16*dt + l%16 and blocks 16G + 4*(l//16) + j."""
+    u16 = raw.view(np.uint16).reshape(-1, 8, 2, 4, 16, 4)      # [G, dt, h, lane//16, lane%16, j]
+    f = (u16.astype(np.uint32) << 16).view(np.float32)
+    out = f.transpose(2, 0, 3, 5, 1, 4).reshape(2, -1, 128)   # [h, 16G + 4*(lane//16) + j, 16*dt + lane%16]
+    return out[0], out[1]
+
+
+def expected_muop(mean: np.ndarray, v_scale: float):
+    """mu/s_v in fp32, split into bf16 high part (round to nearest even) and bf16 low part."""
+    mp = torch.from_numpy(mean.astype(np.float32)) / torch.tensor(np.float32(v_scale))
+    hi = mp.to(torch.bfloat16).float()
+    lo = (mp - hi).to(torch.bfloat16).float()
+    return hi.numpy(), lo.numpy()
+
+
 def unpack_tiles(raw: np.ndarray, idx: np.ndarray) -> np.ndarray:
     """[..., ntiles*16384] bytes -> [..., ntiles*128, 128] codes (row r / key j, channel d)."""
     lead = raw.shape[:-1]
@@ -76,26 +99,32 @@ class GpuRun:
         n = count * torch.tensor([], dtype=dtype).element_size()
         return self.ws[off:off + n].view(dtype).cpu().numpy()
 
-    def views(self):
-        B, S, H, L = self.B, self.S, self.H, self.lay
-        BH, nb = B * H, L.nblk
+    def head_region(self, name, dtype, per_head, bh):
+        """One head's slice of a per-head workspace region (per_head elements each)."""
+        es = torch.tensor([], dtype=dtype).element_size()
+        off = getattr(self.lay, name) + bh * per_head * es
+        return self.ws[off:off + per_head * es].view(dtype).cpu().numpy()
+
+    def head_view(self, bh):
+        """Every prepared product of head bh, unpacked from the documented formats."""
+        S, L = self.S, self.lay
+        nb, npad = L.nblk, L.nrep_pad
         v = {
-            "perm": self.region("perm", torch.int32, BH * S).reshape(BH, S),
-            "assign": self.region("assign", torch.int32, BH * S).reshape(BH, S),
-            "q8": unpack_tiles(self.region("q8", torch.uint8, BH * nb * 16384).reshape(BH, -1), ROW_IDX),
-            "k8": unpack_tiles(self.region("k8", torch.uint8, BH * nb * 16384).reshape(BH, -1), ROW_IDX),
-            "v8": unpack_tiles(self.region("v8", torch.uint8, BH * nb * 16384).reshape(BH, -1), TR_IDX),
-            "q_scale": self.region("q_scale", torch.float32, BH * nb).reshape(BH, nb),
-            "k_scale": self.region("k_scale", torch.float32, BH * nb).reshape(BH, nb),
-            "v_mean": self.region("v_mean", torch.float32, BH * nb * 128).reshape(BH, nb, 128),
-            "hdr": self.region("hdr", torch.float32, BH * 8).reshape(BH, 8),
+            "perm": self.head_region("perm", torch.int32, S, bh),
+            "assign": self.head_region("assign", torch.int32, S, bh),
+            "q8": unpack_tiles(self.head_region("q8", torch.uint8, nb * 16384, bh), ROW_IDX),
+            "k8": unpack_tiles(self.head_region("k8", torch.uint8, nb * 16384, bh), ROW_IDX),
+            "v8": unpack_tiles(self.head_region("v8", torch.uint8, nb * 16384, bh), TR_IDX),
+            "q_scale": self.head_region("q_scale", torch.float32, nb, bh),
+            "k_scale": self.head_region("k_scale", torch.float32, nb, bh),
+            "v_mean": self.head_region("v_mean", torch.float32, nb * 128, bh).reshape(nb, 128),
+            "hdr": self.head_region("hdr", torch.float32, 8, bh),
+            "v_muop": self.head_region("v_muop", torch.uint8, muop_rows(nb) * 512, bh),
         }
-        if L.nrep_pad:
-            v["rep_pos"] = self.region("rep_pos", torch.int32, BH * L.nrep_pad).reshape(BH, L.nrep_pad)
-            v["rep_e8"] = unpack_tiles(self.region("rep_e8", torch.uint8, BH * L.nrep_pad * 128).reshape(BH, -1),
-                                       TR_IDX)
-            v["rep_k8"] = unpack_tiles(self.region("rep_k8", torch.uint8, BH * L.nrep_pad * 128).reshape(BH, -1),
-                                       ROW_IDX)
+        if npad:
+            v["rep_pos"] = self.head_region("rep_pos", torch.int32, npad, bh)
+            v["rep_e8"] = unpack_tiles(self.head_region("rep_e8", torch.uint8, npad * 128, bh), TR_IDX)
+            v["rep_k8"] = unpack_tiles(self.head_region("rep_k8", torch.uint8, npad * 128, bh), ROW_IDX)
         return v
 
 
@@ -110,43 +139,46 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
     opts = vc.v_opts(smooth, kc, iters, seed, beta)
     run = GpuRun(q, k, v, opts, sm_scale)
     B, S, H = run.B, run.S, run.H
-    qn, kn, vn = (_np(t) if t.dim() == 4 else _np(t)[None] for t in (q, k, v))
-    gv = run.views()
-    out = run.out.float().cpu().numpy()
-    if out.ndim == 3:
-        out = out[None]
+    q4, k4, v4, o4 = (t if t.dim() == 4 else t[None] for t in (q, k, v, run.out))
     sm = O.DEFAULT_SM_SCALE if sm_scale == 0.0 else np.float32(sm_scale)
     heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     errs, errs_ex = [], []
     for (b, h) in heads:
         bh = b * H + h
-        hv = O.prepare_v_head(vn[b, :, h], smooth=smooth, k=kc, iters=iters, seed=seed, bh=bh, repair_budget=beta)
-        hq = O.prepare_qk_head(qn[b, :, h], kn[b, :, h], hv.perm)
+        qn, kn, vn = (_np(t[b, :, h]) for t in (q4, k4, v4))     # this head only, as float64
+        hv = O.prepare_v_head(vn, smooth=smooth, k=kc, iters=iters, seed=seed, bh=bh, repair_budget=beta)
+        hq = O.prepare_qk_head(qn, kn, hv.perm)
         tag = f"{name} (b={b},h={h})"
-        assert np.array_equal(gv["assign"][bh], hv.assign), tag + " assign"
-        assert np.array_equal(gv["perm"][bh], hv.perm), tag + " perm"
-        assert np.array_equal(gv["q8"][bh][:S], hq.q8), tag + " q8"
-        assert not gv["q8"][bh][S:].any(), tag + " q8 padding"
-        assert np.array_equal(gv["q_scale"][bh], hq.q_scale), tag + " q_scale"
-        assert np.array_equal(gv["k8"][bh][:S], hq.k8), tag + " k8"
-        assert np.array_equal(gv["k_scale"][bh], hq.k_scale), tag + " k_scale"
-        assert np.array_equal(gv["v8"][bh][:S], hv.v8), tag + " v8"
-        assert not gv["v8"][bh][S:].any(), tag + " v8 padding"
-        assert np.array_equal(gv["v_mean"][bh], hv.mean), tag + " block means"
-        assert gv["hdr"][bh][0] == hv.v_scale, tag + " v_scale"
+        gv = run.head_view(bh)
+        nb = run.lay.nblk
+        assert np.array_equal(gv["assign"], hv.assign), tag + " assign"
+        assert np.array_equal(gv["perm"], hv.perm), tag + " perm"
+        assert np.array_equal(gv["q8"][:S], hq.q8), tag + " q8"
+        assert not gv["q8"][S:].any(), tag + " q8 padding"
+        assert np.array_equal(gv["q_scale"], hq.q_scale), tag + " q_scale"
+        assert np.array_equal(gv["k8"][:S], hq.k8), tag + " k8"
+        assert np.array_equal(gv["k_scale"], hq.k_scale), tag + " k_scale"
+        assert np.array_equal(gv["v8"][:S], hv.v8), tag + " v8"
+        assert not gv["v8"][S:].any(), tag + " v8 padding"
+        assert np.array_equal(gv["v_mean"], hv.mean), tag + " block means"
+        assert gv["hdr"][0] == hv.v_scale, tag + " v_scale"
+        mhi, mlo = decode_muop(gv["v_muop"], nb)
+        ehi, elo = expected_muop(hv.mean, hv.v_scale)
+        assert np.array_equal(mhi[:nb], ehi) and np.array_equal(mlo[:nb], elo), tag + " restore operands"
+        assert not mhi[nb:].any() and not mlo[nb:].any(), tag + " restore operand padding"
         if beta > 0:
             n = hv.rep_pos.size
-            assert np.array_equal(gv["rep_pos"][bh][:n], hv.rep_pos), tag + " repair set"
-            assert np.all(gv["rep_pos"][bh][n:] == -1)
-            assert np.array_equal(gv["rep_e8"][bh][:n], hv.rep_e8), tag + " repair codes"
-            assert np.array_equal(gv["rep_k8"][bh][:n], hq.k8[hv.rep_pos]), tag + " repair K rows"
-            assert gv["hdr"][bh][6] == hv.rep_scale, tag + " repair scale"
+            assert np.array_equal(gv["rep_pos"][:n], hv.rep_pos), tag + " repair set"
+            assert np.all(gv["rep_pos"][n:] == -1)
+            assert np.array_equal(gv["rep_e8"][:n], hv.rep_e8), tag + " repair codes"
+            assert np.array_equal(gv["rep_k8"][:n], hq.k8[hv.rep_pos]), tag + " repair K rows"
+            assert gv["hdr"][6] == hv.rep_scale, tag + " repair scale"
         r = np.arange(S) if rows is None else np.asarray(rows)
         ref = O.bf16_round(O.attend_head(hq, hv, r, sm_scale=sm))
-        got = out[b, r, h].astype(np.float64)
+        got = o4[b, :, h].float().cpu().numpy()[r].astype(np.float64)
         assert np.all(np.isfinite(got)), tag + " non-finite output"
         e = O.rel_l2(got, ref)
-        ex = O.attention_exact(qn[b, :, h], kn[b, :, h], vn[b, :, h], sm_scale=sm, rows=r)
+        ex = O.attention_exact(qn, kn, vn, sm_scale=sm, rows=r)
         e_ex = O.rel_l2(got, ex)
         errs.append(e)
         errs_ex.append(e_ex)
