@@ -14,6 +14,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,12 +40,33 @@ def parse():
     ap.add_argument("--heads", type=int, default=None, help="override H (config 4: 7, 14 or 56)")
     ap.add_argument("--seq", type=int, default=None, help="override S")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=6144, help="query rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling HBM byte counters) and exit")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_fwd_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
     return ap.parse_args()
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in ("vc_attn.hip", "vc_common.hpp", "vc_kernels.hpp"):
+        with open(os.path.join(ROOT, "bit_attention_video_vc_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(path: str, key: str):
+    """HBM bytes per attention launch from the rocprofv3 counter summary, or
+    None if there is none for this workload or the kernel sources changed since."""
+    try:
+        with open(path) as fh:
+            rec = json.load(fh).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(w, q, k, v, rows_n: int) -> dict:
@@ -154,14 +176,7 @@ def main() -> int:
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
     attn_tflops = flops / (attn_avg_ms * 1e-3) / 1e12
 
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            key = f"B{w.B}_H{w.H}_S{w.S}"
-            traffic = tj.get(key, {}).get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = traffic_bytes(args.traffic_json, f"B{w.B}_H{w.H}_S{w.S}")
 
     res = {
         "metric": "FP8 attention fwd TFLOPS + % of MI355X FP8 MFMA peak at S~73k, D=128",
