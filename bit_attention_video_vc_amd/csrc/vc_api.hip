@@ -147,6 +147,8 @@ vc::WsPtrs ws_ptrs(const Plan& p, void* ws) {
   w.perm = reinterpret_cast<int32_t*>(base + L.perm);
   w.rep_pos = reinterpret_cast<int32_t*>(base + L.rep_pos);
   w.cent = reinterpret_cast<int32_t*>(scr + p.scr.cent);
+  w.cent_op = scr + p.scr.cent_op;
+  w.cnorm = reinterpret_cast<int32_t*>(scr + p.scr.cnorm);
   w.csum = reinterpret_cast<int32_t*>(scr + p.scr.csum);
   w.ccount = reinterpret_cast<int32_t*>(scr + p.scr.ccount);
   w.chunk_hist = reinterpret_cast<int32_t*>(scr + p.scr.chunk_hist);

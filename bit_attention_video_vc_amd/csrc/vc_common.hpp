@@ -146,8 +146,11 @@ __device__ __host__ __forceinline__ uint64_t splitmix64(uint64_t z) {
 // Workspace scratch (k-means state, sort counters, repair scores), offsets
 // relative to the scratch region; computed identically on host and device.
 struct Scratch {
-  size_t cent, csum, ccount, chunk_hist, chunk_off, rep_norm, rep_sel, total;
+  size_t cent, cent_op, cnorm, csum, ccount, chunk_hist, chunk_off, rep_norm, rep_sel, total;
 };
+// Centroid operands of the assignment MFMA, per (b,h): [4 ct][4 kk][64 lanes]
+// x 16 bytes (8 bf16 values: centroid 16ct + lane%16, dims 32kk + 8(lane/16) + i).
+constexpr int kCentOpBytes = 4 * 4 * 64 * 16;
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -156,6 +159,8 @@ __host__ __device__ inline Scratch scratch_layout(int64_t BH, int S, int k, int 
   size_t o = 0;
   const int64_t nchunk = (S + kAsgTok - 1) / kAsgTok;
   s.cent = o;        o = align256(o + sizeof(int32_t) * BH * k * kD);
+  s.cent_op = o;     o = align256(o + static_cast<size_t>(BH) * kCentOpBytes);
+  s.cnorm = o;       o = align256(o + sizeof(int32_t) * BH * kMaxK);
   s.csum = o;        o = align256(o + sizeof(int32_t) * BH * k * kD);
   s.ccount = o;      o = align256(o + sizeof(int32_t) * BH * k);
   s.chunk_hist = o;  o = align256(o + sizeof(int32_t) * BH * nchunk * k);

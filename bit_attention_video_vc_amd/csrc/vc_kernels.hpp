@@ -21,7 +21,8 @@ struct WsPtrs {
   float *q_scale, *k_scale, *v_mean, *rep_ks;
   vc_head_hdr* hdr;
   int32_t *assign, *perm, *rep_pos;
-  int32_t *cent, *csum, *ccount, *chunk_hist, *chunk_off;
+  int32_t *cent, *csum, *ccount, *chunk_hist, *chunk_off, *cnorm;
+  uint8_t* cent_op;
   double* rep_norm;
   int nblk, nrep, nrep_pad;
 };

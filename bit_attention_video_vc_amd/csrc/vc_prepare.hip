@@ -50,10 +50,37 @@ __device__ __forceinline__ float sketch1(float x, int shift) {
   return fminf(fmaxf(rintf(ldexpf(x, shift)), -255.0f), 255.0f);
 }
 
+// Centroid operands and squared norms for the assignment pass, from the
+// integer centroids of one (b,h) (exact: |c| <= 255 fits bf16, norms < 2^24).
+// Called by a whole block after the centroids are final; `nthr` threads.
+__device__ void write_cent_ops(int bh, int k, const int32_t* cg, uint8_t* cent_op, int32_t* cnorm, int nthr) {
+  uint8_t* op = cent_op + static_cast<int64_t>(bh) * kCentOpBytes;
+  for (int u = threadIdx.x; u < 4 * 4 * 64; u += nthr) {
+    const int ct = u >> 8, kk = (u >> 6) & 3, lane = u & 63;
+    const int c = 16 * ct + (lane & 15), d0 = 32 * kk + 8 * (lane >> 4);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = c < k ? static_cast<float>(cg[c * kD + d0 + 2 * i]) : 0.0f;
+      const float hi = c < k ? static_cast<float>(cg[c * kD + d0 + 2 * i + 1]) : 0.0f;
+      w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);   // exact: small integers
+    }
+    *reinterpret_cast<uint4*>(op + static_cast<int64_t>(u) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  for (int c = threadIdx.x; c < kMaxK; c += nthr) {
+    int32_t n2 = 0x7FFFFFFF;                    // absent centroid: never the minimum
+    if (c < k) {
+      n2 = 0;
+      for (int d = 0; d < kD; ++d) n2 += cg[c * kD + d] * cg[c * kD + d];
+    }
+    cnorm[bh * kMaxK + c] = n2;
+  }
+}
+
 // Sketch shift and seeded strided initial centroids.  grid (BH), 128 threads.
 __global__ void __launch_bounds__(128) k_kmeans_init(TensorArg v, int S, int H, int k, uint64_t seed,
                                                      vc_head_hdr* hdr, int32_t* cent, int32_t* csum,
-                                                     int32_t* ccount) {
+                                                     int32_t* ccount, uint8_t* cent_op, int32_t* cnorm) {
   const int bh = blockIdx.x, b = bh / H, h = bh % H, d = threadIdx.x;
   const float a = __uint_as_float(hdr[bh].v_amax_bits);
   int shift = 0;
@@ -72,6 +99,8 @@ __global__ void __launch_bounds__(128) k_kmeans_init(TensorArg v, int S, int H, 
     csum[(static_cast<int64_t>(bh) * k + c) * kD + d] = 0;
   }
   if (d < k) ccount[bh * k + d] = 0;
+  __syncthreads();
+  write_cent_ops(bh, k, cent + static_cast<int64_t>(bh) * k * kD, cent_op, cnorm, 128);
 }
 
 // One Lloyd assignment pass over kAsgTok (1024) tokens per workgroup.
@@ -92,61 +121,78 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Raw 16-byte loads of one token-tile iteration (16 tokens per wave, lane
+// group g holds dims 32kk + 8g..8g+7).
+struct TokRaw {
+  uint4 r[4];
+};
+__device__ __forceinline__ TokRaw load_tok(const TensorArg& v, int b, int h, int tok, bool valid, int g) {
+  TokRaw t;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    t.r[kk] = valid ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(v.p) + b * v.sB +
+                                                      static_cast<int64_t>(tok) * v.sS + h * v.sH + 32 * kk + 8 * g)
+                    : make_uint4(0, 0, 0, 0);
+  return t;
+}
+// fp16/bf16 element -> sketch value (an integer in [-255, 255]) as bf16 bits
+__device__ __forceinline__ uint32_t sketch_bits(uint32_t e16, int dtype, int shift) {
+  const float x = dtype == VC_BF16 ? __uint_as_float(e16 << 16) : f16_bits_to_f32(e16);
+  const float s = __builtin_amdgcn_fmed3f(rintf(ldexpf(x, shift)), -255.0f, 255.0f);
+  return __float_as_uint(s) >> 16;           // exact: at most 8 significant bits
+}
+
 template <bool ACCUM, bool FINAL>
 __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k, const vc_head_hdr* hdr,
-                                                       const int32_t* cent, int32_t* csum, int32_t* ccount,
-                                                       int32_t* assign, int32_t* chunk_hist) {
+                                                       const uint8_t* cent_op, const int32_t* cnorm,
+                                                       int32_t* csum, int32_t* ccount, int32_t* assign,
+                                                       int32_t* chunk_hist) {
   __shared__ int32_t sums[ACCUM ? kMaxK * kSumPitch : 1];
-  __shared__ int32_t cnorm_s[kMaxK];
   __shared__ int32_t cnt[kMaxK];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int shift = hdr[bh].shift;
-  const int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
   if (ACCUM)
     for (int i = tid; i < k * kSumPitch; i += 256) sums[i] = 0;
   if (tid < kMaxK) cnt[tid] = 0;
-  if (tid < k) {
-    int32_t n2 = 0;
-    for (int d = 0; d < kD; ++d) {
-      const int32_t c = cg[tid * kD + d];
-      n2 += c * c;
-    }
-    cnorm_s[tid] = n2;
-  }
   const int nct = (k + 15) >> 4;
+  // centroid operands (prepared with the centroids) and norms
   v8bf ca[4][4];
+  const uint8_t* op = cent_op + static_cast<int64_t>(bh) * kCentOpBytes;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int c = 16 * ct + l16;
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        ca[ct][kk][i] = static_cast<__bf16>(c < k ? static_cast<float>(cg[c * kD + 32 * kk + 8 * g + i]) : 0.0f);
-  }
-  __syncthreads();
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 u = ct < nct ? *reinterpret_cast<const uint4*>(op + ((ct * 4 + kk) * 64 + lane) * 16)
+                               : make_uint4(0, 0, 0, 0);
+      ca[ct][kk] = __builtin_bit_cast(v8bf, u);
+    }
   int32_t cn[4][4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * ct + 4 * g + i;
-      cn[ct][i] = c < k ? cnorm_s[c] : 0x7FFFFFFF;
-    }
+    for (int i = 0; i < 4; ++i) cn[ct][i] = cnorm[bh * kMaxK + 16 * ct + 4 * g + i];
+  __syncthreads();
 
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const int s0 = blockIdx.x * kAsgTok;
-  for (int tt = 0; tt < kAsgTok / 64; ++tt) {
-    const int tok = s0 + tt * 64 + w * 16 + l16;
+  constexpr int kIters = kAsgTok / 64;
+  int tok = s0 + w * 16 + l16;
+  TokRaw nxt = load_tok(v, b, h, tok, tok < S, g);
+  for (int tt = 0; tt < kIters; ++tt) {
+    const TokRaw cur = nxt;
     const bool valid = tok < S;
+    const int tok_next = tok + 64;
+    if (tt + 1 < kIters) nxt = load_tok(v, b, h, tok_next, tok_next < S, g);   // one iteration ahead
     v8bf xb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (valid) load8(v.p, b * v.sB + tok * v.sS + h * v.sH + 32 * kk + 8 * g, v.dtype, x);
+      const uint32_t wv[4] = {cur.r[kk].x, cur.r[kk].y, cur.r[kk].z, cur.r[kk].w};
+      uint32_t pk[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xb[kk][i] = static_cast<__bf16>(sketch1(x[i], shift));
+      for (int i = 0; i < 4; ++i)
+        pk[i] = sketch_bits(wv[i] & 0xFFFFu, v.dtype, shift) | (sketch_bits(wv[i] >> 16, v.dtype, shift) << 16);
+      xb[kk] = __builtin_bit_cast(v8bf, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
     v4f acc[4] = {zero, zero, zero, zero};
 #pragma unroll
@@ -190,6 +236,7 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
             atomicAdd(&sums[bc * kSumPitch + 32 * kk + 8 * g + i], static_cast<int32_t>(static_cast<float>(xb[kk][i])));
       }
     }
+    tok = tok_next;
   }
   __syncthreads();
   if (ACCUM) {
@@ -209,7 +256,8 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
 // New centroid = floor((2*sum + n) / (2n)) (mean rounded half up); empty
 // clusters keep their centroid; sums and counts are cleared for the next pass.
 // grid (BH), 256 threads.
-__global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int32_t* csum, int32_t* ccount) {
+__global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int32_t* csum, int32_t* ccount,
+                                                      uint8_t* cent_op, int32_t* cnorm) {
   const int bh = blockIdx.x;
   int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
   int32_t* sg = csum + static_cast<int64_t>(bh) * k * kD;
@@ -225,6 +273,7 @@ __global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int
   }
   __syncthreads();
   if (threadIdx.x < k) ccount[bh * k + threadIdx.x] = 0;
+  write_cent_ops(bh, k, cg, cent_op, cnorm, 256);
 }
 
 // Per-cluster start offsets and per-chunk offsets for the stable scatter.
@@ -664,17 +713,18 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
     hipLaunchKernelGGL(k_v_absmax, dim3((S + 63) / 64, H, B), dim3(256), 0, st, v, S, ws.hdr);
     VC_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_kmeans_init, dim3(BH), dim3(128), 0, st, v, S, H, k, o.seed, ws.hdr, ws.cent, ws.csum,
-                       ws.ccount);
+                       ws.ccount, ws.cent_op, ws.cnorm);
     VC_LAUNCH_CHECK();
     for (int it = 0; it < o.iters; ++it) {
       hipLaunchKernelGGL((k_kmeans_assign<true, false>), dim3(nch, H, B), dim3(256), 0, st, v, S, k, ws.hdr,
-                         ws.cent, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
+                         ws.cent_op, ws.cnorm, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
       VC_LAUNCH_CHECK();
-      hipLaunchKernelGGL(k_kmeans_update, dim3(BH), dim3(256), 0, st, k, ws.cent, ws.csum, ws.ccount);
+      hipLaunchKernelGGL(k_kmeans_update, dim3(BH), dim3(256), 0, st, k, ws.cent, ws.csum, ws.ccount, ws.cent_op,
+                         ws.cnorm);
       VC_LAUNCH_CHECK();
     }
     hipLaunchKernelGGL((k_kmeans_assign<false, true>), dim3(nch, H, B), dim3(256), 0, st, v, S, k, ws.hdr,
-                       ws.cent, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
+                       ws.cent_op, ws.cnorm, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
     VC_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_cluster_scan, dim3(BH), dim3(64), 0, st, S, k, ws.chunk_hist, ws.chunk_off);
     VC_LAUNCH_CHECK();
