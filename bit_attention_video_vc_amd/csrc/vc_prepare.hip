@@ -142,7 +142,7 @@ __device__ __forceinline__ uint32_t sketch_bits(uint32_t e16, int dtype, int shi
   return __float_as_uint(s) >> 16;           // exact: at most 8 significant bits
 }
 
-template <bool ACCUM, bool FINAL>
+template <bool ACCUM, bool FINAL, int NCT>
 __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k, const vc_head_hdr* hdr,
                                                        const uint8_t* cent_op, const int32_t* cnorm,
                                                        int32_t* csum, int32_t* ccount, int32_t* assign,
@@ -155,21 +155,18 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
   if (ACCUM)
     for (int i = tid; i < k * kSumPitch; i += 256) sums[i] = 0;
   if (tid < kMaxK) cnt[tid] = 0;
-  const int nct = (k + 15) >> 4;
+  constexpr int nct = NCT;                     // 16-centroid tiles: ceil(k/16)
   // centroid operands (prepared with the centroids) and norms
-  v8bf ca[4][4];
+  v8bf ca[NCT][4];
   const uint8_t* op = cent_op + static_cast<int64_t>(bh) * kCentOpBytes;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint4 u = ct < nct ? *reinterpret_cast<const uint4*>(op + ((ct * 4 + kk) * 64 + lane) * 16)
-                               : make_uint4(0, 0, 0, 0);
-      ca[ct][kk] = __builtin_bit_cast(v8bf, u);
-    }
-  int32_t cn[4][4];
+    for (int kk = 0; kk < 4; ++kk)
+      ca[ct][kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(op + ((ct * 4 + kk) * 64 + lane) * 16));
+  int32_t cn[NCT][4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int i = 0; i < 4; ++i) cn[ct][i] = cnorm[bh * kMaxK + 16 * ct + 4 * g + i];
   __syncthreads();
@@ -194,19 +191,20 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
         pk[i] = sketch_bits(wv[i] & 0xFFFFu, v.dtype, shift) | (sketch_bits(wv[i] >> 16, v.dtype, shift) << 16);
       xb[kk] = __builtin_bit_cast(v8bf, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
-    v4f acc[4] = {zero, zero, zero, zero};
+    v4f acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = zero;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (ct < nct) acc[ct] = mfma_bf16(ca[ct][kk], xb[kk], acc[ct]);
+      for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma_bf16(ca[ct][kk], xb[kk], acc[ct]);
     int32_t best = 0x7FFFFFFF;
     int bc = 0;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (ct < nct && cn[ct][i] != 0x7FFFFFFF) {
+        if (cn[ct][i] != 0x7FFFFFFF) {
           const int32_t sc = cn[ct][i] - 2 * static_cast<int32_t>(acc[ct][i]);
           if (sc < best) {
             best = sc;
@@ -701,6 +699,19 @@ __global__ void __launch_bounds__(256) k_repair_kpack(int S, int nrep_pad, const
     if (_e != hipSuccess) return _e;                        \
   } while (0)
 
+template <bool ACCUM, bool FINAL>
+void launch_assign(dim3 grid, hipStream_t st, const TensorArg& v, int S, int k, const WsPtrs& ws) {
+  const int nct = (k + 15) / 16;     // 1..4 (k <= 64)
+#define VC_ASSIGN(N)                                                                                    \
+  hipLaunchKernelGGL((k_kmeans_assign<ACCUM, FINAL, N>), grid, dim3(256), 0, st, v, S, k, ws.hdr, ws.cent_op, \
+                     ws.cnorm, ws.csum, ws.ccount, ws.assign, ws.chunk_hist)
+  if (nct == 1) VC_ASSIGN(1);
+  else if (nct == 2) VC_ASSIGN(2);
+  else if (nct == 3) VC_ASSIGN(3);
+  else VC_ASSIGN(4);
+#undef VC_ASSIGN
+}
+
 hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_opts& o, const WsPtrs& ws,
                             hipStream_t st) {
   const int BH = B * H, nblk = (S + kBlock - 1) / kBlock, k = o.k;
@@ -716,15 +727,13 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
                        ws.ccount, ws.cent_op, ws.cnorm);
     VC_LAUNCH_CHECK();
     for (int it = 0; it < o.iters; ++it) {
-      hipLaunchKernelGGL((k_kmeans_assign<true, false>), dim3(nch, H, B), dim3(256), 0, st, v, S, k, ws.hdr,
-                         ws.cent_op, ws.cnorm, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
+      launch_assign<true, false>(dim3(nch, H, B), st, v, S, k, ws);
       VC_LAUNCH_CHECK();
       hipLaunchKernelGGL(k_kmeans_update, dim3(BH), dim3(256), 0, st, k, ws.cent, ws.csum, ws.ccount, ws.cent_op,
                          ws.cnorm);
       VC_LAUNCH_CHECK();
     }
-    hipLaunchKernelGGL((k_kmeans_assign<false, true>), dim3(nch, H, B), dim3(256), 0, st, v, S, k, ws.hdr,
-                       ws.cent_op, ws.cnorm, ws.csum, ws.ccount, ws.assign, ws.chunk_hist);
+    launch_assign<false, true>(dim3(nch, H, B), st, v, S, k, ws);
     VC_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_cluster_scan, dim3(BH), dim3(64), 0, st, S, k, ws.chunk_hist, ws.chunk_off);
     VC_LAUNCH_CHECK();
