@@ -71,6 +71,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Four finite values -> four OCP E4M3 codes, packed little-endian, with
+// gfx950's conversion instruction (round half to even).  For finite inputs
+// of magnitude <= 448 it gives the same bytes as e4m3_encode below -- checked
+// on the device over 2^31 inputs that include every midpoint between
+// neighbouring codes, denormals and signed zeros; the quantisers only feed it
+// x * (448 / amax) with |x| <= amax.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
 // ---- OCP E4M3FN encode: round half to even, saturate to +-448 ----------------
 // The sign bit follows the input's sign, also when the magnitude rounds to 0.
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {

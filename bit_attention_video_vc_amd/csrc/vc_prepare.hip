@@ -439,13 +439,14 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
     uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (p < S) {
       const int s = perm[static_cast<int64_t>(bh) * S + p];
-      float x[8];
+      float x[8], r[8];
       load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = e4m3_encode((x[e] - mu[c8 + e]) * inv);
+      for (int e = 0; e < 8; ++e) r[e] = (x[e] - mu[c8 + e]) * inv;
+      c[0] = e4m3_pack4(r[0], r[1], r[2], r[3]);
+      c[1] = e4m3_pack4(r[4], r[5], r[6], r[7]);
     }
-    *reinterpret_cast<uint2*>(&codes[j * kD + c8]) =
-        make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+    *reinterpret_cast<uint2*>(&codes[j * kD + c8]) = make_uint2(c[0], c[1]);
   }
   __syncthreads();
   store_tr_tile(codes, v8 + (static_cast<int64_t>(bh) * nblk + blk) * kTileBytes);
@@ -489,10 +490,8 @@ __global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const in
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) word |= e4m3_encode(val[it][4 * q + e] * inv) << (8 * e);
-      w[q] = word;
+      w[q] = e4m3_pack4(val[it][4 * q] * inv, val[it][4 * q + 1] * inv, val[it][4 * q + 2] * inv,
+                        val[it][4 * q + 3] * inv);
     }
     *reinterpret_cast<uint4*>(tile + row_tile_off(r, c16)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
