@@ -159,23 +159,25 @@ __device__ __forceinline__ void score_phase(const uint8_t* ktile, int lane, cons
   kop[0] = ld_op_lds(ktile, 0, lane);
   kop[1] = ld_op_lds(ktile, 1, lane);
   __builtin_amdgcn_sched_barrier(0);
+  // Order within sub-tile t, fixed with scheduling barriers (the scheduler
+  // would otherwise hoist the VALU work above the MFMAs and stall on their
+  // results): MFMA(t, sub-tile 0), VALU for (t-1, 0), MFMA(t, 1), VALU for
+  // (t-1, 1), then the operand loads.
 #pragma unroll
   for (int t = 0; t < 9; ++t) {
-    if (t < 8) {
-      const v8i cur = kop[t & 1];
-      sc[t][0] = mfma_fp8(cur, qop[0], zero);
-      sc[t][1] = mfma_fp8(cur, qop[1], zero);
-    }
-    if (t >= 1) {
-      const int u = t - 1;
+    const int u = t - 1;
 #pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
+    for (int qi = 0; qi < 2; ++qi) {
+      if (t < 8) sc[t][qi] = mfma_fp8(kop[t & 1], qop[qi], zero);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t >= 1) {
         mx[qi] = u == 0 ? max4(sc[0][qi]) : max_acc4(mx[qi], sc[u][qi]);
         Pn[qi][u] = static_cast<int>(expcast4(sc[u][qi], s8, cq[qi]));
         // pin the speculative codes here, under the MFMAs (the compiler
         // would otherwise sink them past the recompute branch)
-        asm volatile("" : "+v"(Pn[qi][u]));
+        asm volatile("" : "+v"(Pn[qi][u]), "+v"(mx[qi]));
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (t + 2 < 8) kop[t & 1] = ld_op_lds(ktile, t + 2, lane);
     if (t < 8 && (t & 1)) cp.issue(1 + (t >> 1));   // copy parts 1..4
