@@ -159,25 +159,23 @@ __device__ __forceinline__ void score_phase(const uint8_t* ktile, int lane, cons
   kop[0] = ld_op_lds(ktile, 0, lane);
   kop[1] = ld_op_lds(ktile, 1, lane);
   __builtin_amdgcn_sched_barrier(0);
-  // Order within sub-tile t, fixed with scheduling barriers (the scheduler
-  // would otherwise hoist the VALU work above the MFMAs and stall on their
-  // results): MFMA(t, sub-tile 0), VALU for (t-1, 0), MFMA(t, 1), VALU for
-  // (t-1, 1), then the operand loads.
 #pragma unroll
   for (int t = 0; t < 9; ++t) {
-    const int u = t - 1;
+    if (t < 8) {
+      const v8i cur = kop[t & 1];
+      sc[t][0] = mfma_fp8(cur, qop[0], zero);
+      sc[t][1] = mfma_fp8(cur, qop[1], zero);
+    }
+    if (t >= 1) {
+      const int u = t - 1;
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
-      if (t < 8) sc[t][qi] = mfma_fp8(kop[t & 1], qop[qi], zero);
-      __builtin_amdgcn_sched_barrier(0);
-      if (t >= 1) {
+      for (int qi = 0; qi < 2; ++qi) {
         mx[qi] = u == 0 ? max4(sc[0][qi]) : max_acc4(mx[qi], sc[u][qi]);
         Pn[qi][u] = static_cast<int>(expcast4(sc[u][qi], s8, cq[qi]));
         // pin the speculative codes here, under the MFMAs (the compiler
         // would otherwise sink them past the recompute branch)
-        asm volatile("" : "+v"(Pn[qi][u]), "+v"(mx[qi]));
+        asm volatile("" : "+v"(Pn[qi][u]));
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     if (t + 2 < 8) kop[t & 1] = ld_op_lds(ktile, t + 2, lane);
     if (t < 8 && (t & 1)) cp.issue(1 + (t >> 1));   // copy parts 1..4
@@ -349,7 +347,9 @@ __device__ __forceinline__ void restore_mfma(const v4s (&A)[8][2], const float (
 // Restore operands of a group from its LDS buffer.  The buffer is filled by
 // copies whose completion the step barriers establish, which the compiler's
 // wait insertion cannot see through a runtime-selected buffer; the reads are
-// therefore written as one asm block that waits for its own results.
+// therefore written as one asm block that waits for its own results.  The
+// outputs are early-clobber: the first load's result must not land in the
+// address register the later loads of the block still read.
 __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane, v4s (&A)[8][2]) {
   const uint32_t addr =
       static_cast<uint32_t>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)grp)) + lane * 8;
@@ -371,9 +371,9 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane, v4
       "ds_read_b64 %14, %16 offset:7168\n\t"
       "ds_read_b64 %15, %16 offset:7680\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(A[0][0]), "=v"(A[0][1]), "=v"(A[1][0]), "=v"(A[1][1]), "=v"(A[2][0]), "=v"(A[2][1]), "=v"(A[3][0]),
-        "=v"(A[3][1]), "=v"(A[4][0]), "=v"(A[4][1]), "=v"(A[5][0]), "=v"(A[5][1]), "=v"(A[6][0]), "=v"(A[6][1]),
-        "=v"(A[7][0]), "=v"(A[7][1])
+      : "=&v"(A[0][0]), "=&v"(A[0][1]), "=&v"(A[1][0]), "=&v"(A[1][1]), "=&v"(A[2][0]), "=&v"(A[2][1]), "=&v"(A[3][0]),
+        "=&v"(A[3][1]), "=&v"(A[4][0]), "=&v"(A[4][1]), "=&v"(A[5][0]), "=&v"(A[5][1]), "=&v"(A[6][0]), "=&v"(A[6][1]),
+        "=&v"(A[7][0]), "=&v"(A[7][1])
       : "v"(addr)
       : "memory");
 }
