@@ -31,6 +31,12 @@
 //   * K and V tiles (16 KB each) stream through a 4-deep LDS ring, copied
 //     straight from global memory into LDS three tiles ahead, one barrier
 //     per tile;
+//   * one step interleaves the score MFMAs of tile kb+1 with the P.V MFMAs
+//     of tile kb, and each MFMA carries half an ExpCast (and the running
+//     max) of an earlier score sub-tile; the codes are cast speculatively
+//     against the maximum before the tile and recast from the kept scores
+//     only when the tile raised some row's maximum (decided from each
+//     lane's partial maximum, without the cross-row combine) or is ragged;
 //   * the block-mean restore r_b * mu_b/s_v is deferred: each tile's row sum
 //     is kept (and rescaled with O), and every 16 tiles the sums meet the
 //     prepared mu/s_v operands in 16x16x16 bf16 MFMAs (high/low bf16 parts,
@@ -45,6 +51,8 @@ namespace vc {
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;   // 512: two 128-query blocks per workgroup
 constexpr float kLog2e = 1.44269504088896340736f;
+// Four E4M3 1.0 codes: the ones operand of the row-sum MFMA.
+constexpr int kOnes4 = 0x38383838;
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
   // cbsz = blgp = 0: both operands OCP E4M3; no block scales
@@ -55,6 +63,17 @@ __device__ __forceinline__ v8i ld_op_lds(const uint8_t* base, int sub, int lane)
   // operand for sub-tile `sub`: two 16-byte halves 1 KB apart
   const uint4 lo = *reinterpret_cast<const uint4*>(base + ((sub * 2) * 64 + lane) * 16);
   const uint4 hi = *reinterpret_cast<const uint4*>(base + ((sub * 2 + 1) * 64 + lane) * 16);
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+// Same, from a pointer that already includes the lane's 16-byte offset:
+// the sub-tile offsets then fit the instruction's immediate field.
+__device__ __forceinline__ v8i ld_op_lds_at(const uint8_t* p, int sub) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p + (sub * 2) * 1024);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + (sub * 2 + 1) * 1024);
   v8i r;
   r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
   r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
@@ -140,68 +159,98 @@ constexpr float kNegBig = -3.0e38f;
 struct SoftState {
   float M[2];      // integer log2 running maximum (kNegBig before the first tile)
   float l[2];      // running row sum
+  float cq[2];     // 120 - 8*M: the ExpCast constant for the current maximum
 };
 
-// Score phase of a step: the 16 MFMAs of score tile kb+1 against this
-// wave's two query sub-tiles, with the ExpCast of each 16-key sub-tile one
-// sub-tile behind its MFMAs -- speculatively, against the running maximum
-// before this tile (cq = 120 - 8*M) -- and the running max of the raw
-// scores.  If the tile raises the maximum the caller recomputes the codes
-// from sc, so the result is the same as computing the maximum first.  K
-// operands are read from LDS two sub-tiles ahead; copy parts 1..4 go out
-// between the MFMAs.
-template <typename Copies>
-__device__ __forceinline__ void score_phase(const uint8_t* ktile, int lane, const v8i (&qop)[2], float s8,
-                                            const float (&cq)[2], v4f (&sc)[8][2], v8i (&Pn)[2], float (&mx)[2],
-                                            const Copies& cp) {
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  v8i kop[2];
-  kop[0] = ld_op_lds(ktile, 0, lane);
-  kop[1] = ld_op_lds(ktile, 1, lane);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int t = 0; t < 9; ++t) {
-    if (t < 8) {
-      const v8i cur = kop[t & 1];
-      sc[t][0] = mfma_fp8(cur, qop[0], zero);
-      sc[t][1] = mfma_fp8(cur, qop[1], zero);
-    }
-    if (t >= 1) {
-      const int u = t - 1;
-#pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
-        mx[qi] = u == 0 ? max4(sc[0][qi]) : max_acc4(mx[qi], sc[u][qi]);
-        Pn[qi][u] = static_cast<int>(expcast4(sc[u][qi], s8, cq[qi]));
-        // pin the speculative codes here, under the MFMAs (the compiler
-        // would otherwise sink them past the recompute branch)
-        asm volatile("" : "+v"(Pn[qi][u]));
-      }
-    }
-    if (t + 2 < 8) kop[t & 1] = ld_op_lds(ktile, t + 2, lane);
-    if (t < 8 && (t & 1)) cp.issue(1 + (t >> 1));   // copy parts 1..4
-    __builtin_amdgcn_sched_barrier(0);
-  }
+// ExpCast and running max of half an accumulator (keys i0, i0+1 of one
+// 16-key sub-tile): two FMAs, two conversions into the packed code dword and
+// one 3-input max.
+__device__ __forceinline__ void expcast_half(const v4f& s, int i0, float s8, float c, uint32_t& w, float& mx) {
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[i0], s8, c), i0, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[i0 + 1], s8, c), i0 + 1, w);
+  mx = fmaxf(fmaxf(mx, s[i0]), s[i0 + 1]);
 }
 
-// P.V phase of a step: O^T += V^T . P^T for tile kb (16 MFMAs), V operands
-// read two sub-tiles ahead; copy parts 0 and 5 go out between the MFMAs.
+// The matrix-core work of one step, interleaved: for each 16-key/16-channel
+// sub-tile t, the score MFMAs of tile kb+1 (K in LDS, both query sub-tiles)
+// and the P.V MFMAs of tile kb (V in LDS, codes P of tile kb), then the two
+// row-sum MFMAs of tile kb (codes against a tile of E4M3 ones).  Every MFMA
+// is followed by half the ExpCast of one earlier score sub-tile (issued at
+// least two MFMAs before, so its result is ready) -- speculatively, against
+// the running maximum before this tile (cq = 120 - 8*M) -- so the vector
+// ALU work runs under the matrix core instead of after it.  Order and
+// placement are fixed with scheduling barriers.  K and V operands are read
+// from LDS two sub-tiles ahead; copy parts 0..5 go out one per sub-tile.
 template <typename Copies>
-__device__ __forceinline__ void pv_phase(const uint8_t* vt, int lane, const v8i (&P)[2], v4f (&O)[8][2],
-                                         const Copies& cp) {
-  v8i vop[2];
-  vop[0] = ld_op_lds(vt, 0, lane);
-  vop[1] = ld_op_lds(vt, 1, lane);
+__device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* vt, int lane, const v8i (&qop)[2],
+                                           const v8i (&P)[2], float s8, const float (&cq)[2], v4f (&sc)[8][2],
+                                           v8i (&Pn)[2], float (&mx)[2], v4f (&O)[8][2], float (&r)[2],
+                                           const Copies& cp) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const v8i ones = {kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4};
+  const uint8_t* kl = ktile + lane;   // lane = the lane's byte offset (16 * lane id)
+  const uint8_t* vl = vt + lane;
+  v8i kop[2], vop[2];
+  kop[0] = ld_op_lds_at(kl, 0);
+  vop[0] = ld_op_lds_at(vl, 0);
+  kop[1] = ld_op_lds_at(kl, 1);
+  vop[1] = ld_op_lds_at(vl, 1);
+  uint32_t w[8][2];
+  mx[0] = mx[1] = kNegBig;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const v8i vc = vop[dt & 1];
-    O[dt][0] = mfma_fp8(vc, P[0], O[dt][0]);
-    O[dt][1] = mfma_fp8(vc, P[1], O[dt][1]);
-    if (dt + 2 < 8) vop[dt & 1] = ld_op_lds(vt, dt + 2, lane);
-    if (dt == 2) cp.issue(0);
-    if (dt == 5) cp.issue(5);
+  for (int t = 0; t < 8; ++t) {
+    // slot 4t: scores (t, 0); ExpCast of (t-1, 1), first half
+    sc[t][0] = mfma_fp8(kop[t & 1], qop[0], zero);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t >= 1) {
+      w[t - 1][1] = 0;
+      expcast_half(sc[t - 1][1], 0, s8, cq[1], w[t - 1][1], mx[1]);
+      asm volatile("" : "+v"(w[t - 1][1]), "+v"(mx[1]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // slot 4t+1: scores (t, 1); second half of (t-1, 1)
+    sc[t][1] = mfma_fp8(kop[t & 1], qop[1], zero);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t >= 1) {
+      expcast_half(sc[t - 1][1], 2, s8, cq[1], w[t - 1][1], mx[1]);
+      Pn[1][t - 1] = static_cast<int>(w[t - 1][1]);
+      asm volatile("" : "+v"(Pn[1][t - 1]), "+v"(mx[1]));
+    }
+    if (t + 2 < 8) kop[t & 1] = ld_op_lds_at(kl, t + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // slot 4t+2: P.V channels t, query sub-tile 0; first half of (t, 0)
+    O[t][0] = mfma_fp8(vop[t & 1], P[0], O[t][0]);
+    __builtin_amdgcn_sched_barrier(0);
+    w[t][0] = 0;
+    expcast_half(sc[t][0], 0, s8, cq[0], w[t][0], mx[0]);
+    asm volatile("" : "+v"(w[t][0]), "+v"(mx[0]));
+    __builtin_amdgcn_sched_barrier(0);
+    // slot 4t+3: P.V channels t, sub-tile 1; second half of (t, 0)
+    O[t][1] = mfma_fp8(vop[t & 1], P[1], O[t][1]);
+    __builtin_amdgcn_sched_barrier(0);
+    expcast_half(sc[t][0], 2, s8, cq[0], w[t][0], mx[0]);
+    Pn[0][t] = static_cast<int>(w[t][0]);
+    asm volatile("" : "+v"(Pn[0][t]), "+v"(mx[0]));
+    if (t + 2 < 8) vop[t & 1] = ld_op_lds_at(vl, t + 2);
+    if (t < 6) cp.issue(t);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // row sums of tile kb; ExpCast of (7, 1) under them
+  const v4f r0 = mfma_fp8(ones, P[0], zero);
+  __builtin_amdgcn_sched_barrier(0);
+  w[7][1] = 0;
+  expcast_half(sc[7][1], 0, s8, cq[1], w[7][1], mx[1]);
+  asm volatile("" : "+v"(w[7][1]), "+v"(mx[1]));
+  __builtin_amdgcn_sched_barrier(0);
+  const v4f r1 = mfma_fp8(ones, P[1], zero);
+  __builtin_amdgcn_sched_barrier(0);
+  expcast_half(sc[7][1], 2, s8, cq[1], w[7][1], mx[1]);
+  Pn[1][7] = static_cast<int>(w[7][1]);
+  asm volatile("" : "+v"(Pn[1][7]), "+v"(mx[1]));
+  __builtin_amdgcn_sched_barrier(0);
+  r[0] = r0[0];
+  r[1] = r1[0];
 }
 
 // Score tile without restore (tile 0 in the prologue).
@@ -238,6 +287,7 @@ __device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma,
     const float mn = fmaxf(st.M[qi], ceilf(mx * sigma));
     alpha[qi] = st.M[qi] == kNegBig ? 0.0f : ldexpf(1.0f, static_cast<int>(fmaxf(st.M[qi] - mn, -160.0f)));
     st.M[qi] = mn;
+    st.cq[qi] = 120.0f - 8.0f * mn;
     const float c = 120.0f - 8.0f * mn;
 #pragma unroll
     for (int t = 0; t < 8; ++t) P[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, c));
@@ -253,13 +303,13 @@ struct TileCtx {
   uint8_t* grp1;            // (even and odd groups)
   float sqs, sm_scale;
   int nblk, kval_last, tid, lane, g, l16, w;
+  int lane16;   // 16 * lane, opaque to the compiler (kept in one register)
 };
 
 // Per-wave accumulators carried across tiles.
 struct TileAcc {
   v4f O[8][2];     // O^T: lane holds channels 16dt+4g+i of query l16 (+16 per sub-tile)
   v8i P[2];        // E4M3 codes of the current tile (P^T operand)
-  float r[2];      // row sum of the current tile (for its block-mean restore)
   float rr[4][2];  // deferred restore weights: lane group g, slot j holds the
                    // row sum of tile 16G+4g+j of the current group G
   SoftState st;
@@ -378,77 +428,72 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane, v4
       : "memory");
 }
 
-// One tile step kb (J = kb mod 4): the score phase of tile kb+1 (K in
-// kcur), the maximum check (codes recomputed if the tile raised the maximum
-// or is ragged), the P.V phase of tile kb (V in vcur), the rescale of O, l
-// and the restore weights, and the row sum.  (Running the independent P.V
-// phase first in half of the waves measured slower.)  Tile kb's row sum joins the deferred restore weights, and after the
-// last tile of a group of 16 the group's restore runs.  Copies run three
-// steps ahead: this step copies K(kb+4) into kfree, V(kb+3) into vfree and
-// restore-operand row kb+3 (distinct LDS arrays, so the copies overlap the
-// reads of this step and the next two), as its last vector-memory
-// instructions (see step_barrier).  Tile indices past the last tile are
-// clamped to it and a score tile past the end is masked out entirely, which
-// leaves the state unchanged (alpha = 1, codes and row sum 0): every step
-// runs the same code.
+// One tile step kb (J = kb mod 4): the interleaved MFMA phase (scores of
+// tile kb+1 with K in kcur, P.V and row sums of tile kb with V in vcur),
+// the maximum check (codes recomputed from the kept scores if the tile
+// raised the maximum or is ragged), tile kb's row sum into l and into the
+// deferred restore weights, and the rescale of O, l and the weights.
+// After the last tile of a group of 16 the group's restore runs.  Copies
+// run three steps ahead: this step copies K(kb+4) into kfree, V(kb+3) into
+// vfree and restore-operand row kb+3 (distinct LDS arrays, so the copies
+// overlap the reads of this step and the next two), as its last
+// vector-memory instructions (see step_barrier).  Tile indices past the
+// last tile are clamped to it and a score tile past the end is masked out
+// entirely, which leaves the state unchanged (alpha = 1, codes 0): every
+// step runs the same code.
 template <int J>
 __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
-                                          const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2],
-                                          const uint8_t* ones_lds, TileAcc& acc) {
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                                          const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2], TileAcc& acc) {
   const int nblk = c.nblk, last = nblk - 1, lane = c.lane, g = c.g;
   const float ks_next = *reinterpret_cast<const float*>(kcur + kTileBytes);
   const StepCopies cp(c, kb + kStages < last ? kb + kStages : last, kb + kStages - 1 < last ? kb + kStages - 1 : last,
                       kb + kStages - 1, kfree, vfree);
-  static_assert(2 * kDmaPerTile + 2 == 6, "copy parts 1-4 go under the scores, 0 and 5 under P.V");
-  // tile kb's row sum becomes restore weight (tile kb%16 of its group)
-  if (g == ((kb >> 2) & 3)) {
-    acc.rr[J][0] = acc.r[0];
-    acc.rr[J][1] = acc.r[1];
-  }
+  static_assert(2 * kDmaPerTile + 2 == 6, "six copy parts, one per sub-tile");
   const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
   const float s8 = 8.0f * sigma;
   v8i Pn[2];
-  float alpha[2];
+  float alpha[2], r[2];
   bool changed;
   {
     v4f sc[8][2];
     float mx[2];
-    const float cq[2] = {120.0f - 8.0f * acc.st.M[0], 120.0f - 8.0f * acc.st.M[1]};
-    score_phase(kcur, lane, qop, s8, cq, sc, Pn, mx, cp);
+    mfma_phase(kcur, vcur, c.lane16, qop, acc.P, s8, acc.st.cq, sc, Pn, mx, acc.O, r, cp);
     const bool ragged = kb + 2 >= nblk;
-    if (ragged) {
-      mask_tile(sc, g, kb + 2 == nblk ? c.kval_last : 0);
+    // Did any row's maximum rise?  ceil(fl(m*sigma)) > M for an integer M
+    // exactly when fl(m*sigma) > M, and fl(m*sigma) is monotone in m, so
+    // each lane's partial maximum decides without the cross-row combine.
+    changed = __any(mx[0] * sigma > acc.st.M[0] || mx[1] * sigma > acc.st.M[1]);
+    if (__builtin_expect(changed || ragged, 0)) {
+      if (ragged) {
+        mask_tile(sc, g, kb + 2 == nblk ? c.kval_last : 0);
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi) {
+          mx[qi] = max4(sc[0][qi]);
+#pragma unroll
+          for (int t = 1; t < 8; ++t) mx[qi] = max_acc4(mx[qi], sc[t][qi]);
+        }
+      }
+      float mn[2];
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) mn[qi] = fmaxf(acc.st.M[qi], ceilf(max_over_rows(mx[qi]) * sigma));
+      changed = __any(mn[0] != acc.st.M[0] || mn[1] != acc.st.M[1]);
 #pragma unroll
       for (int qi = 0; qi < 2; ++qi) {
-        mx[qi] = max4(sc[0][qi]);
+        alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn[qi], -160.0f)));
+        acc.st.M[qi] = mn[qi];
+        acc.st.cq[qi] = 120.0f - 8.0f * mn[qi];
 #pragma unroll
-        for (int t = 1; t < 8; ++t) mx[qi] = max_acc4(mx[qi], sc[t][qi]);
+        for (int t = 0; t < 8; ++t) Pn[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, acc.st.cq[qi]));
       }
-    }
-    float mn[2];
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
-      mx[qi] = max_over_rows(mx[qi]);
-      mn[qi] = fmaxf(acc.st.M[qi], ceilf(mx[qi] * sigma));
-    }
-    changed = __any(mn[0] != acc.st.M[0] || mn[1] != acc.st.M[1]);
-    if (changed || ragged) {
-#pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
-        const float cn = 120.0f - 8.0f * mn[qi];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) Pn[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, cn));
-      }
-    }
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
-      alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn[qi], -160.0f)));
-      acc.st.M[qi] = mn[qi];
     }
   }
-  pv_phase(vcur, lane, acc.P, acc.O, cp);
-
+  // tile kb's row sum: into l, and restore weight (tile kb%16 of its group)
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) acc.st.l[qi] += r[qi];
+  if ((c.lane16 >> 8) == ((kb >> 2) & 3)) {   // lane group g = lane / 16
+    acc.rr[J][0] = r[0];
+    acc.rr[J][1] = r[1];
+  }
   if (changed) {
 #pragma unroll
     for (int qi = 0; qi < 2; ++qi) {
@@ -459,14 +504,8 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
       for (int j = 0; j < 4; ++j) acc.rr[j][qi] *= alpha[qi];
     }
   }
-  const v8i ones = ld_op_lds(ones_lds, 0, lane);
-#pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    const float r = mfma_fp8(ones, Pn[qi], zero)[0];
-    acc.st.l[qi] += r;
-    acc.r[qi] = r;
-    acc.P[qi] = Pn[qi];
-  }
+  acc.P[0] = Pn[0];
+  acc.P[1] = Pn[1];
   if ((kb & (kMuOpGroup - 1)) == kMuOpGroup - 1) {
     // the group's operand rows were copied by steps kb-18 .. kb-3, which
     // the barrier of step kb-1 has made visible
@@ -493,7 +532,6 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   __shared__ __align__(16) uint8_t grp1[kGrpBytes];     // odd groups
   uint8_t* const kring[kStages] = {kbuf0, kbuf1, kbuf2, kbuf3};
   uint8_t* const vring[kStages] = {vbuf0, vbuf1, vbuf2, vbuf3};
-  __shared__ __align__(16) uint8_t ones_lds[2048];   // E4M3 1.0 operand for the row sums
 
   // XCD-aware order: hardware deals workgroup ids round-robin over 8 XCDs;
   // give XCD x a contiguous range of (head, query-block pair) work items.
@@ -535,6 +573,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   c.tid = tid;
   c.w = w;
   c.lane = lane;
+  {
+    int l16b = lane * 16;
+    asm volatile("" : "+v"(l16b));
+    c.lane16 = l16b;
+  }
   c.g = g;
   c.l16 = l16;
   const float sqs = c.sqs;
@@ -544,7 +587,6 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   qop[0] = ld_op_global(qtile, 2 * wq, lane);
   qop[1] = ld_op_global(qtile, 2 * wq + 1, lane);
 
-  for (int i = tid; i < 2048 / 4; i += kAttnThreads) reinterpret_cast<uint32_t*>(ones_lds)[i] = 0x38383838u;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   TileAcc acc;
@@ -574,13 +616,6 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
     if (nblk == 1 && c.kval_last < kBlock) mask_tile(sc, g, c.kval_last);
     float alpha[2];
     softmax_tile(sc, ((sqs * c.ks[0]) * a.sm_scale) * kLog2e, acc.st, alpha, acc.P);
-    const v8i ones = ld_op_lds(ones_lds, 0, lane);
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
-      const float r = mfma_fp8(ones, acc.P[qi], zero)[0];
-      acc.st.l[qi] = r;
-      acc.r[qi] = r;
-    }
   }
   __syncthreads();   // kring[0] (K(0)) is refilled in the first step
 
@@ -591,14 +626,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   static_assert(kStages == 4, "tile_step<J> takes J = kb mod 4");
   int kb = 0;
   for (; kb + kStages <= nblk; kb += kStages) {
-    tile_step<0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, ones_lds, acc);
-    tile_step<1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, ones_lds, acc);
-    tile_step<2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, ones_lds, acc);
-    tile_step<3>(c, kb + 3, kbuf0, kbuf3, vbuf3, vbuf2, qop, ones_lds, acc);
+    tile_step<0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, acc);
+    tile_step<1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, acc);
+    tile_step<2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, acc);
+    tile_step<3>(c, kb + 3, kbuf0, kbuf3, vbuf3, vbuf2, qop, acc);
   }
-  if (kb < nblk) tile_step<0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, ones_lds, acc);
-  if (kb + 1 < nblk) tile_step<1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, ones_lds, acc);
-  if (kb + 2 < nblk) tile_step<2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, ones_lds, acc);
+  if (kb < nblk) tile_step<0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, acc);
+  if (kb + 1 < nblk) tile_step<1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, acc);
+  if (kb + 2 < nblk) tile_step<2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, acc);
   // drain the copies still in flight before the workgroup retires
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
