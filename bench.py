@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=6144, help="query rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling HBM byte counters) and exit")
+    ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, keep launching the attention kernel for SECONDS "
+                         "(a steady load for sampling power and clocks with amd-smi)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_fwd_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -212,6 +215,16 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    if args.hold > 0:
+        n_hold, t_hold0 = 0, time.perf_counter()
+        while time.perf_counter() - t_hold0 < args.hold:
+            for _ in range(10):
+                vc.vc_attention_fwd(out, opts, ws, 0.0, stream)
+            torch.cuda.synchronize()
+            n_hold += 10
+            log(f"hold: {n_hold} launches")
+        t_hold = time.perf_counter() - t_hold0
+        res["hold"] = {"seconds": round(t_hold, 2), "launches": n_hold, "avg_ms": round(1e3 * t_hold / n_hold, 3)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
