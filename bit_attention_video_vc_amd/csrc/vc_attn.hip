@@ -328,10 +328,12 @@ struct StepCopies {
   uint8_t* rdst;
   __device__ __forceinline__ StepCopies(const TileCtx& ctx, int tk, int tv, int row, uint8_t* kfree, uint8_t* vfree)
       : c(ctx) {
-    koff = static_cast<uint32_t>(tk) * kTileBytes + static_cast<uint32_t>(c.tid) * 16;
-    voff = static_cast<uint32_t>(tv) * kTileBytes + static_cast<uint32_t>(c.tid) * 16;
+    // per-lane parts from the one lane-offset register (16 * tid = 1024 * w + 16 * lane)
+    const uint32_t tid16 = static_cast<uint32_t>(c.w) * 1024 + static_cast<uint32_t>(c.lane16);
+    koff = static_cast<uint32_t>(tk) * kTileBytes + tid16;
+    voff = static_cast<uint32_t>(tv) * kTileBytes + tid16;
     soff = static_cast<uint32_t>(tk) * 4;
-    roff = static_cast<uint32_t>(row) * kMuOpRowBytes + c.lane * 16;
+    roff = static_cast<uint32_t>(row) * kMuOpRowBytes + static_cast<uint32_t>(c.lane16);
     kdst = kfree;
     vdst = vfree;
     rdst = ((row / kMuOpGroup) & 1 ? c.grp1 : c.grp0) + (row % kMuOpGroup) * kMuOpRowBytes;
@@ -373,25 +375,34 @@ __device__ __forceinline__ v4s bf16x4_hi_lo(const float (&x)[4], v4s& lo) {
   }
   return hi;
 }
-__device__ __forceinline__ void restore_mfma(const v4s (&A)[8][2], const float (&rr)[4][2], v4f (&O)[8][2]) {
-  v4s bh[2], bl[2];
+// The B operands of the restore: the weights split into bf16 high and low
+// parts.
+__device__ __forceinline__ void restore_weights(const float (&rr)[4][2], v4s (&bh)[2], v4s (&bl)[2]) {
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
     const float x[4] = {rr[0][qi], rr[1][qi], rr[2][qi], rr[3][qi]};
     bh[qi] = bf16x4_hi_lo(x, bl[qi]);
   }
+}
+// Restore MFMAs for the channel sub-tiles dt0 .. dt0+ND-1 (A[i] for dt0+i).
+template <int ND>
+__device__ __forceinline__ void restore_mfma(const v4s (&A)[ND][2], int dt0, const v4s (&bh)[2], const v4s (&bl)[2],
+                                             v4f (&O)[8][2]) {
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int i = 0; i < ND; ++i)
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi) O[dt][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[dt][0], bh[qi], O[dt][qi], 0, 0, 0);
+    for (int qi = 0; qi < 2; ++qi)
+      O[dt0 + i][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[i][0], bh[qi], O[dt0 + i][qi], 0, 0, 0);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int i = 0; i < ND; ++i)
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi) O[dt][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[dt][0], bl[qi], O[dt][qi], 0, 0, 0);
+    for (int qi = 0; qi < 2; ++qi)
+      O[dt0 + i][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[i][0], bl[qi], O[dt0 + i][qi], 0, 0, 0);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int i = 0; i < ND; ++i)
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi) O[dt][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[dt][1], bh[qi], O[dt][qi], 0, 0, 0);
+    for (int qi = 0; qi < 2; ++qi)
+      O[dt0 + i][qi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[i][1], bh[qi], O[dt0 + i][qi], 0, 0, 0);
 }
 
 // Restore operands of a group from its LDS buffer.  The buffer is filled by
@@ -400,30 +411,23 @@ __device__ __forceinline__ void restore_mfma(const v4s (&A)[8][2], const float (
 // therefore written as one asm block that waits for its own results.  The
 // outputs are early-clobber: the first load's result must not land in the
 // address register the later loads of the block still read.
-__device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane, v4s (&A)[8][2]) {
-  const uint32_t addr =
-      static_cast<uint32_t>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)grp)) + lane * 8;
+__device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane16, int half, v4s (&A)[4][2]) {
+  // rows 2*dt + h for dt = 4*half .. 4*half+3: 8 consecutive rows; 8 bytes
+  // per lane (lane16 = 16 * lane)
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)grp)) +
+                        half * 8 * kMuOpRowBytes + (static_cast<uint32_t>(lane16) >> 1);
   asm volatile(
-      "ds_read_b64 %0, %16 offset:0\n\t"
-      "ds_read_b64 %1, %16 offset:512\n\t"
-      "ds_read_b64 %2, %16 offset:1024\n\t"
-      "ds_read_b64 %3, %16 offset:1536\n\t"
-      "ds_read_b64 %4, %16 offset:2048\n\t"
-      "ds_read_b64 %5, %16 offset:2560\n\t"
-      "ds_read_b64 %6, %16 offset:3072\n\t"
-      "ds_read_b64 %7, %16 offset:3584\n\t"
-      "ds_read_b64 %8, %16 offset:4096\n\t"
-      "ds_read_b64 %9, %16 offset:4608\n\t"
-      "ds_read_b64 %10, %16 offset:5120\n\t"
-      "ds_read_b64 %11, %16 offset:5632\n\t"
-      "ds_read_b64 %12, %16 offset:6144\n\t"
-      "ds_read_b64 %13, %16 offset:6656\n\t"
-      "ds_read_b64 %14, %16 offset:7168\n\t"
-      "ds_read_b64 %15, %16 offset:7680\n\t"
+      "ds_read_b64 %0, %8 offset:0\n\t"
+      "ds_read_b64 %1, %8 offset:512\n\t"
+      "ds_read_b64 %2, %8 offset:1024\n\t"
+      "ds_read_b64 %3, %8 offset:1536\n\t"
+      "ds_read_b64 %4, %8 offset:2048\n\t"
+      "ds_read_b64 %5, %8 offset:2560\n\t"
+      "ds_read_b64 %6, %8 offset:3072\n\t"
+      "ds_read_b64 %7, %8 offset:3584\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(A[0][0]), "=&v"(A[0][1]), "=&v"(A[1][0]), "=&v"(A[1][1]), "=&v"(A[2][0]), "=&v"(A[2][1]), "=&v"(A[3][0]),
-        "=&v"(A[3][1]), "=&v"(A[4][0]), "=&v"(A[4][1]), "=&v"(A[5][0]), "=&v"(A[5][1]), "=&v"(A[6][0]), "=&v"(A[6][1]),
-        "=&v"(A[7][0]), "=&v"(A[7][1])
+        "=&v"(A[3][1])
       : "v"(addr)
       : "memory");
 }
@@ -509,9 +513,16 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
   if ((kb & (kMuOpGroup - 1)) == kMuOpGroup - 1) {
     // the group's operand rows were copied by steps kb-18 .. kb-3, which
     // the barrier of step kb-1 has made visible
-    v4s A[8][2];
-    restore_ops_lds((kb / kMuOpGroup) & 1 ? c.grp1 : c.grp0, lane, A);
-    restore_mfma(A, acc.rr, acc.O);
+    // in two halves of four channel sub-tiles (fewer live registers)
+    const uint8_t* grp = (kb / kMuOpGroup) & 1 ? c.grp1 : c.grp0;
+    v4s bh[2], bl[2];
+    restore_weights(acc.rr, bh, bl);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      v4s A[4][2];
+      restore_ops_lds(grp, c.lane16, half, A);
+      restore_mfma<4>(A, 4 * half, bh, bl, acc.O);
+    }
   }
   step_barrier();
 }
@@ -647,7 +658,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl) A[dt][hl] = *reinterpret_cast<const v4s*>(rows + (2 * dt + hl) * kMuOpRowBytes);
-    restore_mfma(A, acc.rr, acc.O);
+    v4s bh[2], bl[2];
+    restore_weights(acc.rr, bh, bl);
+    restore_mfma<8>(A, 0, bh, bl, acc.O);
   }
 
   SoftState& st = acc.st;
