@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
                     help="after the timed steps, keep launching the attention kernel for SECONDS "
                          "(a steady load for sampling power and clocks with amd-smi)")
+    ap.add_argument("--ablation-exp", action="store_true",
+                    help="also time the attention kernel of libvc_ablation_exp.so (FP32 exponential + E4M3 cast "
+                         "instead of ExpCast) on the same prepared workspace")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_fwd_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -215,6 +218,31 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    if args.ablation_exp:
+        main_lib = vc.lib_path
+        vc.use_library(vc.ablation_exp_lib_path)
+        log(f"ablation build: {vc.lib().vc_version().decode()}")
+        for _ in range(2):
+            vc.vc_attention_fwd(out, opts, ws, 0.0, stream)
+        abl = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in abl:
+            a.record(stream)
+            vc.vc_attention_fwd(out, opts, ws, 0.0, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        abl_ms = sum(a.elapsed_time(b) for a, b in abl) / len(abl)
+        vc.use_library(main_lib)
+        # the ExpCast kernel again, right after, on the same box state
+        for a, b in abl:
+            a.record(stream)
+            vc.vc_attention_fwd(out, opts, ws, 0.0, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ref_ms = sum(a.elapsed_time(b) for a, b in abl) / len(abl)
+        res["ablation_exp_cast"] = {
+            "what": "attention kernel with an FP32 exponential (v_exp_f32) and an E4M3 cast in place of ExpCast",
+            "kernel_ms": round(abl_ms, 4), "tflops": round(flops / (abl_ms * 1e-3) / 1e12, 2),
+            "expcast_kernel_ms": round(ref_ms, 4), "expcast_speedup": round(abl_ms / ref_ms, 4)}
     if args.hold > 0:
         n_hold, t_hold0 = 0, time.perf_counter()
         while time.perf_counter() - t_hold0 < args.hold:

@@ -22,12 +22,15 @@ import torch
 
 __all__ = [
     "VcDesc", "VcVOpts", "VcAttnOpts", "VcWsLayout", "VcHeadHdr", "VCError", "lib", "lib_path",
+    "ablation_exp_lib_path", "use_library",
     "v_opts", "desc_of", "vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd",
     "alloc_workspace", "attention", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libvc.so")
+# Measurement build: FP32 exponential + E4M3 cast in place of ExpCast.
+ablation_exp_lib_path = os.path.join(_HERE, "libvc_ablation_exp.so")
 
 VC_OK, VC_ERR_ARG, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_DEVICE = range(5)
 VC_F16, VC_BF16 = 0, 1
@@ -98,6 +101,14 @@ def lib() -> ctypes.CDLL:
             getattr(L, f).restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def use_library(path: str) -> None:
+    """Make the binding call the library at `path` from now on (e.g. the
+    ExpCast ablation build); it is loaded on the next call."""
+    global _lib, lib_path
+    lib_path = path
+    _lib = None
 
 
 def _check(status: int) -> None:

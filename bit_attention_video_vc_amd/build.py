@@ -3,7 +3,11 @@
     python -m bit_attention_video_vc_amd.build
 
 The library is written next to this file so that it travels with the source
-tree; nothing is installed.
+tree; nothing is installed.  A second library, libvc_ablation_exp.so, is
+built from the same sources with VC_ABLATION_EXP_CAST: the attention kernel
+with an FP32 exponential and an E4M3 cast in place of ExpCast, for measuring
+what ExpCast saves (it is not the method; the benchmark times it beside
+libvc.so on request).
 """
 from __future__ import annotations
 
@@ -16,6 +20,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libvc.so")
+ABLATION_EXP_LIB = os.path.join(HERE, "libvc_ablation_exp.so")
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -45,7 +50,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def _build_lib(out: str, defines: list[str], tag: str, verbose: bool) -> str:
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
     objdir = os.path.join(HERE, "_build")
@@ -53,14 +58,25 @@ def build(verbose: bool = False) -> str:
     compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
     objs = []
     for src in srcs:
-        obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [hipcc(), *compile_flags, *PER_FILE_FLAGS.get(os.path.basename(src), []), *inc, "-c", src, "-o", obj]
+        obj = os.path.join(objdir, os.path.basename(src) + tag + ".o")
+        cmd = [hipcc(), *compile_flags, *PER_FILE_FLAGS.get(os.path.basename(src), []), *defines, *inc, "-c", src,
+               "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Build libvc.so; returns its path."""
+    return _build_lib(LIB, [], "", verbose)
+
+
+def build_ablation_exp(verbose: bool = False) -> str:
+    """Build libvc_ablation_exp.so (FP32 exp + E4M3 cast instead of ExpCast)."""
+    return _build_lib(ABLATION_EXP_LIB, ["-DVC_ABLATION_EXP_CAST"], ".ablation_exp", verbose)
 
 
 def _run(cmd, verbose):
@@ -74,3 +90,4 @@ def _run(cmd, verbose):
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_ablation_exp(verbose=True))

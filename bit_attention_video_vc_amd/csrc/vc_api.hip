@@ -207,7 +207,12 @@ bool same_shape(const vc_desc* a, const vc_desc* b) { return a->B == b->B && a->
 
 extern "C" {
 
+#ifndef VC_ABLATION_EXP_CAST
 const char* vc_version(void) { return "0.1.0"; }
+#else
+// the measurement build (FP32 exponential + E4M3 cast instead of ExpCast)
+const char* vc_version(void) { return "0.1.0+ablation-exp-cast"; }
+#endif
 
 const char* vc_status_string(vc_status s) {
   switch (s) {

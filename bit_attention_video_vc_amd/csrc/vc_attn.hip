@@ -137,14 +137,47 @@ __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// ExpCast of one 16x16 accumulator (4 keys per lane) into one packed dword.
-__device__ __forceinline__ uint32_t expcast4(const v4f& s, float s8, float c) {
-  uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[0], s8, c), 0, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[1], s8, c), 1, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[2], s8, c), 2, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[3], s8, c), 3, w);
-  return w;
+// The probability cast of two scores into bytes 2h, 2h+1 of a packed code
+// dword, with the per-tile scale a and the per-row constant b:
+//   ExpCast:  code = sat_u8(rne(fma(acc, a, b))), a = 8*sigma, b = 120 - 8*M
+// (one FMA and one byte conversion per score).  A build with
+// VC_ABLATION_EXP_CAST instead takes the FP32 exponential that ExpCast
+// replaces ("VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+// Attention", Abstract): p = 2^fma(acc, a, b) with a = sigma, b = 8 - M (so
+// p = 256 * 2^(acc*sigma - M)) on the transcendental unit, then an E4M3
+// cast (round to nearest even) -- for measuring what the cast saves; it is
+// not the method.
+#ifndef VC_ABLATION_EXP_CAST
+__device__ __forceinline__ float cast_scale(float sigma) { return 8.0f * sigma; }
+__device__ __forceinline__ float cast_const(float m) { return 120.0f - 8.0f * m; }
+__device__ __forceinline__ uint32_t pcast2(float x0, float x1, float a, float b, int h, uint32_t w) {
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x0, a, b), 2 * h, w);
+  return __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x1, a, b), 2 * h + 1, w);
+}
+#else
+__device__ __forceinline__ float cast_scale(float sigma) { return sigma; }
+__device__ __forceinline__ float cast_const(float m) { return 8.0f - m; }
+__device__ __forceinline__ uint32_t pcast2(float x0, float x1, float a, float b, int h, uint32_t w) {
+  const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, a, b));
+  const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, a, b));
+  // the word select of the conversion is an immediate
+  return static_cast<uint32_t>(h ? __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, static_cast<int>(w), true)
+                                 : __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, static_cast<int>(w), false));
+}
+// one score into byte i of w (keys with their own scale: the repair tiles)
+__device__ __forceinline__ uint32_t pcast1(float x, float a, float b, int i, uint32_t w) {
+  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(x, a, b)), 0.0f,
+                                                                          0, false)) & 0xFFu;
+  return (w & ~(0xFFu << (8 * i))) | (c << (8 * i));
+}
+// cast constant that sends a score to code 0 (masked repair slots)
+constexpr float kCastOff = -200.0f;
+#endif
+
+// Cast of one 16x16 accumulator (4 keys per lane) into one packed dword.
+__device__ __forceinline__ uint32_t expcast4(const v4f& s, float a, float b) {
+  uint32_t w = pcast2(s[0], s[1], a, b, 0, 0u);
+  return pcast2(s[2], s[3], a, b, 1, w);
 }
 
 __device__ __forceinline__ float max4(const v4f& s) { return fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])); }
@@ -159,15 +192,14 @@ constexpr float kNegBig = -3.0e38f;
 struct SoftState {
   float M[2];      // integer log2 running maximum (kNegBig before the first tile)
   float l[2];      // running row sum
-  float cq[2];     // 120 - 8*M: the ExpCast constant for the current maximum
+  float cq[2];     // cast_const(M) (120 - 8*M): the cast constant for the current maximum
 };
 
 // ExpCast and running max of half an accumulator (keys i0, i0+1 of one
 // 16-key sub-tile): two FMAs, two conversions into the packed code dword and
 // one 3-input max.
 __device__ __forceinline__ void expcast_half(const v4f& s, int i0, float s8, float c, uint32_t& w, float& mx) {
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[i0], s8, c), i0, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[i0 + 1], s8, c), i0 + 1, w);
+  w = pcast2(s[i0], s[i0 + 1], s8, c, i0 >> 1, w);
   mx = fmaxf(fmaxf(mx, s[i0]), s[i0 + 1]);
 }
 
@@ -277,7 +309,7 @@ __device__ __forceinline__ void mask_tile(v4f (&sc)[8][2], int g, int kval) {
 // Integer running max, rescale factor and ExpCast codes for one tile.
 __device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma, SoftState& st, float (&alpha)[2],
                                              v8i (&P)[2]) {
-  const float s8 = 8.0f * sigma;
+  const float s8 = cast_scale(sigma);
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
     float mx = max4(sc[0][qi]);
@@ -287,8 +319,8 @@ __device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma,
     const float mn = fmaxf(st.M[qi], ceilf(mx * sigma));
     alpha[qi] = st.M[qi] == kNegBig ? 0.0f : ldexpf(1.0f, static_cast<int>(fmaxf(st.M[qi] - mn, -160.0f)));
     st.M[qi] = mn;
-    st.cq[qi] = 120.0f - 8.0f * mn;
-    const float c = 120.0f - 8.0f * mn;
+    st.cq[qi] = cast_const(mn);
+    const float c = st.cq[qi];
 #pragma unroll
     for (int t = 0; t < 8; ++t) P[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, c));
   }
@@ -454,7 +486,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
                       kb + kStages - 1, kfree, vfree);
   static_assert(2 * kDmaPerTile + 2 == 6, "six copy parts, one per sub-tile");
   const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
-  const float s8 = 8.0f * sigma;
+  const float s8 = cast_scale(sigma);
   v8i Pn[2];
   float alpha[2], r[2];
   bool changed;
@@ -485,7 +517,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
       for (int qi = 0; qi < 2; ++qi) {
         alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn[qi], -160.0f)));
         acc.st.M[qi] = mn[qi];
-        acc.st.cq[qi] = 120.0f - 8.0f * mn[qi];
+        acc.st.cq[qi] = cast_const(mn[qi]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) Pn[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, acc.st.cq[qi]));
       }
@@ -686,11 +718,22 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int j = rt * kBlock + 16 * t + 4 * g + i;
           const float sig = ((sqs * rks[j]) * a.sm_scale) * kLog2e;
+          // slots past the repair set cast to code 0
+#ifndef VC_ABLATION_EXP_CAST
+          // (the ExpCast constants written out: as calls of cast_scale and
+          // cast_const the register allocation of the whole kernel spills)
           const float s8j = j < nrep ? 8.0f * sig : 0.0f;
           const float c0 = j < nrep ? 120.0f - 8.0f * st.M[0] : -1.0f;
           const float c1 = j < nrep ? 120.0f - 8.0f * st.M[1] : -1.0f;
           w0 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[i], s8j, c0), i, w0);
           w1 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[i], s8j, c1), i, w1);
+#else
+          const float s8j = j < nrep ? cast_scale(sig) : 0.0f;
+          const float c0 = j < nrep ? cast_const(st.M[0]) : kCastOff;
+          const float c1 = j < nrep ? cast_const(st.M[1]) : kCastOff;
+          w0 = pcast1(s0[i], s8j, c0, i, w0);
+          w1 = pcast1(s1[i], s8j, c1, i, w1);
+#endif
         }
         Pr[0][t] = static_cast<int>(w0);
         Pr[1][t] = static_cast<int>(w1);

@@ -115,6 +115,49 @@ def test_expcast_accuracy_envelope_unquantised():
     assert O.rel_l2(b, ex) < 0.04
 
 
+def _integer_log_head(qmax, seed=11, S=300, D=128):
+    """Integer q, one-hot integer k: every score is an integer in [-2*qmax, 2*qmax]."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-qmax, qmax + 1, size=(S, D)).astype(np.float64)
+    k = np.zeros((S, D))
+    k[np.arange(S), rng.integers(0, D, size=S)] = rng.integers(0, 3, size=S)   # one non-zero per key
+    v = rng.standard_normal((S, D))
+    return q, k, v
+
+
+def _casts(q, k, v, sm, pcasts):
+    hv = O.prepare_v_head(v, smooth=False, k=1, iters=0, quant=False)
+    hq = O.HeadQK(None, None, None, None)
+    return {pc: O.attend_head(hq, hv, None, sm_scale=sm, pcast=pc, quant=False, q_raw=q, k_raw=k[hv.perm],
+                              int_max=True) for pc in pcasts}
+
+
+def test_casts_exact_on_integer_log_scores():
+    # Special case with a closed form: when every score times sigma is an
+    # integer t and d = t - M is within reach of E4M3, 256 * 2^d is a power of
+    # two that E4M3 holds exactly, so the "exp then E4M3 cast" path that
+    # ExpCast replaces ("VC-Attention: Value Smoothing and Softmax Casting for
+    # Low-bit Attention", Abstract) gives the exact probabilities for d down
+    # to -17 (its smallest subnormal 2^-9; without the factor 256 everything
+    # below d = -9 would underflow), and ExpCast's byte 120 + 8d -- an E4M3
+    # normal number 2^(8+d) -- is exact for d >= -14 and 0 below.
+    sm = 1.0 / math.log2(math.e)                     # sigma = sm * log2(e) = 1 exactly in fp64
+    assert float(np.float64(sm)) * math.log2(math.e) == 1.0
+    q, k, v = _integer_log_head(4)                   # scores in [-8, 8]: d reaches -16
+    x = q @ k.T
+    assert (x - x.max(axis=1, keepdims=True)).min() == -16.0
+    out = _casts(q, k, v, sm, ("exact", "exp_e4m3", "expcast"))
+    assert np.array_equal(out["exp_e4m3"], out["exact"])
+    assert not np.array_equal(out["expcast"], out["exact"])       # d = -15, -16 cast to 0
+    q, k, v = _integer_log_head(3, seed=12)          # scores in [-6, 6]: d >= -12
+    out = _casts(q, k, v, sm, ("exact", "exp_e4m3", "expcast"))
+    assert np.array_equal(out["expcast"], out["exact"])
+    assert np.array_equal(out["exp_e4m3"], out["exact"])
+    # off-integer scores: the E4M3 path rounds, so it is not trivially exact
+    out = _casts(q, k, v, sm * 1.1, ("exact", "exp_e4m3"))
+    assert not np.array_equal(out["exp_e4m3"], out["exact"])
+
+
 # --------------------------------------------------------- whole pipeline pins
 def _cfg(cid, **kw):
     w = synth.workload(cid, **kw)
