@@ -46,6 +46,12 @@ Where the pages leave a step open, the reading taken is stated at the step
      error with its own per-(b,h) scale; their probabilities are not added to
      the row sum a second time.
  R11 Softmax scale defaults to fp32(1/sqrt(128)); output is bf16 (RNE).
+ R12 4-bit residual ([NUN] paragraph 2 names NVFP4 beside E4M3), taken as
+     OCP MXFP4: E2M1 codes, one power-of-two (E8M0) scale per group of 32
+     keys of one channel within a 128-key tile -- the 32 keys that one
+     matrix-core lane holds (see mx_group_of_key) -- the scale being the
+     smallest power of two X with max|R|/X <= 6, so nothing is clipped;
+     values round half to even; no per-head scale (s_v = 1, mu' = mu).
 
 Parity pins: every function here is pinned by tests under ``tests/`` that use
 closed forms, brute force, library routines or invariants -- none is "parity
@@ -107,6 +113,87 @@ def e4m3_encode(x) -> np.ndarray:
     code = np.where(sub, val * 2.0 ** 9, (ev + 6) * 8 + mant)
     code = code.astype(np.int64) | np.where(neg, 0x80, 0)
     return code.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# OCP E2M1 (FP4) codec and MX groups (R12)
+# --------------------------------------------------------------------------
+E2M1_MAX = 6.0
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 code (bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa) -> value."""
+    c = np.asarray(codes, dtype=np.int64)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int64)))
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Nearest E2M1 code, ties to the even mantissa, saturating at +-6; the sign
+    bit follows the input's sign (also when the magnitude rounds to 0)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E2M1_MAX)
+    grid = e2m1_decode(np.arange(8))                    # 0, 0.5, 1, 1.5, 2, 3, 4, 6 (ascending)
+    i = np.searchsorted(grid, a, side="left")           # first grid value >= a
+    lo = np.clip(i - 1, 0, 7)
+    hi = np.clip(i, 0, 7)
+    dlo, dhi = a - grid[lo], grid[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((hi & 1) == 0))
+    code = np.where(pick_hi, hi, lo)
+    return (code | np.where(np.signbit(x), 8, 0)).astype(np.int64)
+
+
+def mx_group_of_key(j) -> np.ndarray:
+    """Group (0..3) of key j (0..127) of a tile: the matrix-core lane group g
+    that holds it as an FP4 operand.  The product O^T += V^T . P^T pairs
+    key 16t + 4u + i with the P operand's K index 32u + 4t + i; with FP4
+    operands lane group g holds the K indices 64*(g&1) + 16*(g>>1) + [0,16)
+    and the same + 32 (measured on the device)."""
+    j = np.asarray(j, dtype=np.int64)
+    t, u, i = j // 16, (j % 16) // 4, j % 4
+    kb = 32 * u + 4 * t + i
+    return kb // 64 + 2 * (((kb % 64) // 16) % 2)
+
+
+def mx_scale_exponent(amax) -> np.ndarray:
+    """Smallest e with amax / 2^e <= 6 (exact), clamped to [-127, 127]; 0 if amax == 0."""
+    a = np.asarray(amax, dtype=np.float64)
+    e = np.zeros(a.shape, dtype=np.int64)
+    nz = a > 0
+    m, ex = np.frexp(a[nz] / E2M1_MAX)                  # a/6 = m * 2^ex, m in [0.5, 1)
+    e[nz] = np.where(m == 0.5, ex - 1, ex)              # exact powers of two need no rounding up
+    return np.clip(e, -127, 127)
+
+
+def quantize_mxfp4(resid: np.ndarray):
+    """R12: resid [S, D] fp32 (permuted order) -> codes [S, D] (E2M1) and
+    exponents [nblk, D, 4] (scale of (tile, channel, group) = 2^e)."""
+    S, D = resid.shape
+    nblk = (S + BLOCK - 1) // BLOCK
+    codes = np.zeros((S, D), dtype=np.int64)
+    expo = np.zeros((nblk, D, 4), dtype=np.int64)
+    grp = mx_group_of_key(np.arange(BLOCK))
+    for b in range(nblk):
+        rows = resid[b * BLOCK: min(S, (b + 1) * BLOCK)].astype(np.float64)
+        gk = grp[:rows.shape[0]]
+        for g in range(4):
+            sel = gk == g
+            if not np.any(sel):
+                continue
+            e = mx_scale_exponent(np.max(np.abs(rows[sel]), axis=0))          # [D]
+            expo[b, :, g] = e
+            codes[b * BLOCK + np.nonzero(sel)[0]] = e2m1_encode(rows[sel] / np.ldexp(1.0, e)[None, :])
+    return codes, expo
+
+
+def mxfp4_dequant(codes: np.ndarray, expo: np.ndarray) -> np.ndarray:
+    """Values of quantize_mxfp4's output, [S, D] float64."""
+    S, D = codes.shape
+    grp = mx_group_of_key(np.arange(S) % BLOCK)
+    e = expo[np.arange(S) // BLOCK][np.arange(S), :, grp]                     # [S, D]
+    return e2m1_decode(codes) * np.ldexp(1.0, e)
 
 
 def bf16_round(x) -> np.ndarray:
@@ -258,6 +345,15 @@ class HeadV:
     rep_scale: np.float32 = F32(1.0)
     rep_norm2: np.ndarray | None = None     # [S] squared error norm (fp64)
     centroids: np.ndarray | None = None
+    v_format: str = "e4m3"                  # "e4m3" (per-head scale) or "mxfp4" (R12)
+    v4: np.ndarray | None = None            # [S, D] E2M1 codes (mxfp4)
+    v4_exp: np.ndarray | None = None        # [nblk, D, 4] scale exponents (mxfp4)
+
+    def v_values(self) -> np.ndarray:
+        """Dequantised residual the P.V product consumes, [S, D] float64."""
+        if self.v_format == "mxfp4":
+            return mxfp4_dequant(self.v4, self.v4_exp)
+        return float(self.v_scale) * e4m3_decode(self.v8)
 
 
 def block_means(vp: np.ndarray, block: int = BLOCK) -> np.ndarray:
@@ -280,12 +376,13 @@ def repair_count(beta: float, S: int) -> int:
 
 def prepare_v_head(v: np.ndarray, *, smooth: bool = True, k: int = 32, iters: int = 5,
                    seed: int = 0, bh: int = 0, repair_budget: float = 0.0,
-                   quant: bool = True) -> HeadV:
+                   quant: bool = True, v_format: str = "e4m3") -> HeadV:
     """V-Smooth for one head, V given as [S, D] float64 (exact bf16/fp16 values).
 
     1. cluster (integer k-means on the sketch) and order tokens by cluster;
     2. subtract each 128-position block's mean: R = fp32(v - mu);
-    3. quantise R with one per-head amax scale to E4M3;
+    3. quantise R with one per-head amax scale to E4M3 (v_format="e4m3"), or
+       to MXFP4 with one power-of-two scale per 32-key group (R12; no repair);
     4. optional repair set (R10).
     quant=False keeps R unquantised (v8 then holds no codes; used by the
     identity tests through attend_head's quant switch).
@@ -313,6 +410,12 @@ def prepare_v_head(v: np.ndarray, *, smooth: bool = True, k: int = 32, iters: in
     resid = (vp - mu_rows).astype(F32)               # single rounding of the exact difference
     if not quant:
         return HeadV(assign, perm, mu, resid, np.zeros((S, D), np.uint8), F32(1.0), centroids=cent)
+    if v_format == "mxfp4":
+        if repair_count(repair_budget, S) > 0:
+            raise ValueError("the MXFP4 residual has no repair")
+        v4, v4e = quantize_mxfp4(resid)
+        return HeadV(assign, perm, mu, resid, np.zeros((S, D), np.uint8), F32(1.0), centroids=cent,
+                     v_format="mxfp4", v4=v4, v4_exp=v4e)
     v8, s_v = quantize_amax(resid)
     hv = HeadV(assign, perm, mu, resid, v8, s_v, centroids=cent)
     n_rep = repair_count(repair_budget, S)
@@ -405,7 +508,7 @@ def attend_head(hq: HeadQK, hv: HeadV, rows=None, *, sm_scale=DEFAULT_SM_SCALE,
     if quant:
         Qd = e4m3_decode(hq.q8[rows])
         Kd = e4m3_decode(hq.k8)
-        Vd = F32(hv.v_scale) * e4m3_decode(hv.v8)
+        Vd = hv.v_values()
         s_q = hq.q_scale[rows // BLOCK][:, None]
         s_k = hq.k_scale
     else:
