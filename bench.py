@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
                     help="after the timed steps, keep launching the attention kernel for SECONDS "
                          "(a steady load for sampling power and clocks with amd-smi)")
+    ap.add_argument("--v-format", choices=["e4m3", "mxfp4"], default="e4m3",
+                    help="residual format of V-Smooth: E4M3 with a per-head scale (the default), or the 4-bit "
+                         "MXFP4 variant (E2M1 with a power-of-two scale per 32-key group; no repair)")
     ap.add_argument("--ablation-exp", action="store_true",
                     help="also time the attention kernel of libvc_ablation_exp.so (FP32 exponential + E4M3 cast "
                          "instead of ExpCast) on the same prepared workspace")
@@ -145,7 +148,11 @@ def main() -> int:
     qd, kd, vd = (t.to("cuda") for t in (q, k, v))
     torch.cuda.synchronize()
 
-    opts = vc.v_opts(True, w.k, w.iters, 0, w.repair_budget)
+    v_fmt = vc.VC_V_MXFP4 if args.v_format == "mxfp4" else vc.VC_V_E4M3
+    if v_fmt == vc.VC_V_MXFP4 and w.repair_budget > 0:
+        print("bench.py: the MXFP4 residual has no repair; pick a workload without it", file=sys.stderr)
+        return 2
+    opts = vc.v_opts(True, w.k, w.iters, 0, w.repair_budget, v_fmt)
     ws = vc.alloc_workspace(vd, opts)
     out = torch.empty(qd.shape, dtype=torch.bfloat16, device="cuda")
     lay = vc.vc_workspace_layout(vd, opts)
@@ -199,7 +206,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D} {str(w.dtype).replace('torch.', '')} in, bf16 out, "
-                        f"non-causal, V-Smooth k={w.k} T={w.iters}, repair={w.repair_budget}",
+                        f"non-causal, V-Smooth k={w.k} T={w.iters}, repair={w.repair_budget}"
+                        + (", 4-bit MXFP4 residual" if v_fmt == vc.VC_V_MXFP4 else ""),
             "step": "full call: vc_prepare_v + vc_prepare_qk + vc_attention_fwd",
             "flop_per_step": flops,
             "parallelism": "single GPU",

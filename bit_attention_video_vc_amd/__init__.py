@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "VcDesc", "VcVOpts", "VcAttnOpts", "VcWsLayout", "VcHeadHdr", "VCError", "lib", "lib_path",
     "ablation_exp_lib_path", "use_library",
-    "v_opts", "desc_of", "vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd",
+    "v_opts", "VC_V_E4M3", "VC_V_MXFP4", "desc_of", "vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd",
     "alloc_workspace", "attention", "EXPORTS",
 ]
 
@@ -48,7 +48,7 @@ class VcDesc(ctypes.Structure):
 
 class VcVOpts(ctypes.Structure):
     _fields_ = [("smooth", ctypes.c_int32), ("k", ctypes.c_int32), ("iters", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64), ("repair_budget", ctypes.c_float),
+                ("v_format", ctypes.c_int32), ("seed", ctypes.c_uint64), ("repair_budget", ctypes.c_float),
                 ("reserved2", ctypes.c_float)]
 
 
@@ -117,8 +117,12 @@ def _check(status: int) -> None:
         raise VCError(status, f"{L.vc_status_string(status).decode()}: {L.vc_last_error().decode()}")
 
 
-def v_opts(smooth: bool = True, k: int = 32, iters: int = 5, seed: int = 0, repair_budget: float = 0.0) -> VcVOpts:
-    return VcVOpts(int(bool(smooth)), int(k), int(iters), 0, int(seed), float(repair_budget), 0.0)
+VC_V_E4M3, VC_V_MXFP4 = 0, 1
+
+
+def v_opts(smooth: bool = True, k: int = 32, iters: int = 5, seed: int = 0, repair_budget: float = 0.0,
+           v_format: int = VC_V_E4M3) -> VcVOpts:
+    return VcVOpts(int(bool(smooth)), int(k), int(iters), int(v_format), int(seed), float(repair_budget), 0.0)
 
 
 def desc_of(t: torch.Tensor) -> VcDesc:
@@ -176,9 +180,10 @@ def vc_attention_fwd(out: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, sm_scal
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, smooth: bool = True, clusters: int = 32,
               iters: int = 5, seed: int = 0, repair_budget: float = 0.0, sm_scale: float = 0.0,
-              ws: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+              v_format: int = VC_V_E4M3, ws: torch.Tensor | None = None, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
     """Full call: prepare_v, prepare_qk and the fused forward; returns bf16 [B,S,H,128] (or [S,H,128])."""
-    o = v_opts(smooth, clusters, iters, seed, repair_budget)
+    o = v_opts(smooth, clusters, iters, seed, repair_budget, v_format)
     if ws is None:
         ws = alloc_workspace(v, o)
     if out is None:

@@ -60,6 +60,9 @@ vc_status check_opts(const vc_v_opts* o, int S) {
     if (o->iters < 0 || o->iters > 64) return fail(VC_ERR_ARG, "iters must be in [0, 64]");
   }
   if (!(o->repair_budget >= 0.0f && o->repair_budget < 1.0f)) return fail(VC_ERR_ARG, "repair_budget must be in [0, 1)");
+  if (o->v_format != VC_V_E4M3 && o->v_format != VC_V_MXFP4) return fail(VC_ERR_ARG, "v_format must be 0 or 1");
+  if (o->v_format == VC_V_MXFP4 && o->repair_budget > 0.0f)
+    return fail(VC_ERR_UNSUPPORTED, "the MXFP4 residual has no repair");
   return VC_OK;
 }
 
@@ -305,6 +308,7 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   a.nrep_pad = p.nrep_pad;
   a.total_wg = static_cast<int>(total);
   a.sm_scale = sm;
+  a.v_format = opts->v_format;
   const hipError_t e = vc::launch_attention(a, p.B * p.H, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(VC_ERR_DEVICE, "attention launch: %s", hipGetErrorString(e));
   return ok();

@@ -106,10 +106,17 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 constexpr int kDmaPerTile = kTileBytes / (16 * kAttnThreads);   // copy instructions per 16 KB tile
 // LDS ring depth for K and for V tiles; copies run kStages-1 tiles ahead.
 constexpr int kStages = 4;
+// V tile formats (VF = vc_v_format): E4M3, 16 KB; MXFP4, 8 KB of E2M1 codes
+// then 512 B of scale exponents (8 per lane), copied with a 1 KB landing zone.
+constexpr int kFp4CodeBytes = 8192;
+template <int VF> struct VTile {
+  static constexpr int kBytes = VF ? kFp4CodeBytes + 1024 : kTileBytes;       // LDS buffer
+  static constexpr int kDma = VF ? kFp4CodeBytes / (16 * kAttnThreads) : kDmaPerTile;   // code copies per wave
+};
 // Copy instructions per step: every wave copies its share of one K and one
-// V tile; wave 0 also copies the K tile's scale and one restore-operand row.
-constexpr int kDmaPerStep = 2 * kDmaPerTile;
-constexpr int kDmaPerStep0 = kDmaPerStep + 2;
+// V tile; wave 0 also copies the K tile's scale and one restore-operand row
+// (and, for MXFP4, wave 1 the V tile's scales).
+template <int VF> constexpr int kDmaPerStep = kDmaPerTile + VTile<VF>::kDma;
 // A K buffer: the K tile, then its scale, written by every lane of a 4-byte
 // copy (256 bytes).
 constexpr int kKBufBytes = kTileBytes + 256;
@@ -120,19 +127,18 @@ constexpr int kGrpBytes = kMuOpGroup * kMuOpRowBytes + kMuOpRowBytes;
 // End of a tile step: every wave waits until at most the (kStages-2) *
 // kDmaPerStep newest of its copies may still be in flight, and until its LDS
 // reads have returned; then the workgroup barrier.  The copies of a step are
-// always its last vector-memory instructions, so for waves 1..7 (kDmaPerStep
-// copies per step) this means every copy issued kStages-2 or more steps
-// earlier has landed.  Wave 0 issues kDmaPerStep0 per step, so the same count
-// also completes all but the last two copies of the step before; its two
-// extra copies (a K scale and a restore-operand row) are read kStages-1
-// steps after issue at the earliest, and so have landed too.  One count for
-// all waves keeps the compiler's own wait analysis exact.
+// always its last vector-memory instructions and every wave issues at least
+// kDmaPerStep of them per step, so the count means that every copy issued
+// kStages-2 or more steps earlier has landed (waves with extra copies -- a K
+// scale, a restore-operand row, MXFP4 scales -- only finish earlier).  One
+// count for all waves keeps the compiler's own wait analysis exact.
+template <int VF>
 __device__ __forceinline__ void step_barrier() {
   // s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14.
   // Written as a builtin so the compiler's own wait insertion knows that
   // every older copy has landed after this point.
-  constexpr int kVm = (kStages - 2) * kDmaPerStep;
-  static_assert(kVm < 64 && kDmaPerStep0 - kDmaPerStep <= kDmaPerStep, "vmcnt field; wave 0 bound");
+  constexpr int kVm = (kStages - 2) * kDmaPerStep<VF>;
+  static_assert(kVm < 64, "vmcnt field");
   __builtin_amdgcn_s_waitcnt((kVm & 15) | (7 << 4) | (0 << 8) | ((kVm >> 4) << 14));
   __builtin_amdgcn_s_barrier();
 }
@@ -213,7 +219,32 @@ __device__ __forceinline__ void expcast_half(const v4f& s, int i0, float s8, flo
 // ALU work runs under the matrix core instead of after it.  Order and
 // placement are fixed with scheduling barriers.  K and V operands are read
 // from LDS two sub-tiles ahead; copy parts 0..5 go out one per sub-tile.
-template <typename Copies>
+// The V operand of channel sub-tile dt: E4M3, 32 bytes per lane; MXFP4, 16
+// bytes of E2M1 codes per lane (the matrix core reads four registers).
+template <int VF>
+__device__ __forceinline__ v8i ld_vop(const uint8_t* vl, int dt) {
+  if (VF == 0) return ld_op_lds_at(vl, dt);
+  const uint4 c = *reinterpret_cast<const uint4*>(vl + dt * 1024);
+  v8i r = {static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z), static_cast<int>(c.w), 0, 0, 0, 0};
+  return r;
+}
+// O^T[dt] += V^T[dt] . P^T; for MXFP4 with the lane's E8M0 scale of this dt
+// (byte dt%4 of vsc[dt/4]) on V and scale 1 (127) on P.
+// (dt is a constant once the caller's loop is unrolled; the byte select is
+// an immediate of the instruction, hence the switch)
+template <int VF>
+__device__ __forceinline__ v4f pv_mfma(const v8i& vop, const v8i& p, const v4f& o, const uint32_t (&vsc)[2], int dt) {
+  if (VF == 0) return mfma_fp8(vop, p, o);
+  const int sc = static_cast<int>(vsc[dt >> 2]);
+  switch (dt & 3) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 0, sc, 0, 127);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 1, sc, 0, 127);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 2, sc, 0, 127);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 3, sc, 0, 127);
+  }
+}
+
+template <int VF, typename Copies>
 __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* vt, int lane, const v8i (&qop)[2],
                                            const v8i (&P)[2], float s8, const float (&cq)[2], v4f (&sc)[8][2],
                                            v8i (&Pn)[2], float (&mx)[2], v4f (&O)[8][2], float (&r)[2],
@@ -223,10 +254,17 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
   const uint8_t* kl = ktile + lane;   // lane = the lane's byte offset (16 * lane id)
   const uint8_t* vl = vt + lane;
   v8i kop[2], vop[2];
+  uint32_t vsc[2] = {0u, 0u};
+  if (VF) {
+    // the lane's 8 scale exponents (one per channel sub-tile), 8 bytes at 8*lane
+    const uint2 s2 = *reinterpret_cast<const uint2*>(vt + kFp4CodeBytes + (lane >> 1));
+    vsc[0] = s2.x;
+    vsc[1] = s2.y;
+  }
   kop[0] = ld_op_lds_at(kl, 0);
-  vop[0] = ld_op_lds_at(vl, 0);
+  vop[0] = ld_vop<VF>(vl, 0);
   kop[1] = ld_op_lds_at(kl, 1);
-  vop[1] = ld_op_lds_at(vl, 1);
+  vop[1] = ld_vop<VF>(vl, 1);
   uint32_t w[8][2];
   mx[0] = mx[1] = kNegBig;
   __builtin_amdgcn_sched_barrier(0);
@@ -252,19 +290,19 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
     if (t + 2 < 8) kop[t & 1] = ld_op_lds_at(kl, t + 2);
     __builtin_amdgcn_sched_barrier(0);
     // slot 4t+2: P.V channels t, query sub-tile 0; first half of (t, 0)
-    O[t][0] = mfma_fp8(vop[t & 1], P[0], O[t][0]);
+    O[t][0] = pv_mfma<VF>(vop[t & 1], P[0], O[t][0], vsc, t);
     __builtin_amdgcn_sched_barrier(0);
     w[t][0] = 0;
     expcast_half(sc[t][0], 0, s8, cq[0], w[t][0], mx[0]);
     asm volatile("" : "+v"(w[t][0]), "+v"(mx[0]));
     __builtin_amdgcn_sched_barrier(0);
     // slot 4t+3: P.V channels t, sub-tile 1; second half of (t, 0)
-    O[t][1] = mfma_fp8(vop[t & 1], P[1], O[t][1]);
+    O[t][1] = pv_mfma<VF>(vop[t & 1], P[1], O[t][1], vsc, t);
     __builtin_amdgcn_sched_barrier(0);
     expcast_half(sc[t][0], 2, s8, cq[0], w[t][0], mx[0]);
     Pn[0][t] = static_cast<int>(w[t][0]);
     asm volatile("" : "+v"(Pn[0][t]), "+v"(mx[0]));
-    if (t + 2 < 8) vop[t & 1] = ld_op_lds_at(vl, t + 2);
+    if (t + 2 < 8) vop[t & 1] = ld_vop<VF>(vl, t + 2);
     if (t < 6) cp.issue(t);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -352,6 +390,7 @@ struct TileAcc {
 // K, then V (every wave), part 0 the scale and part 2*kDmaPerTile+1 the row
 // (wave 0 only) -- issued one at a time at points spread over the step, so
 // that the workgroup's copies do not all queue at once.
+template <int VF>
 struct StepCopies {
   const TileCtx& c;
   uint32_t koff, voff, soff, roff;
@@ -381,7 +420,12 @@ struct StepCopies {
       copy16_to_lds(c.kr, koff + j * (16 * kAttnThreads), kdst + j * (16 * kAttnThreads) + w * 1024);
     } else if (part <= 2 * kDmaPerTile) {
       const int j = part - 1 - kDmaPerTile;
-      copy16_to_lds(c.vr, voff + j * (16 * kAttnThreads), vdst + j * (16 * kAttnThreads) + w * 1024);
+      if (j < VTile<VF>::kDma) {
+        copy16_to_lds(c.vr, voff + j * (16 * kAttnThreads), vdst + j * (16 * kAttnThreads) + w * 1024);
+      } else if (VF && w == 1) {
+        // MXFP4: the tile's 512 scale bytes (and 512 unused bytes of the slot)
+        copy16_to_lds(c.vr, voff - static_cast<uint32_t>(w) * 1024 + kFp4CodeBytes, vdst + kFp4CodeBytes);
+      }
     } else {
       if (w == 0) copy16_to_lds(c.mr, roff, rdst);
     }
@@ -477,12 +521,12 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane16, 
 // last tile are clamped to it and a score tile past the end is masked out
 // entirely, which leaves the state unchanged (alpha = 1, codes 0): every
 // step runs the same code.
-template <int J>
+template <int VF, int J>
 __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
                                           const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2], TileAcc& acc) {
   const int nblk = c.nblk, last = nblk - 1, lane = c.lane, g = c.g;
   const float ks_next = *reinterpret_cast<const float*>(kcur + kTileBytes);
-  const StepCopies cp(c, kb + kStages < last ? kb + kStages : last, kb + kStages - 1 < last ? kb + kStages - 1 : last,
+  const StepCopies<VF> cp(c, kb + kStages < last ? kb + kStages : last, kb + kStages - 1 < last ? kb + kStages - 1 : last,
                       kb + kStages - 1, kfree, vfree);
   static_assert(2 * kDmaPerTile + 2 == 6, "six copy parts, one per sub-tile");
   const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
@@ -493,7 +537,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
   {
     v4f sc[8][2];
     float mx[2];
-    mfma_phase(kcur, vcur, c.lane16, qop, acc.P, s8, acc.st.cq, sc, Pn, mx, acc.O, r, cp);
+    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, s8, acc.st.cq, sc, Pn, mx, acc.O, r, cp);
     const bool ragged = kb + 2 >= nblk;
     // Did any row's maximum rise?  ceil(fl(m*sigma)) > M for an integer M
     // exactly when fl(m*sigma) > M, and fl(m*sigma) is monotone in m, so
@@ -556,9 +600,10 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
       restore_mfma<4>(A, 4 * half, bh, bl, acc.O);
     }
   }
-  step_barrier();
+  step_barrier<VF>();
 }
 
+template <int VF>
 __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   // distinct arrays for the ring slots: a copy into one provably does not
   // alias reads of another
@@ -567,10 +612,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   __shared__ __align__(16) uint8_t kbuf1[kKBufBytes];
   __shared__ __align__(16) uint8_t kbuf2[kKBufBytes];
   __shared__ __align__(16) uint8_t kbuf3[kKBufBytes];
-  __shared__ __align__(16) uint8_t vbuf0[kTileBytes];
-  __shared__ __align__(16) uint8_t vbuf1[kTileBytes];
-  __shared__ __align__(16) uint8_t vbuf2[kTileBytes];
-  __shared__ __align__(16) uint8_t vbuf3[kTileBytes];
+  __shared__ __align__(16) uint8_t vbuf0[VTile<VF>::kBytes];
+  __shared__ __align__(16) uint8_t vbuf1[VTile<VF>::kBytes];
+  __shared__ __align__(16) uint8_t vbuf2[VTile<VF>::kBytes];
+  __shared__ __align__(16) uint8_t vbuf3[VTile<VF>::kBytes];
   __shared__ __align__(16) uint8_t grp0[kGrpBytes];     // restore operands, even groups
   __shared__ __align__(16) uint8_t grp1[kGrpBytes];     // odd groups
   uint8_t* const kring[kStages] = {kbuf0, kbuf1, kbuf2, kbuf3};
@@ -645,9 +690,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   const int last = nblk - 1;
 #pragma unroll
   for (int j = 0; j + 1 < kStages; ++j)
-    StepCopies(c, j < last ? j : last, j < last ? j : last, j, kring[j], vring[j]).issue_all();
+    StepCopies<VF>(c, j < last ? j : last, j < last ? j : last, j, kring[j], vring[j]).issue_all();
   {
-    const StepCopies cp(c, kStages - 1 < last ? kStages - 1 : last, 0, 0, kring[kStages - 1], vring[0]);
+    const StepCopies<VF> cp(c, kStages - 1 < last ? kStages - 1 : last, 0, 0, kring[kStages - 1], vring[0]);
 #pragma unroll
     for (int p = 0; p <= kDmaPerTile; ++p) cp.issue(p);
   }
@@ -669,14 +714,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   static_assert(kStages == 4, "tile_step<J> takes J = kb mod 4");
   int kb = 0;
   for (; kb + kStages <= nblk; kb += kStages) {
-    tile_step<0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, acc);
-    tile_step<1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, acc);
-    tile_step<2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, acc);
-    tile_step<3>(c, kb + 3, kbuf0, kbuf3, vbuf3, vbuf2, qop, acc);
+    tile_step<VF, 0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, acc);
+    tile_step<VF, 1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, acc);
+    tile_step<VF, 2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, acc);
+    tile_step<VF, 3>(c, kb + 3, kbuf0, kbuf3, vbuf3, vbuf2, qop, acc);
   }
-  if (kb < nblk) tile_step<0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, acc);
-  if (kb + 1 < nblk) tile_step<1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, acc);
-  if (kb + 2 < nblk) tile_step<2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, acc);
+  if (kb < nblk) tile_step<VF, 0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, acc);
+  if (kb + 1 < nblk) tile_step<VF, 1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, acc);
+  if (kb + 2 < nblk) tile_step<VF, 2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, acc);
   // drain the copies still in flight before the workgroup retires
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -771,7 +816,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
 
 hipError_t launch_attention(const AttnArgs& a, int BH, hipStream_t st) {
   (void)BH;
-  hipLaunchKernelGGL(k_vc_attn_fwd, dim3(a.total_wg), dim3(kAttnThreads), 0, st, a);
+  if (a.v_format == VC_V_MXFP4)
+    hipLaunchKernelGGL(k_vc_attn_fwd<VC_V_MXFP4>, dim3(a.total_wg), dim3(kAttnThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_vc_attn_fwd<VC_V_E4M3>, dim3(a.total_wg), dim3(kAttnThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -42,6 +42,7 @@ struct AttnArgs {
   int64_t osB, osS, osH;
   int S, H, nblk, nrep_pad, total_wg;
   float sm_scale;
+  int v_format;       // vc_v_format of the residual tiles in v8
 };
 
 hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_opts& o, const WsPtrs& ws,

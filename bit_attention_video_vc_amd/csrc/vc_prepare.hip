@@ -452,6 +452,94 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
   store_tr_tile(codes, v8 + (static_cast<int64_t>(bh) * nblk + blk) * kTileBytes);
 }
 
+// MXFP4 residual ("Nunchux AI lanza VC-Attention kernel ...", paragraph 2:
+// a 4-bit residual beside E4M3; taken as OCP MXFP4 for the gfx950 matrix
+// core): R = fp32(v - mu), one E8M0 scale per channel and group of 32 keys
+// -- the keys one matrix-core lane holds as an FP4 operand -- chosen as the
+// smallest power of two X with max|R|/X <= 6, and E2M1 codes of R/X (round
+// half to even, sign from R).  No per-head scale (s_v = 1, mu' = mu).
+// grid (nblk, H, B), 256 threads; thread = 2 (channel, group) pairs.
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+  const float a = fabsf(y);
+  // thresholds of round half to even on the grid 0, .5, 1, 1.5, 2, 3, 4, 6
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+                     (a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+// Smallest e with amax <= 6 * 2^e, for amax = m * 2^k (m in [0.5, 1)):
+// e = k - 3 when m <= 0.75, else k - 2; 0 for amax == 0; clamped to the
+// E8M0 range.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int k;
+  const float m = frexpf(amax, &k);
+  const int e = k - (m <= 0.75f ? 3 : 2);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+__global__ void __launch_bounds__(256) k_v_quant_pack_fp4(TensorArg v, int S, const int32_t* perm,
+                                                          const float* v_mean, vc_head_hdr* hdr, uint8_t* v8,
+                                                          uint8_t* v_muop) {
+  __shared__ float res[kBlock][kD + 1];   // residual of the tile (padded rows against bank conflicts)
+  __shared__ float mu[kD];
+  const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
+  if (threadIdx.x < kD) {
+    const int ch = threadIdx.x;
+    const float m = v_mean[(static_cast<int64_t>(bh) * nblk + blk) * kD + ch];
+    mu[ch] = m;
+    // restore operand: mu (s_v = 1) split into bf16 high and low parts
+    const uint16_t hi = static_cast<uint16_t>(f32_to_bf16_bits(m));
+    const uint16_t lo = static_cast<uint16_t>(f32_to_bf16_bits(m - __uint_as_float(static_cast<uint32_t>(hi) << 16)));
+    const int p = blk % kMuOpGroup, row = (blk - p) + 2 * (ch >> 4);
+    const int off = ((p >> 2) * 16 + (ch & 15)) * 8 + (p & 3) * 2;
+    uint8_t* base = v_muop + static_cast<int64_t>(bh) * muop_rows(nblk) * kMuOpRowBytes;
+    *reinterpret_cast<uint16_t*>(base + static_cast<int64_t>(row) * kMuOpRowBytes + off) = hi;
+    *reinterpret_cast<uint16_t*>(base + static_cast<int64_t>(row + 1) * kMuOpRowBytes + off) = lo;
+  }
+  if (blk == 0 && threadIdx.x == 0) {
+    hdr[bh].v_scale = 1.0f;
+    hdr[bh].v_inv = 1.0f;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < kBlock * 16; t += blockDim.x) {
+    const int j = t >> 4, c8 = (t & 15) * 8;
+    const int p = blk * kBlock + j;
+    float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (p < S) {
+      const int s = perm[static_cast<int64_t>(bh) * S + p];
+      float x[8];
+      load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = x[e] - mu[c8 + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) res[j][c8 + e] = r[e];
+  }
+  __syncthreads();
+  uint8_t* tile = v8 + (static_cast<int64_t>(bh) * nblk + blk) * kTileBytes;
+  for (int task = threadIdx.x; task < kD * 4; task += blockDim.x) {
+    const int d = task & (kD - 1), u = task >> 7;     // channel, lane group
+    // nibble n of lane group u holds P-operand K index kb, which is key
+    // 16*((kb%32)/4) + 4*(kb/32) + kb%4
+    float amax = 0.0f;
+#pragma unroll 8
+    for (int n = 0; n < 32; ++n) {
+      const int kb = 64 * (u & 1) + 16 * (u >> 1) + 32 * (n >> 4) + (n & 15);
+      amax = fmaxf(amax, fabsf(res[16 * ((kb & 31) >> 2) + 4 * (kb >> 5) + (kb & 3)][d]));
+    }
+    const int e = mx_exponent(amax);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 8
+    for (int n = 0; n < 32; ++n) {
+      const int kb = 64 * (u & 1) + 16 * (u >> 1) + 32 * (n >> 4) + (n & 15);
+      const float y = ldexpf(res[16 * ((kb & 31) >> 2) + 4 * (kb >> 5) + (kb & 3)][d], -e);
+      w[n >> 3] |= e2m1_encode(y) << (4 * (n & 7));
+    }
+    const int lane = u * 16 + (d & 15), dt = d >> 4;
+    *reinterpret_cast<uint4*>(tile + (dt * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    tile[8192 + lane * 8 + dt] = static_cast<uint8_t>(e + 127);
+  }
+}
+
 // Per-block amax E4M3 quantisation of 128 rows into a row tile.  GATHER: row
 // p is token perm[p] (K); otherwise row p is token p (Q).
 // grid (nblk, H, B), 256 threads; 4 (row, 16-channel) tasks per thread.
@@ -749,7 +837,11 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
   hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws.v_muop), 0u,
                      static_cast<int64_t>(BH) * muop_rows(nblk) * (kMuOpRowBytes / 4));
   VC_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_v_quant_pack, gblk, dim3(256), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.v8, ws.v_muop);
+  if (o.v_format == VC_V_MXFP4)
+    hipLaunchKernelGGL(k_v_quant_pack_fp4, gblk, dim3(256), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.v8,
+                       ws.v_muop);
+  else
+    hipLaunchKernelGGL(k_v_quant_pack, gblk, dim3(256), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.v8, ws.v_muop);
   VC_LAUNCH_CHECK();
   if (ws.nrep > 0) {
     const dim3 grep(ws.nrep_pad / kBlock, H, B);

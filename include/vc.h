@@ -73,13 +73,22 @@ typedef struct {
   int64_t sB, sS, sH;
 } vc_desc;
 
+/* Residual formats ("Nunchux AI lanza VC-Attention kernel ...", paragraph 2:
+ * the residual is kept in 8 bits (E4M3) or 4 bits (NVFP4)). */
+typedef enum {
+  VC_V_E4M3 = 0,           /* E4M3 codes with one scale per (b,h)                 */
+  VC_V_MXFP4 = 1           /* OCP MXFP4 on gfx950: E2M1 codes, one power-of-two
+                              (E8M0) scale per channel and group of 32 keys of a
+                              128-key tile; no repair                            */
+} vc_v_format;
+
 /* V-Smooth options. */
 typedef struct {
   int32_t smooth;          /* 1: k-means reorder + block-mean subtraction;
                               0: identity order, no mean (plain per-head FP8 V) */
   int32_t k;               /* clusters per (b,h): 1 <= k <= min(S, 64)         */
   int32_t iters;           /* Lloyd iterations after the seeded init: 0..64     */
-  int32_t reserved;
+  int32_t v_format;        /* vc_v_format of the residual (0 = E4M3)            */
   uint64_t seed;           /* init offset: splitmix64(seed ^ (b*H+h))           */
   float repair_budget;     /* beta in [0,1): ceil(beta*S) repaired tokens per
                               (b,h); 0 disables repair                          */
@@ -100,6 +109,8 @@ typedef struct {
  *   k8      u8  [BH][nblk] tiles: K codes, PERMUTED order (row p = token perm[p])
  *   k_scale f32 [BH][nblk]
  *   v8      u8  [BH][nblk] tiles: residual codes, permuted order, transposed
+ *               (VC_V_MXFP4: the tile slot holds the E2M1 tile and its scales,
+ *               see below)
  *   v_mean  f32 [BH][nblk][128] block means mu_b
  *   v_muop  u8  [BH][R][512] mu_b / s_v as bf16 high and low parts, laid
  *               out as matrix-core operands; R = 16*ceil((nblk+3)/16); row
@@ -120,6 +131,12 @@ typedef struct {
  *   transposed tile (v8, rep_e8): the byte for (key j, channel d) is at
  *     ((((d/16)*2 + i/16)*64 + (d%16) + 16*g) * 16) + i%16,
  *     with g = (j%16)/4 and i = 4*(j/16) + j%4.
+ *   MXFP4 tile (v8 with VC_V_MXFP4; 8704 of the slot's 16384 bytes): with
+ *     kb = 32*g + i (g, i as above), lane group u = kb/64 + 2*((kb%64)/16 % 2)
+ *     and nibble n = 16*((kb%64)/32) + kb%16, the E2M1 code of (key j,
+ *     channel d) is nibble n%2 (low first) of byte
+ *     ((d/16)*64 + u*16 + d%16) * 16 + n/2; the E8M0 exponent byte (scale
+ *     2^(byte-127)) of the group (tile, d, u) is at 8192 + (u*16 + d%16)*8 + d/16.
  */
 typedef struct {
   size_t total;

@@ -46,7 +46,7 @@ Where the pages leave a step open, the reading taken is stated at the step
      error with its own per-(b,h) scale; their probabilities are not added to
      the row sum a second time.
  R11 Softmax scale defaults to fp32(1/sqrt(128)); output is bf16 (RNE).
- R12 4-bit residual ([NUN] paragraph 2 names NVFP4 beside E4M3), taken as
+ R15 4-bit residual ([NUN] paragraph 2 names NVFP4 beside E4M3), taken as
      OCP MXFP4: E2M1 codes, one power-of-two (E8M0) scale per group of 32
      keys of one channel within a 128-key tile -- the 32 keys that one
      matrix-core lane holds (see mx_group_of_key) -- the scale being the
@@ -116,7 +116,7 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# OCP E2M1 (FP4) codec and MX groups (R12)
+# OCP E2M1 (FP4) codec and MX groups (R15)
 # --------------------------------------------------------------------------
 E2M1_MAX = 6.0
 
@@ -168,7 +168,7 @@ def mx_scale_exponent(amax) -> np.ndarray:
 
 
 def quantize_mxfp4(resid: np.ndarray):
-    """R12: resid [S, D] fp32 (permuted order) -> codes [S, D] (E2M1) and
+    """R15: resid [S, D] fp32 (permuted order) -> codes [S, D] (E2M1) and
     exponents [nblk, D, 4] (scale of (tile, channel, group) = 2^e)."""
     S, D = resid.shape
     nblk = (S + BLOCK - 1) // BLOCK
@@ -345,7 +345,7 @@ class HeadV:
     rep_scale: np.float32 = F32(1.0)
     rep_norm2: np.ndarray | None = None     # [S] squared error norm (fp64)
     centroids: np.ndarray | None = None
-    v_format: str = "e4m3"                  # "e4m3" (per-head scale) or "mxfp4" (R12)
+    v_format: str = "e4m3"                  # "e4m3" (per-head scale) or "mxfp4" (R15)
     v4: np.ndarray | None = None            # [S, D] E2M1 codes (mxfp4)
     v4_exp: np.ndarray | None = None        # [nblk, D, 4] scale exponents (mxfp4)
 
@@ -382,7 +382,7 @@ def prepare_v_head(v: np.ndarray, *, smooth: bool = True, k: int = 32, iters: in
     1. cluster (integer k-means on the sketch) and order tokens by cluster;
     2. subtract each 128-position block's mean: R = fp32(v - mu);
     3. quantise R with one per-head amax scale to E4M3 (v_format="e4m3"), or
-       to MXFP4 with one power-of-two scale per 32-key group (R12; no repair);
+       to MXFP4 with one power-of-two scale per 32-key group (R15; no repair);
     4. optional repair set (R10).
     quant=False keeps R unquantised (v8 then holds no codes; used by the
     identity tests through attend_head's quant switch).

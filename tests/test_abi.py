@@ -119,6 +119,8 @@ def test_layout_rejects_bad_descriptors(mut, code):
     (vc.v_opts(True, 4, 1, 0, 1.0), vc.VC_ERR_ARG),
     (vc.v_opts(True, 4, 1, 0, -0.1), vc.VC_ERR_ARG),
     (vc.v_opts(True, 4, 1, 0, float("nan")), vc.VC_ERR_ARG),
+    (vc.v_opts(True, 4, 1, 0, 0.0, 2), vc.VC_ERR_ARG),                    # unknown residual format
+    (vc.v_opts(True, 4, 1, 0, 0.01, vc.VC_V_MXFP4), vc.VC_ERR_UNSUPPORTED),   # MXFP4 has no repair
 ])
 def test_layout_rejects_bad_options(opts, code):
     st, _ = _layout(_desc(S=256), opts)

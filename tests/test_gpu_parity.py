@@ -50,6 +50,34 @@ ROW_IDX = _row_tile_index()
 TR_IDX = _tr_tile_index()
 
 
+def _mxfp4_tile_index():
+    """Byte, nibble shift and scale byte of (key j, channel d) in an MXFP4 tile
+    slot, from the layout documented with the C ABI."""
+    j = np.arange(128)[:, None]
+    d = np.arange(128)[None, :]
+    kb = 32 * ((j % 16) // 4) + 4 * (j // 16) + j % 4
+    u = kb // 64 + 2 * (((kb % 64) // 16) % 2)
+    n = 16 * ((kb % 64) // 32) + kb % 16
+    lane = u * 16 + d % 16
+    byte = ((d // 16) * 64 + lane) * 16 + n // 2
+    shift = 4 * (n % 2)
+    uu = np.arange(4)[None, :, None]
+    dd = np.arange(128)[:, None, None]
+    sbyte = (8192 + (uu * 16 + dd % 16) * 8 + dd // 16)[:, :, 0]        # [d, u]
+    return byte, shift, sbyte
+
+
+MX_BYTE, MX_SHIFT, MX_SBYTE = _mxfp4_tile_index()
+
+
+def unpack_mxfp4(raw: np.ndarray, nblk: int):
+    """nblk MXFP4 tile slots -> E2M1 codes [nblk*128, 128] and exponents [nblk, 128, 4]."""
+    t = raw.reshape(nblk, 16384)
+    codes = (t[:, MX_BYTE] >> MX_SHIFT) & 15                             # [nblk, 128, 128]
+    expo = t[:, MX_SBYTE].astype(np.int64) - 127                        # [nblk, d, u]
+    return codes.reshape(-1, 128).astype(np.int64), expo
+
+
 def muop_rows(nblk):
     return 16 * ((nblk + 3 + 15) // 16)
 
@@ -133,10 +161,12 @@ def _np(t):
 
 
 def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0.0, rows=None, heads=None,
-                         sm_scale=0.0, name="", exact_tol=TOL_EXACT):
+                         sm_scale=0.0, name="", exact_tol=TOL_EXACT, v_format="e4m3"):
     """Run the GPU path and compare every prepared product and the output with the oracle."""
-    say(f"{name}: shape={tuple(q.shape)} dtype={q.dtype} smooth={smooth} k={kc} T={iters} beta={beta}")
-    opts = vc.v_opts(smooth, kc, iters, seed, beta)
+    say(f"{name}: shape={tuple(q.shape)} dtype={q.dtype} smooth={smooth} k={kc} T={iters} beta={beta} "
+        f"v_format={v_format}")
+    fmt = vc.VC_V_MXFP4 if v_format == "mxfp4" else vc.VC_V_E4M3
+    opts = vc.v_opts(smooth, kc, iters, seed, beta, fmt)
     run = GpuRun(q, k, v, opts, sm_scale)
     B, S, H = run.B, run.S, run.H
     q4, k4, v4, o4 = (t if t.dim() == 4 else t[None] for t in (q, k, v, run.out))
@@ -146,7 +176,8 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
     for (b, h) in heads:
         bh = b * H + h
         qn, kn, vn = (_np(t[b, :, h]) for t in (q4, k4, v4))     # this head only, as float64
-        hv = O.prepare_v_head(vn, smooth=smooth, k=kc, iters=iters, seed=seed, bh=bh, repair_budget=beta)
+        hv = O.prepare_v_head(vn, smooth=smooth, k=kc, iters=iters, seed=seed, bh=bh, repair_budget=beta,
+                              v_format=v_format)
         hq = O.prepare_qk_head(qn, kn, hv.perm)
         tag = f"{name} (b={b},h={h})"
         gv = run.head_view(bh)
@@ -158,8 +189,20 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
         assert np.array_equal(gv["q_scale"], hq.q_scale), tag + " q_scale"
         assert np.array_equal(gv["k8"][:S], hq.k8), tag + " k8"
         assert np.array_equal(gv["k_scale"], hq.k_scale), tag + " k_scale"
-        assert np.array_equal(gv["v8"][:S], hv.v8), tag + " v8"
-        assert not gv["v8"][S:].any(), tag + " v8 padding"
+        if v_format == "mxfp4":
+            codes, expo = unpack_mxfp4(run.head_region("v8", torch.uint8, nb * 16384, bh), nb)
+            assert np.array_equal(codes[:S], hv.v4), tag + " E2M1 codes"
+            assert not codes[S:].any(), tag + " E2M1 padding"
+            # groups with no real key (past S in the last tile) carry no defined scale
+            grp = O.mx_group_of_key(np.arange(128))
+            last_real = S - 128 * (nb - 1)
+            live = np.ones((nb, 128, 4), bool)
+            for u in range(4):
+                live[nb - 1, :, u] = np.any(grp[:last_real] == u)
+            assert np.array_equal(expo[live], hv.v4_exp[live]), tag + " E8M0 scales"
+        else:
+            assert np.array_equal(gv["v8"][:S], hv.v8), tag + " v8"
+            assert not gv["v8"][S:].any(), tag + " v8 padding"
         assert np.array_equal(gv["v_mean"], hv.mean), tag + " block means"
         assert gv["hdr"][0] == hv.v_scale, tag + " v_scale"
         mhi, mlo = decode_muop(gv["v_muop"], nb)
@@ -281,3 +324,39 @@ def test_zero_value_head_and_zero_blocks():
     k[:, 0:128, 1] = 0                  # zero K rows (join whichever permuted block they land in)
     check_against_oracle(q.cuda(), k.cuda(), v.cuda(), kc=3, iters=2, name="zero head/blocks",
                          exact_tol=TOL_EXACT_ZERO_MEAN_V)
+
+
+# ---- 4-bit residual (MXFP4) ---------------------------------------------------
+# The 4-bit residual is coarser than E4M3 (the oracle itself sits up to ~4% from
+# exact attention on config 2), so its runs get the gross-error envelope.
+def test_mxfp4_config2():
+    w, q, k, v = _cfg(2)
+    check_against_oracle(q, k, v, kc=w.k, iters=w.iters, name="config2 mxfp4", v_format="mxfp4",
+                         exact_tol=TOL_EXACT_ZERO_MEAN_V)
+
+
+@pytest.mark.parametrize("S", [1, 129, 1000])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_mxfp4_ragged(S, dtype):
+    g = torch.Generator().manual_seed(200 + S)
+    B, H = 2, 3
+    q = torch.randn(B, S, H, 128, generator=g).to(dtype).cuda()
+    k = (1.5 * torch.randn(B, S, H, 128, generator=g)).to(dtype).cuda()
+    v = (torch.randn(B, S, H, 128, generator=g) + 3 * torch.randn(B, 1, H, 128, generator=g)).to(dtype).cuda()
+    check_against_oracle(q, k, v, kc=min(5, S), iters=3, name=f"mxfp4 ragged S={S} {dtype}",
+                         exact_tol=TOL_EXACT_ZERO_MEAN_V, v_format="mxfp4")
+
+
+def test_mxfp4_smooth_off_and_zero_head():
+    w, q, k, v = _cfg(2, H=2, S=700)
+    v[:, :, 1] = 0                      # an all-zero head: scales 2^0, codes 0
+    check_against_oracle(q, k, v, smooth=False, kc=4, iters=2, name="mxfp4 smooth=0", v_format="mxfp4",
+                         exact_tol=TOL_EXACT_ZERO_MEAN_V)
+
+
+def test_mxfp4_rejects_repair():
+    w, q, k, v = _cfg(1)
+    opts = vc.v_opts(True, 2, 1, 0, 0.01, vc.VC_V_MXFP4)
+    with pytest.raises(vc.VCError) as e:
+        vc.alloc_workspace(v, opts)
+    assert e.value.status == vc.VC_ERR_UNSUPPORTED

@@ -1,4 +1,4 @@
-"""Pins of the oracle's 4-bit residual path (reading R12: OCP MXFP4 -- E2M1
+"""Pins of the oracle's 4-bit residual path (reading R15: OCP MXFP4 -- E2M1
 codes with one power-of-two scale per group of 32 keys).
 
 The 4-bit option is named in "Nunchux AI lanza VC-Attention kernel ..."
