@@ -28,7 +28,16 @@ constexpr int kMaxK = 64;        // clusters per head
 constexpr int kMuOpRowBytes = 512;
 constexpr int kMuOpGroup = 16;
 __host__ __device__ inline int muop_rows(int nblk) { return kMuOpGroup * ((nblk + 3 + kMuOpGroup - 1) / kMuOpGroup); }
-constexpr int kAsgTok = 1024;    // tokens per k-means assignment / sort chunk
+// Tokens per k-means assignment / sort chunk (one workgroup each): 1024,
+// halved down to 256 while the B*H*chunks grid would not fill the GPU
+// several times over (short sequences).
+constexpr int kAsgTokMax = 1024;
+constexpr int kAsgTokMin = 256;
+__host__ __device__ inline int asg_tokens(int64_t BH, int S) {
+  int t = kAsgTokMax;
+  while (t > kAsgTokMin && BH * ((S + t - 1) / t) < 1024) t >>= 1;
+  return t;
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -169,7 +178,8 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~stati
 __host__ __device__ inline Scratch scratch_layout(int64_t BH, int S, int k, int nrep) {
   Scratch s;
   size_t o = 0;
-  const int64_t nchunk = (S + kAsgTok - 1) / kAsgTok;
+  const int asg = asg_tokens(BH, S);
+  const int64_t nchunk = (S + asg - 1) / asg;
   s.cent = o;        o = align256(o + sizeof(int32_t) * BH * k * kD);
   s.cent_op = o;     o = align256(o + static_cast<size_t>(BH) * kCentOpBytes);
   s.cnorm = o;       o = align256(o + sizeof(int32_t) * BH * kMaxK);

@@ -53,11 +53,14 @@ __device__ __forceinline__ float sketch1(float x, int shift) {
 // Centroid operands and squared norms for the assignment pass, from the
 // integer centroids of one (b,h) (exact: |c| <= 255 fits bf16, norms < 2^24).
 // Called by a whole block after the centroids are final; `nthr` threads.
-__device__ void write_cent_ops(int bh, int k, const int32_t* cg, uint8_t* cent_op, int32_t* cnorm, int nthr) {
+__device__ void write_cent_ops(int bh, int k, const int32_t* cg, uint8_t* cent_op, int32_t* cnorm, int nthr,
+                               int c0 = 0, int c1 = kMaxK) {
+  // operands and norms of centroids c0 .. c1-1 (c >= k: absent, zero operand)
   uint8_t* op = cent_op + static_cast<int64_t>(bh) * kCentOpBytes;
   for (int u = threadIdx.x; u < 4 * 4 * 64; u += nthr) {
     const int ct = u >> 8, kk = (u >> 6) & 3, lane = u & 63;
     const int c = 16 * ct + (lane & 15), d0 = 32 * kk + 8 * (lane >> 4);
+    if (c < c0 || c >= c1) continue;
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -67,21 +70,26 @@ __device__ void write_cent_ops(int bh, int k, const int32_t* cg, uint8_t* cent_o
     }
     *reinterpret_cast<uint4*>(op + static_cast<int64_t>(u) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  for (int c = threadIdx.x; c < kMaxK; c += nthr) {
+  // squared norms, one wave per centroid at a time: lane l adds dims 2l, 2l+1
+  // (exact integers, so the order of the sum does not matter)
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nwv = nthr >> 6;
+  for (int c = c0 + wv; c < c1; c += nwv) {
     int32_t n2 = 0x7FFFFFFF;                    // absent centroid: never the minimum
     if (c < k) {
-      n2 = 0;
-      for (int d = 0; d < kD; ++d) n2 += cg[c * kD + d] * cg[c * kD + d];
+      const int32_t a = cg[c * kD + 2 * lane], b = cg[c * kD + 2 * lane + 1];
+      n2 = a * a + b * b;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) n2 += __shfl_xor(n2, o, 64);
     }
-    cnorm[bh * kMaxK + c] = n2;
+    if (lane == 0) cnorm[bh * kMaxK + c] = n2;
   }
 }
 
-// Sketch shift and seeded strided initial centroids.  grid (BH), 128 threads.
-__global__ void __launch_bounds__(128) k_kmeans_init(TensorArg v, int S, int H, int k, uint64_t seed,
+// Sketch shift and seeded strided initial centroids.  grid (BH), 256 threads.
+__global__ void __launch_bounds__(256) k_kmeans_init(TensorArg v, int S, int H, int k, uint64_t seed,
                                                      vc_head_hdr* hdr, int32_t* cent, int32_t* csum,
                                                      int32_t* ccount, uint8_t* cent_op, int32_t* cnorm) {
-  const int bh = blockIdx.x, b = bh / H, h = bh % H, d = threadIdx.x;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
   const float a = __uint_as_float(hdr[bh].v_amax_bits);
   int shift = 0;
   if (a > 0.0f) {
@@ -89,21 +97,33 @@ __global__ void __launch_bounds__(128) k_kmeans_init(TensorArg v, int S, int H, 
     frexpf(a, &e);              // a in [2^(e-1), 2^e)
     shift = 8 - e;              // 7 - floor(log2 a)
   }
-  if (d == 0) hdr[bh].shift = shift;
+  if (tid == 0) hdr[bh].shift = shift;
   const int stride = S / k > 1 ? S / k : 1;
   const int phi = static_cast<int>(splitmix64(seed ^ static_cast<uint64_t>(bh)) % static_cast<uint64_t>(stride));
-  for (int c = 0; c < k; ++c) {
-    const int t = static_cast<int>((static_cast<int64_t>(c) * S) / k) + phi;
-    const float x = load1(v.p, b * v.sB + t * v.sS + h * v.sH + d, v.dtype);
-    cent[(static_cast<int64_t>(bh) * k + c) * kD + d] = static_cast<int32_t>(sketch1(x, shift));
-    csum[(static_cast<int64_t>(bh) * k + c) * kD + d] = 0;
+  // (centroid c, dim d) pairs i = 128c + d, 32 per thread; every load is
+  // issued before the first store (c*S < 2^31 for S <= 2^24, k <= 64)
+  constexpr int kPer = kMaxK * kD / 256;
+  float xs[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + 256 * j, c = i >> 7, d = i & (kD - 1);
+    const int t = (c * S) / k + phi;
+    xs[j] = c < k ? load1(v.p, b * v.sB + static_cast<int64_t>(t) * v.sS + h * v.sH + d, v.dtype) : 0.0f;
   }
-  if (d < k) ccount[bh * k + d] = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + 256 * j, c = i >> 7;
+    if (c < k) {
+      cent[static_cast<int64_t>(bh) * k * kD + i] = static_cast<int32_t>(sketch1(xs[j], shift));
+      csum[static_cast<int64_t>(bh) * k * kD + i] = 0;
+    }
+  }
+  if (tid < k) ccount[bh * k + tid] = 0;
   __syncthreads();
-  write_cent_ops(bh, k, cent + static_cast<int64_t>(bh) * k * kD, cent_op, cnorm, 128);
+  write_cent_ops(bh, k, cent + static_cast<int64_t>(bh) * k * kD, cent_op, cnorm, 256);
 }
 
-// One Lloyd assignment pass over kAsgTok (1024) tokens per workgroup.
+// One Lloyd assignment pass over asg (asg_tokens: 256..1024) tokens per workgroup.
 //   ACCUM: add the block's per-cluster sketch sums and counts to csum/ccount.
 //   FINAL: write assign[] and the block's cluster histogram (for the sort).
 // Distances run on the matrix core: scores^T = C . X^T with
@@ -113,7 +133,7 @@ __global__ void __launch_bounds__(128) k_kmeans_init(TensorArg v, int S, int H, 
 // is an integer below 2^24, so the fp32 accumulation is exact in any order.
 // Lane l then holds the scores of centroids 16ct + 4(l/16) + i for token
 // l%16: an in-lane argmin over its centroids and a 4-lane combine give the
-// cluster, ties to the lowest index.  grid (ceil(S/1024), H, B), 256 threads.
+// cluster, ties to the lowest index.  grid (ceil(S/asg), H, B), 256 threads.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kSumPitch = kD + 1;   // padded LDS pitch of the per-cluster sums
 
@@ -143,7 +163,7 @@ __device__ __forceinline__ uint32_t sketch_bits(uint32_t e16, int dtype, int shi
 }
 
 template <bool ACCUM, bool FINAL, int NCT>
-__global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k, const vc_head_hdr* hdr,
+__global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k, int asg, const vc_head_hdr* hdr,
                                                        const uint8_t* cent_op, const int32_t* cnorm,
                                                        int32_t* csum, int32_t* ccount, int32_t* assign,
                                                        int32_t* chunk_hist) {
@@ -172,8 +192,8 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
   __syncthreads();
 
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int s0 = blockIdx.x * kAsgTok;
-  constexpr int kIters = kAsgTok / 64;
+  const int s0 = blockIdx.x * asg;
+  const int kIters = asg / 64;
   int tok = s0 + w * 16 + l16;
   TokRaw nxt = load_tok(v, b, h, tok, tok < S, g);
   for (int tt = 0; tt < kIters; ++tt) {
@@ -246,40 +266,44 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
     if (tid < k && cnt[tid] != 0) atomicAdd(&ccount[bh * k + tid], cnt[tid]);
   }
   if (FINAL && tid < k) {
-    const int nchunk = (S + kAsgTok - 1) / kAsgTok;
+    const int nchunk = (S + asg - 1) / asg;
     chunk_hist[(static_cast<int64_t>(bh) * nchunk + blockIdx.x) * k + tid] = cnt[tid];
   }
 }
 
 // New centroid = floor((2*sum + n) / (2n)) (mean rounded half up); empty
 // clusters keep their centroid; sums and counts are cleared for the next pass.
-// grid (BH), 256 threads.
+// The quotient is taken in fp64: |2*sum + n| < 2^53, so the correctly rounded
+// fp64 quotient lies on the same side of every integer as the exact one
+// (|q| <= 255 and a non-integer quotient is >= 1/(2n) >= 2^-25 from one).
+// grid (BH, ceil(k/8)), 256 threads; a workgroup owns 8 centroids.
+constexpr int kUpdCent = 8;
 __global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int32_t* csum, int32_t* ccount,
                                                       uint8_t* cent_op, int32_t* cnorm) {
   const int bh = blockIdx.x;
+  const int c0 = blockIdx.y * kUpdCent, c1 = c0 + kUpdCent < k ? c0 + kUpdCent : k;
   int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
   int32_t* sg = csum + static_cast<int64_t>(bh) * k * kD;
-  for (int i = threadIdx.x; i < k * kD; i += blockDim.x) {
-    const int64_t n = ccount[bh * k + i / kD];
+  for (int i = c0 * kD + threadIdx.x; i < c1 * kD; i += blockDim.x) {
+    const int32_t n = ccount[bh * k + i / kD];
     if (n > 0) {
-      const int64_t num = 2 * static_cast<int64_t>(sg[i]) + n, den = 2 * n;
-      int64_t q = num / den;
-      if ((num % den != 0) && (num < 0)) q -= 1;     // floor division
-      cg[i] = static_cast<int32_t>(q);
+      const int64_t num = 2 * static_cast<int64_t>(sg[i]) + n;
+      cg[i] = static_cast<int32_t>(floor(static_cast<double>(num) / static_cast<double>(2 * n)));
     }
     sg[i] = 0;
   }
   __syncthreads();
-  if (threadIdx.x < k) ccount[bh * k + threadIdx.x] = 0;
-  write_cent_ops(bh, k, cg, cent_op, cnorm, 256);
+  if (threadIdx.x < c1 - c0) ccount[bh * k + c0 + threadIdx.x] = 0;
+  write_cent_ops(bh, k, cg, cent_op, cnorm, 256, c0, c1);
 }
 
 // Per-cluster start offsets and per-chunk offsets for the stable scatter.
 // grid (BH), 64 threads (thread = cluster).
-__global__ void __launch_bounds__(64) k_cluster_scan(int S, int k, const int32_t* chunk_hist, int32_t* chunk_off) {
+__global__ void __launch_bounds__(64) k_cluster_scan(int S, int k, int asg, const int32_t* chunk_hist,
+                                                     int32_t* chunk_off) {
   __shared__ int32_t tot[kMaxK];
   const int bh = blockIdx.x, c = threadIdx.x;
-  const int nchunk = (S + kAsgTok - 1) / kAsgTok;
+  const int nchunk = (S + asg - 1) / asg;
   const int32_t* hst = chunk_hist + static_cast<int64_t>(bh) * nchunk * k;
   int32_t* off = chunk_off + static_cast<int64_t>(bh) * nchunk * k;
   int32_t t = 0;
@@ -299,23 +323,23 @@ __global__ void __launch_bounds__(64) k_cluster_scan(int S, int k, const int32_t
 }
 
 // Stable counting-sort scatter: perm[pos] = token, ordered by (cluster, token).
-// One 1024-token chunk per workgroup, walked in token order in four passes
-// of 256; ranks within a wave come from ballots.  grid (ceil(S/1024), H, B),
+// One asg-token chunk per workgroup, walked in token order in passes of
+// 256; ranks within a wave come from ballots.  grid (ceil(S/1024), H, B),
 // 256 threads.
-__global__ void __launch_bounds__(256) k_cluster_scatter(int S, int k, const int32_t* assign,
+__global__ void __launch_bounds__(256) k_cluster_scatter(int S, int k, int asg, const int32_t* assign,
                                                          const int32_t* chunk_off, int32_t* perm) {
   __shared__ int32_t wcount[4][kMaxK];
   __shared__ int32_t run[kMaxK];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nchunk = (S + kAsgTok - 1) / kAsgTok;
+  const int nchunk = (S + asg - 1) / asg;
   const int32_t* off = chunk_off + (static_cast<int64_t>(bh) * nchunk + blockIdx.x) * k;
   if (tid < kMaxK) run[tid] = 0;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int it = 0; it < kAsgTok / 256; ++it) {
+  for (int it = 0; it < asg / 256; ++it) {
     for (int i = tid; i < 4 * kMaxK; i += 256) (&wcount[0][0])[i] = 0;
     __syncthreads();
-    const int s = blockIdx.x * kAsgTok + it * 256 + tid;
+    const int s = blockIdx.x * asg + it * 256 + tid;
     const bool valid = s < S;
     const int c = valid ? assign[static_cast<int64_t>(bh) * S + s] : -1;
     uint64_t rem = __ballot(valid);
@@ -351,31 +375,48 @@ __global__ void k_identity_perm(int S, int32_t* assign, int32_t* perm) {
 }
 
 // Block means over permuted positions and the residual amax per head.
-// mu = fp32(fp64(sum) / n); R = fp32(v - mu).  grid (nblk, H, B), 128 threads.
-__global__ void __launch_bounds__(128) k_v_block_stats(TensorArg v, int S, int smooth, const int32_t* perm,
+// mu = fp32(fp64(sum) / n), the sum in position order; R = fp32(v - mu).
+// The block's gathered rows are read once, 16 bytes per load, into LDS.
+// grid (nblk, H, B), 256 threads.
+__global__ void __launch_bounds__(256) k_v_block_stats(TensorArg v, int S, int smooth, const int32_t* perm,
                                                        float* v_mean, vc_head_hdr* hdr) {
+  __shared__ uint4 rows[kBlock][kD / 8];      // raw 16-bit values of the block's rows
   __shared__ int32_t pp[kBlock];
   __shared__ float red[16];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const int p0 = blk * kBlock;
   const int n = S - p0 < kBlock ? S - p0 : kBlock;
-  if (d < n) pp[d] = perm[static_cast<int64_t>(bh) * S + p0 + d];
+  if (tid < n) pp[tid] = perm[static_cast<int64_t>(bh) * S + p0 + tid];
   __syncthreads();
-  float mu = 0.0f;
-  if (smooth) {
-    double sum = 0.0;
-    for (int j = 0; j < n; ++j) sum += static_cast<double>(load1(v.p, b * v.sB + pp[j] * v.sS + h * v.sH + d, v.dtype));
-    mu = static_cast<float>(sum / static_cast<double>(n));
+  for (int t = tid; t < n * (kD / 8); t += blockDim.x) {
+    const int j = t >> 4, c8 = (t & 15) * 8;
+    rows[j][t & 15] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(v.p) + b * v.sB +
+                                                      static_cast<int64_t>(pp[j]) * v.sS + h * v.sH + c8);
   }
-  v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + d] = mu;
+  __syncthreads();
   float m = 0.0f;
-  for (int j = 0; j < n; ++j) {
-    const float x = load1(v.p, b * v.sB + pp[j] * v.sS + h * v.sH + d, v.dtype);
-    m = fmaxf(m, fabsf(x - mu));
+  if (tid < kD) {
+    const int d = tid;
+    const uint16_t* col = reinterpret_cast<const uint16_t*>(&rows[0][0]) + d;
+    float mu = 0.0f;
+    if (smooth) {
+      double sum = 0.0;
+      for (int j = 0; j < n; ++j) {
+        const uint32_t e = col[j * kD];
+        sum += static_cast<double>(v.dtype == VC_BF16 ? bf16_bits_to_f32(e) : f16_bits_to_f32(e));
+      }
+      mu = static_cast<float>(sum / static_cast<double>(n));
+    }
+    v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + d] = mu;
+    for (int j = 0; j < n; ++j) {
+      const uint32_t e = col[j * kD];
+      const float x = v.dtype == VC_BF16 ? bf16_bits_to_f32(e) : f16_bits_to_f32(e);
+      m = fmaxf(m, fabsf(x - mu));
+    }
   }
   m = block_max(m, red);
-  if (d == 0 && m > 0.0f) atomicMax(&hdr[bh].r_amax_bits, __float_as_uint(m));
+  if (tid == 0 && m > 0.0f) atomicMax(&hdr[bh].r_amax_bits, __float_as_uint(m));
 }
 
 __device__ __forceinline__ void v_scales(const vc_head_hdr& hd, float* s, float* inv) {
@@ -787,10 +828,10 @@ __global__ void __launch_bounds__(256) k_repair_kpack(int S, int nrep_pad, const
   } while (0)
 
 template <bool ACCUM, bool FINAL>
-void launch_assign(dim3 grid, hipStream_t st, const TensorArg& v, int S, int k, const WsPtrs& ws) {
+void launch_assign(dim3 grid, hipStream_t st, const TensorArg& v, int S, int k, int asg, const WsPtrs& ws) {
   const int nct = (k + 15) / 16;     // 1..4 (k <= 64)
 #define VC_ASSIGN(N)                                                                                    \
-  hipLaunchKernelGGL((k_kmeans_assign<ACCUM, FINAL, N>), grid, dim3(256), 0, st, v, S, k, ws.hdr, ws.cent_op, \
+  hipLaunchKernelGGL((k_kmeans_assign<ACCUM, FINAL, N>), grid, dim3(256), 0, st, v, S, k, asg, ws.hdr, ws.cent_op, \
                      ws.cnorm, ws.csum, ws.ccount, ws.assign, ws.chunk_hist)
   if (nct == 1) VC_ASSIGN(1);
   else if (nct == 2) VC_ASSIGN(2);
@@ -807,31 +848,33 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
                      static_cast<int64_t>(BH) * (sizeof(vc_head_hdr) / 4));
   VC_LAUNCH_CHECK();
   if (o.smooth) {
-    const int nch = (S + kAsgTok - 1) / kAsgTok;
+    const int asg = asg_tokens(BH, S);
+    const int nch = (S + asg - 1) / asg;
     hipLaunchKernelGGL(k_v_absmax, dim3((S + 63) / 64, H, B), dim3(256), 0, st, v, S, ws.hdr);
     VC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_kmeans_init, dim3(BH), dim3(128), 0, st, v, S, H, k, o.seed, ws.hdr, ws.cent, ws.csum,
+    hipLaunchKernelGGL(k_kmeans_init, dim3(BH), dim3(256), 0, st, v, S, H, k, o.seed, ws.hdr, ws.cent, ws.csum,
                        ws.ccount, ws.cent_op, ws.cnorm);
     VC_LAUNCH_CHECK();
     for (int it = 0; it < o.iters; ++it) {
-      launch_assign<true, false>(dim3(nch, H, B), st, v, S, k, ws);
+      launch_assign<true, false>(dim3(nch, H, B), st, v, S, k, asg, ws);
       VC_LAUNCH_CHECK();
-      hipLaunchKernelGGL(k_kmeans_update, dim3(BH), dim3(256), 0, st, k, ws.cent, ws.csum, ws.ccount, ws.cent_op,
+      hipLaunchKernelGGL(k_kmeans_update, dim3(BH, (k + kUpdCent - 1) / kUpdCent), dim3(256), 0, st, k, ws.cent,
+                         ws.csum, ws.ccount, ws.cent_op,
                          ws.cnorm);
       VC_LAUNCH_CHECK();
     }
-    launch_assign<false, true>(dim3(nch, H, B), st, v, S, k, ws);
+    launch_assign<false, true>(dim3(nch, H, B), st, v, S, k, asg, ws);
     VC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_cluster_scan, dim3(BH), dim3(64), 0, st, S, k, ws.chunk_hist, ws.chunk_off);
+    hipLaunchKernelGGL(k_cluster_scan, dim3(BH), dim3(64), 0, st, S, k, asg, ws.chunk_hist, ws.chunk_off);
     VC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_cluster_scatter, dim3(nch, H, B), dim3(256), 0, st, S, k, ws.assign, ws.chunk_off,
+    hipLaunchKernelGGL(k_cluster_scatter, dim3(nch, H, B), dim3(256), 0, st, S, k, asg, ws.assign, ws.chunk_off,
                        ws.perm);
     VC_LAUNCH_CHECK();
   } else {
     hipLaunchKernelGGL(k_identity_perm, dim3((S + 255) / 256, H, B), dim3(256), 0, st, S, ws.assign, ws.perm);
     VC_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(k_v_block_stats, gblk, dim3(128), 0, st, v, S, o.smooth, ws.perm, ws.v_mean, ws.hdr);
+  hipLaunchKernelGGL(k_v_block_stats, gblk, dim3(256), 0, st, v, S, o.smooth, ws.perm, ws.v_mean, ws.hdr);
   VC_LAUNCH_CHECK();
   // restore operands: zero first (blocks past the last stay zero)
   hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws.v_muop), 0u,
