@@ -18,6 +18,9 @@
 //   O     = 2^(M-M') * O + P . V8 + r * mu_b / s_v
 // then the repair tiles add P_rep . E8 (scale s_e, codes against the final
 // M, not added to l) and out = bf16(s_v * (O + (s_e/s_v) O_rep) / l).
+// With the 4-bit V residual the P.V MFMA takes block scales anyway, so O, l
+// and the row sums there stay relative to an anchor A <= M and the codes'
+// MFMA scale 2^(M-A) replaces the rescale (exact: powers of two).
 //
 // Layout and schedule:
 //   * one workgroup = 8 waves = two 128-query blocks of one (b,h); wave w
@@ -35,8 +38,9 @@
 //     of tile kb, and each MFMA carries half an ExpCast (and the running
 //     max) of an earlier score sub-tile; the codes are cast speculatively
 //     against the maximum before the tile and recast from the kept scores
-//     only when the tile raised some row's maximum (decided from each
-//     lane's partial maximum, without the cross-row combine) or is ragged;
+//     only for a 16-query sub-tile whose maximum the tile raised (decided
+//     from each lane's partial maximum, without the cross-row combine), and
+//     for ragged tiles;
 //   * the block-mean restore r_b * mu_b/s_v is deferred: each tile's row sum
 //     is kept (and rescaled with O), and every 16 tiles the sums meet the
 //     prepared mu/s_v operands in 16x16x16 bf16 MFMAs (high/low bf16 parts,
@@ -57,6 +61,13 @@ constexpr int kOnes4 = 0x38383838;
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
   // cbsz = blgp = 0: both operands OCP E4M3; no block scales
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// Same with a power-of-two scale on the B operand's columns: byte QI of se
+// is the E8M0 exponent (127 = 1.0) that every lane applies to its column;
+// byte 2 of se is 127, the scale of A (one register serves both).
+template <int QI>
+__device__ __forceinline__ v4f mfma_fp8_sb(const v8i& a, const v8i& b, const v4f& c, int se) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 2, se, QI, se);
 }
 
 __device__ __forceinline__ v8i ld_op_lds(const uint8_t* base, int sub, int lane) {
@@ -199,7 +210,19 @@ struct SoftState {
   float M[2];      // integer log2 running maximum (kNegBig before the first tile)
   float l[2];      // running row sum
   float cq[2];     // cast_const(M) (120 - 8*M): the cast constant for the current maximum
+  // MXFP4 V: O, l and the restore weights are held relative to an anchor
+  // maximum A <= M per query instead of M itself: byte qi of se is
+  // 127 + (M - A), the E8M0 scale that the P.V and row-sum MFMAs put on codes
+  // cast against M (byte 2 is 127, the ones operand's scale).  A rise of M
+  // then changes one byte instead of rescaling every accumulator; A moves up
+  // to M (with the rescale) only once M - A would pass kAnchorSpan.  E4M3 V
+  // keeps A = M (the unscaled MFMA is the faster one there) and se at 127.
+  int se;
 };
+// Largest M - A kept before the accumulators are rescaled: O stays below
+// 2^(kAnchorSpan + 41) (codes <= 256, |V| <= 448, <= 2^24 keys), far from
+// the FP32 limit.
+constexpr int kAnchorSpan = 64;
 
 // ExpCast and running max of half an accumulator (keys i0, i0+1 of one
 // 16-key sub-tile): two FMAs, two conversions into the packed code dword and
@@ -228,19 +251,21 @@ __device__ __forceinline__ v8i ld_vop(const uint8_t* vl, int dt) {
   v8i r = {static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z), static_cast<int>(c.w), 0, 0, 0, 0};
   return r;
 }
-// O^T[dt] += V^T[dt] . P^T; for MXFP4 with the lane's E8M0 scale of this dt
-// (byte dt%4 of vsc[dt/4]) on V and scale 1 (127) on P.
+// O^T[dt] += V^T[dt] . P^T for query sub-tile QI, with byte QI of se on P
+// (codes relative to the anchor, SoftState::se); for MXFP4 also the lane's
+// E8M0 scale of this dt (byte dt%4 of vsc[dt/4]) on V.
 // (dt is a constant once the caller's loop is unrolled; the byte select is
 // an immediate of the instruction, hence the switch)
-template <int VF>
-__device__ __forceinline__ v4f pv_mfma(const v8i& vop, const v8i& p, const v4f& o, const uint32_t (&vsc)[2], int dt) {
+template <int VF, int QI>
+__device__ __forceinline__ v4f pv_mfma(const v8i& vop, const v8i& p, const v4f& o, const uint32_t (&vsc)[2], int dt,
+                                       int se) {
   if (VF == 0) return mfma_fp8(vop, p, o);
   const int sc = static_cast<int>(vsc[dt >> 2]);
   switch (dt & 3) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 0, sc, 0, 127);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 1, sc, 0, 127);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 2, sc, 0, 127);
-    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 3, sc, 0, 127);
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 0, sc, QI, se);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 1, sc, QI, se);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 2, sc, QI, se);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, p, o, 4, 0, 3, sc, QI, se);
   }
 }
 
@@ -248,7 +273,7 @@ template <int VF, typename Copies>
 __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* vt, int lane, const v8i (&qop)[2],
                                            const v8i (&P)[2], float s8, const float (&cq)[2], v4f (&sc)[8][2],
                                            v8i (&Pn)[2], float (&mx)[2], v4f (&O)[8][2], float (&r)[2],
-                                           const Copies& cp) {
+                                           int se, const Copies& cp) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const v8i ones = {kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4};
   const uint8_t* kl = ktile + lane;   // lane = the lane's byte offset (16 * lane id)
@@ -290,14 +315,16 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
     if (t + 2 < 8) kop[t & 1] = ld_op_lds_at(kl, t + 2);
     __builtin_amdgcn_sched_barrier(0);
     // slot 4t+2: P.V channels t, query sub-tile 0; first half of (t, 0)
-    O[t][0] = pv_mfma<VF>(vop[t & 1], P[0], O[t][0], vsc, t);
+    O[t][0] = pv_mfma<VF, 0>(vop[t & 1], P[0], O[t][0], vsc, t, se);
+    asm volatile("" : "+v"(O[t][0]));
     __builtin_amdgcn_sched_barrier(0);
     w[t][0] = 0;
     expcast_half(sc[t][0], 0, s8, cq[0], w[t][0], mx[0]);
     asm volatile("" : "+v"(w[t][0]), "+v"(mx[0]));
     __builtin_amdgcn_sched_barrier(0);
     // slot 4t+3: P.V channels t, sub-tile 1; second half of (t, 0)
-    O[t][1] = pv_mfma<VF>(vop[t & 1], P[1], O[t][1], vsc, t);
+    O[t][1] = pv_mfma<VF, 1>(vop[t & 1], P[1], O[t][1], vsc, t, se);
+    asm volatile("" : "+v"(O[t][1]));
     __builtin_amdgcn_sched_barrier(0);
     expcast_half(sc[t][0], 2, s8, cq[0], w[t][0], mx[0]);
     Pn[0][t] = static_cast<int>(w[t][0]);
@@ -307,13 +334,15 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
     __builtin_amdgcn_sched_barrier(0);
   }
   // row sums of tile kb; ExpCast of (7, 1) under them
-  const v4f r0 = mfma_fp8(ones, P[0], zero);
+  v4f r0 = VF ? mfma_fp8_sb<0>(ones, P[0], zero, se) : mfma_fp8(ones, P[0], zero);
+  asm volatile("" : "+v"(r0));
   __builtin_amdgcn_sched_barrier(0);
   w[7][1] = 0;
   expcast_half(sc[7][1], 0, s8, cq[1], w[7][1], mx[1]);
   asm volatile("" : "+v"(w[7][1]), "+v"(mx[1]));
   __builtin_amdgcn_sched_barrier(0);
-  const v4f r1 = mfma_fp8(ones, P[1], zero);
+  v4f r1 = VF ? mfma_fp8_sb<1>(ones, P[1], zero, se) : mfma_fp8(ones, P[1], zero);
+  asm volatile("" : "+v"(r1));
   __builtin_amdgcn_sched_barrier(0);
   expcast_half(sc[7][1], 2, s8, cq[1], w[7][1], mx[1]);
   Pn[1][7] = static_cast<int>(w[7][1]);
@@ -533,17 +562,21 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
   const float s8 = cast_scale(sigma);
   v8i Pn[2];
   float alpha[2], r[2];
-  bool changed;
+  bool resc[2] = {false, false};
   {
     v4f sc[8][2];
     float mx[2];
-    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, s8, acc.st.cq, sc, Pn, mx, acc.O, r, cp);
+    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, s8, acc.st.cq, sc, Pn, mx, acc.O, r, acc.st.se, cp);
     const bool ragged = kb + 2 >= nblk;
     // Did any row's maximum rise?  ceil(fl(m*sigma)) > M for an integer M
     // exactly when fl(m*sigma) > M, and fl(m*sigma) is monotone in m, so
     // each lane's partial maximum decides without the cross-row combine.
-    changed = __any(mx[0] * sigma > acc.st.M[0] || mx[1] * sigma > acc.st.M[1]);
-    if (__builtin_expect(changed || ragged, 0)) {
+    // Decided per query sub-tile: only a sub-tile whose maximum rose is
+    // recast (and rescaled).
+    bool ch[2];
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) ch[qi] = ragged || __any(mx[qi] * sigma > acc.st.M[qi]);
+    if (__builtin_expect(ch[0] || ch[1], 0)) {
       if (ragged) {
         mask_tile(sc, g, kb + 2 == nblk ? c.kval_last : 0);
 #pragma unroll
@@ -553,15 +586,26 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
           for (int t = 1; t < 8; ++t) mx[qi] = max_acc4(mx[qi], sc[t][qi]);
         }
       }
-      float mn[2];
-#pragma unroll
-      for (int qi = 0; qi < 2; ++qi) mn[qi] = fmaxf(acc.st.M[qi], ceilf(max_over_rows(mx[qi]) * sigma));
-      changed = __any(mn[0] != acc.st.M[0] || mn[1] != acc.st.M[1]);
 #pragma unroll
       for (int qi = 0; qi < 2; ++qi) {
-        alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn[qi], -160.0f)));
-        acc.st.M[qi] = mn[qi];
-        acc.st.cq[qi] = cast_const(mn[qi]);
+        if (!ch[qi]) continue;
+        const float mn = fmaxf(acc.st.M[qi], ceilf(max_over_rows(mx[qi]) * sigma));
+        if (VF == 0) {
+          // codes and accumulators against M: rescale by 2^(M - M')
+          alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn, -160.0f)));
+        } else {
+          // the anchor scale of the new codes, 127 + (M' - A); past the span
+          // the anchor moves up to M' and the accumulators are rescaled by
+          // 2^(A - M')
+          const int e = static_cast<int>((acc.st.se >> (8 * qi)) & 0xFF) - 127 +
+                        static_cast<int>(fminf(mn - acc.st.M[qi], 2.0f * kAnchorSpan));
+          const bool far = e > kAnchorSpan;
+          alpha[qi] = far ? ldexpf(1.0f, -e) : 1.0f;
+          acc.st.se = (acc.st.se & ~(0xFF << (8 * qi))) | ((far ? 127 : 127 + e) << (8 * qi));
+        }
+        resc[qi] = __any(alpha[qi] != 1.0f);
+        acc.st.M[qi] = mn;
+        acc.st.cq[qi] = cast_const(mn);
 #pragma unroll
         for (int t = 0; t < 8; ++t) Pn[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, acc.st.cq[qi]));
       }
@@ -574,9 +618,9 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
     acc.rr[J][0] = r[0];
     acc.rr[J][1] = r[1];
   }
-  if (changed) {
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
+  for (int qi = 0; qi < 2; ++qi) {
+    if (__builtin_expect(resc[qi], 0)) {
       acc.st.l[qi] *= alpha[qi];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) acc.O[dt][qi] *= alpha[qi];
@@ -680,6 +724,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   TileAcc acc;
   acc.st.M[0] = acc.st.M[1] = kNegBig;
   acc.st.l[0] = acc.st.l[1] = 0.0f;
+  acc.st.se = 0x7F7F7F7F;   // the anchor starts at tile 0's maximum
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc.O[dt][0] = acc.O[dt][1] = zero;
 #pragma unroll
@@ -786,8 +831,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const v8i eop = ld_op_global(re + static_cast<int64_t>(rt) * kTileBytes, dt, lane);
-        const v4f o0 = mfma_fp8(eop, Pr[0], zero);
-        const v4f o1 = mfma_fp8(eop, Pr[1], zero);
+        // codes against M, accumulators against the anchor
+        const v4f o0 = mfma_fp8_sb<0>(eop, Pr[0], zero, st.se);
+        const v4f o1 = mfma_fp8_sb<1>(eop, Pr[1], zero, st.se);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           O[dt][0][i] = fmaf(fe, o0[i], O[dt][0][i]);
