@@ -539,14 +539,19 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane16, 
 
 // One tile step kb (J = kb mod 4): the interleaved MFMA phase (scores of
 // tile kb+1 with K in kcur, P.V and row sums of tile kb with V in vcur),
-// the maximum check (codes recomputed from the kept scores if the tile
-// raised the maximum or is ragged), tile kb's row sum into l and into the
-// deferred restore weights, and the rescale of O, l and the weights.
-// After the last tile of a group of 16 the group's restore runs.  Copies
-// run three steps ahead: this step copies K(kb+4) into kfree, V(kb+3) into
-// vfree and restore-operand row kb+3 (distinct LDS arrays, so the copies
-// overlap the reads of this step and the next two), as its last
-// vector-memory instructions (see step_barrier).  Tile indices past the
+// the step barrier, the maximum check per query sub-tile (codes recomputed
+// from the kept scores where the tile raised the maximum, and for ragged
+// tiles), tile kb's row sum into l and into the deferred restore weights,
+// and the rescale of O, l and the weights of a sub-tile whose maximum rose
+// (MXFP4: only when the anchor moves).  After the last tile of a group of
+// 16 the group's restore runs.  Copies run three steps ahead: this step
+// copies K(kb+4) into kfree, V(kb+3) into vfree and restore-operand row
+// kb+3 (distinct LDS arrays, so the copies overlap the reads of this step
+// and the next two), as its last vector-memory instructions (see
+// step_barrier).  Everything after the barrier works in registers or on a
+// restore-operand group copied at least three steps before and not
+// refilled for another thirteen, so it needs no barrier of its own.  Tile
+// indices past the
 // last tile are clamped to it and a score tile past the end is masked out
 // entirely, which leaves the state unchanged (alpha = 1, codes 0): every
 // step runs the same code.
@@ -567,6 +572,11 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
     v4f sc[8][2];
     float mx[2];
     mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, s8, acc.st.cq, sc, Pn, mx, acc.O, r, acc.st.se, cp);
+    // the step's LDS reads and copies are all issued: the rest of the step
+    // works in registers (and on restore operands copied long before), so
+    // a wave that recasts or restores runs on while the others start the
+    // next step
+    step_barrier<VF>();
     const bool ragged = kb + 2 >= nblk;
     // Did any row's maximum rise?  ceil(fl(m*sigma)) > M for an integer M
     // exactly when fl(m*sigma) > M, and fl(m*sigma) is monotone in m, so
@@ -644,7 +654,6 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
       restore_mfma<4>(A, 4 * half, bh, bl, acc.O);
     }
   }
-  step_barrier<VF>();
 }
 
 template <int VF>
