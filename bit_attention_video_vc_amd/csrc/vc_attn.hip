@@ -31,16 +31,16 @@
 //   * the S^T accumulator bytes (keys 16t+4g+i for lane group g) are exactly
 //     the B-operand slots of O^T = V^T.P^T, so P never leaves registers; the
 //     prepare stage stores V8 in that slot order;
-//   * K and V tiles (16 KB each) stream through a 4-deep LDS ring, copied
-//     straight from global memory into LDS three tiles ahead, one barrier
-//     per tile;
-//   * one step interleaves the score MFMAs of tile kb+1 with the P.V MFMAs
-//     of tile kb, and each MFMA carries half an ExpCast (and the running
-//     max) of an earlier score sub-tile; the codes are cast speculatively
-//     against the maximum before the tile and recast from the kept scores
-//     only for a 16-query sub-tile whose maximum the tile raised (decided
-//     from each lane's partial maximum, without the cross-row combine), and
-//     for ragged tiles;
+//   * K and V tiles (16 KB each) stream through 4-deep LDS rings, copied
+//     straight from global memory into LDS three steps ahead, one barrier
+//     per step;
+//   * scores run one tile ahead of their cast: step kb does the P.V MFMAs
+//     of tile kb and then the score MFMAs of tile kb+2, and under them the
+//     vector ALU casts tile kb+1's scores (computed by the previous step)
+//     against the maximum after tile kb+1 and keeps the running max of tile
+//     kb+2's; so a code is cast once, against the final maximum of its own
+//     tile.  Whether a maximum rose is decided from each lane's partial
+//     maximum; the cross-row combine runs only when one did;
 //   * the block-mean restore r_b * mu_b/s_v is deferred: each tile's row sum
 //     is kept (and rescaled with O), and every 16 tiles the sums meet the
 //     prepared mu/s_v operands in 16x16x16 bf16 MFMAs (high/low bf16 parts,
@@ -224,24 +224,17 @@ struct SoftState {
 // the FP32 limit.
 constexpr int kAnchorSpan = 64;
 
-// ExpCast and running max of half an accumulator (keys i0, i0+1 of one
-// 16-key sub-tile): two FMAs, two conversions into the packed code dword and
-// one 3-input max.
-__device__ __forceinline__ void expcast_half(const v4f& s, int i0, float s8, float c, uint32_t& w, float& mx) {
+// Half the ExpCast of an accumulator (keys i0, i0+1 of one 16-key
+// sub-tile): two FMAs and two conversions into the packed code dword.
+__device__ __forceinline__ void cast_half(const v4f& s, int i0, float s8, float c, uint32_t& w) {
   w = pcast2(s[i0], s[i0 + 1], s8, c, i0 >> 1, w);
-  mx = fmaxf(fmaxf(mx, s[i0]), s[i0 + 1]);
+}
+// Running max over one accumulator: two 3-input maxima.
+__device__ __forceinline__ void max_acc(const v4f& s, float& mx) {
+  mx = fmaxf(fmaxf(mx, s[0]), s[1]);
+  mx = fmaxf(fmaxf(mx, s[2]), s[3]);
 }
 
-// The matrix-core work of one step, interleaved: for each 16-key/16-channel
-// sub-tile t, the score MFMAs of tile kb+1 (K in LDS, both query sub-tiles)
-// and the P.V MFMAs of tile kb (V in LDS, codes P of tile kb), then the two
-// row-sum MFMAs of tile kb (codes against a tile of E4M3 ones).  Every MFMA
-// is followed by half the ExpCast of one earlier score sub-tile (issued at
-// least two MFMAs before, so its result is ready) -- speculatively, against
-// the running maximum before this tile (cq = 120 - 8*M) -- so the vector
-// ALU work runs under the matrix core instead of after it.  Order and
-// placement are fixed with scheduling barriers.  K and V operands are read
-// from LDS two sub-tiles ahead; copy parts 0..5 go out one per sub-tile.
 // The V operand of channel sub-tile dt: E4M3, 32 bytes per lane; MXFP4, 16
 // bytes of E2M1 codes per lane (the matrix core reads four registers).
 template <int VF>
@@ -269,15 +262,51 @@ __device__ __forceinline__ v4f pv_mfma(const v8i& vop, const v8i& p, const v4f& 
   }
 }
 
+// The new maximum of query sub-tile qi from the held tile's partial row
+// maxima: the cross-row combine, the integer ceiling and the cast constant;
+// d = how far it rose (>= 0, an integer).  Did any row's maximum rise?
+// ceil(fl(m*sigma)) > M for an integer M exactly when fl(m*sigma) > M, and
+// fl(m*sigma) is monotone in m, so each lane's partial maximum decides
+// without the cross-row combine, which then runs only when one did (a
+// wave-uniform branch).
+__device__ __forceinline__ void new_max(SoftState& st, int qi, float mh, float sig, float& d) {
+  d = 0.0f;
+  if (__builtin_expect(__any(mh * sig > st.M[qi]), 0)) {
+    const float mn = fmaxf(st.M[qi], ceilf(max_over_rows(mh) * sig));
+    d = mn - st.M[qi];
+    st.M[qi] = mn;
+    st.cq[qi] = cast_const(mn);
+  }
+}
+
+// The matrix-core work of one step kb, in two halves.  First the P.V MFMAs
+// of tile kb (V in LDS, codes P of tile kb) and its two row-sum MFMAs
+// (codes against a tile of E4M3 ones); under them the vector ALU finishes
+// the running max of tile kb+1's scores (sh, computed by the previous step,
+// with per-lane partial maxima mh), takes the maximum after tile kb+1 and
+// starts the ExpCast of those scores against it into Pn.  Then the score
+// MFMAs of tile kb+2 (K in LDS, both query sub-tiles) into sn; under them
+// the rest of the cast and the per-lane running max (mn) of the new scores
+// (sub-tile 7's max is left to the next step).  A tile's maximum is thus
+// known before its codes are cast, so no cast is ever redone; and the held
+// scores are cast before the new ones arrive, so the two sets share
+// registers.  Each MFMA is followed by a few of these instructions (a score
+// sub-tile is read two MFMAs after it was issued, so its result is ready);
+// order and placement are fixed with scheduling barriers.  Operands are
+// read from LDS two sub-tiles ahead; copy parts 0..5 go out spread over the
+// step.
 template <int VF, typename Copies>
 __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* vt, int lane, const v8i (&qop)[2],
-                                           const v8i (&P)[2], float s8, const float (&cq)[2], v4f (&sc)[8][2],
-                                           v8i (&Pn)[2], float (&mx)[2], v4f (&O)[8][2], float (&r)[2],
-                                           int se, const Copies& cp) {
+                                           const v8i (&P)[2], float sig, SoftState& st, float (&d)[2],
+                                           const v4f (&sh)[8][2], const float (&mh)[2], v4f (&sn)[8][2],
+                                           v8i (&Pn)[2], float (&mn)[2], v4f (&O)[8][2], float (&r)[2],
+                                           const Copies& cp) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const v8i ones = {kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4};
   const uint8_t* kl = ktile + lane;   // lane = the lane's byte offset (16 * lane id)
   const uint8_t* vl = vt + lane;
+  const float s8 = cast_scale(sig);
+  const int se = st.se;
   v8i kop[2], vop[2];
   uint32_t vsc[2] = {0u, 0u};
   if (VF) {
@@ -286,70 +315,94 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
     vsc[0] = s2.x;
     vsc[1] = s2.y;
   }
-  kop[0] = ld_op_lds_at(kl, 0);
   vop[0] = ld_vop<VF>(vl, 0);
-  kop[1] = ld_op_lds_at(kl, 1);
   vop[1] = ld_vop<VF>(vl, 1);
   uint32_t w[8][2];
-  mx[0] = mx[1] = kNegBig;
+  float mx[2] = {mh[0], mh[1]};
+  // cast half i of the held scores: sub-tile i/4, query sub-tile (i/2)%2,
+  // keys 2*(i%2) and 2*(i%2)+1 of the lane's four
+  auto half = [&](int i) {
+    const int t = i >> 2, q = (i >> 1) & 1, h = i & 1;
+    if (h == 0) w[t][q] = 0;
+    cast_half(sh[t][q], 2 * h, s8, st.cq[q], w[t][q]);
+    if (h == 1) {
+      Pn[q][t] = static_cast<int>(w[t][q]);
+      asm volatile("" : "+v"(Pn[q][t]));
+    } else {
+      asm volatile("" : "+v"(w[t][q]));
+    }
+  };
   __builtin_amdgcn_sched_barrier(0);
+  // ---- first half: 18 slots ----
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    // slot 4t: scores (t, 0); ExpCast of (t-1, 1), first half
-    sc[t][0] = mfma_fp8(kop[t & 1], qop[0], zero);
+  for (int dt = 0; dt < 8; ++dt) {
+    O[dt][0] = pv_mfma<VF, 0>(vop[dt & 1], P[0], O[dt][0], vsc, dt, se);
+    asm volatile("" : "+v"(O[dt][0]));
     __builtin_amdgcn_sched_barrier(0);
-    if (t >= 1) {
-      w[t - 1][1] = 0;
-      expcast_half(sc[t - 1][1], 0, s8, cq[1], w[t - 1][1], mx[1]);
-      asm volatile("" : "+v"(w[t - 1][1]), "+v"(mx[1]));
+    if (dt == 0) {
+      // the held tile's last sub-tile, then the maximum after it
+      max_acc(sh[7][0], mx[0]);
+      new_max(st, 0, mx[0], sig, d[0]);
+      asm volatile("" : "+v"(st.cq[0]), "+v"(d[0]));
+    } else {
+      half(2 * dt - 1);                    // slots 2, 4, .. 14: halves 1, 3, .. 13
     }
     __builtin_amdgcn_sched_barrier(0);
-    // slot 4t+1: scores (t, 1); second half of (t-1, 1)
-    sc[t][1] = mfma_fp8(kop[t & 1], qop[1], zero);
+    O[dt][1] = pv_mfma<VF, 1>(vop[dt & 1], P[1], O[dt][1], vsc, dt, se);
+    asm volatile("" : "+v"(O[dt][1]));
     __builtin_amdgcn_sched_barrier(0);
-    if (t >= 1) {
-      expcast_half(sc[t - 1][1], 2, s8, cq[1], w[t - 1][1], mx[1]);
-      Pn[1][t - 1] = static_cast<int>(w[t - 1][1]);
-      asm volatile("" : "+v"(Pn[1][t - 1]), "+v"(mx[1]));
+    if (dt == 0) {
+      max_acc(sh[7][1], mx[1]);
+      new_max(st, 1, mx[1], sig, d[1]);
+      asm volatile("" : "+v"(st.cq[1]), "+v"(d[1]));
+      half(0);
+    } else {
+      half(2 * dt);                        // slots 3, 5, .. 15: halves 2, 4, .. 14
     }
-    if (t + 2 < 8) kop[t & 1] = ld_op_lds_at(kl, t + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    // slot 4t+2: P.V channels t, query sub-tile 0; first half of (t, 0)
-    O[t][0] = pv_mfma<VF, 0>(vop[t & 1], P[0], O[t][0], vsc, t, se);
-    asm volatile("" : "+v"(O[t][0]));
-    __builtin_amdgcn_sched_barrier(0);
-    w[t][0] = 0;
-    expcast_half(sc[t][0], 0, s8, cq[0], w[t][0], mx[0]);
-    asm volatile("" : "+v"(w[t][0]), "+v"(mx[0]));
-    __builtin_amdgcn_sched_barrier(0);
-    // slot 4t+3: P.V channels t, sub-tile 1; second half of (t, 0)
-    O[t][1] = pv_mfma<VF, 1>(vop[t & 1], P[1], O[t][1], vsc, t, se);
-    asm volatile("" : "+v"(O[t][1]));
-    __builtin_amdgcn_sched_barrier(0);
-    expcast_half(sc[t][0], 2, s8, cq[0], w[t][0], mx[0]);
-    Pn[0][t] = static_cast<int>(w[t][0]);
-    asm volatile("" : "+v"(Pn[0][t]), "+v"(mx[0]));
-    if (t + 2 < 8) vop[t & 1] = ld_vop<VF>(vl, t + 2);
-    if (t < 6) cp.issue(t);
+    if (dt + 2 < 8) vop[dt & 1] = ld_vop<VF>(vl, dt + 2);
+    if (dt == 7) kop[0] = ld_op_lds_at(kl, 0);
+    if ((dt & 1) && dt < 6) cp.issue(dt >> 1);      // parts 0, 1, 2
     __builtin_amdgcn_sched_barrier(0);
   }
-  // row sums of tile kb; ExpCast of (7, 1) under them
+  // row sums of tile kb
   v4f r0 = VF ? mfma_fp8_sb<0>(ones, P[0], zero, se) : mfma_fp8(ones, P[0], zero);
   asm volatile("" : "+v"(r0));
   __builtin_amdgcn_sched_barrier(0);
-  w[7][1] = 0;
-  expcast_half(sc[7][1], 0, s8, cq[1], w[7][1], mx[1]);
-  asm volatile("" : "+v"(w[7][1]), "+v"(mx[1]));
+  half(15);
+  half(16);
+  kop[1] = ld_op_lds_at(kl, 1);
   __builtin_amdgcn_sched_barrier(0);
   v4f r1 = VF ? mfma_fp8_sb<1>(ones, P[1], zero, se) : mfma_fp8(ones, P[1], zero);
   asm volatile("" : "+v"(r1));
   __builtin_amdgcn_sched_barrier(0);
-  expcast_half(sc[7][1], 2, s8, cq[1], w[7][1], mx[1]);
-  Pn[1][7] = static_cast<int>(w[7][1]);
-  asm volatile("" : "+v"(Pn[1][7]), "+v"(mx[1]));
+  half(17);
+  half(18);
   __builtin_amdgcn_sched_barrier(0);
   r[0] = r0[0];
   r[1] = r1[0];
+  // ---- second half: 16 slots ----
+  mn[0] = mn[1] = kNegBig;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    sn[t][0] = mfma_fp8(kop[t & 1], qop[0], zero);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t >= 1) {
+      max_acc(sn[t - 1][0], mn[0]);
+      asm volatile("" : "+v"(mn[0]));
+    }
+    if (2 * t < 13) half(19 + 2 * t);
+    __builtin_amdgcn_sched_barrier(0);
+    sn[t][1] = mfma_fp8(kop[t & 1], qop[1], zero);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t >= 1) {
+      max_acc(sn[t - 1][1], mn[1]);
+      asm volatile("" : "+v"(mn[1]));
+    }
+    if (2 * t + 1 < 13) half(20 + 2 * t);
+    if (t + 2 < 8) kop[t & 1] = ld_op_lds_at(kl, t + 2);
+    if ((t & 1) && t < 6) cp.issue(3 + (t >> 1));   // parts 3, 4, 5
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Score tile without restore (tile 0 in the prologue).
@@ -373,9 +426,8 @@ __device__ __forceinline__ void mask_tile(v4f (&sc)[8][2], int g, int kval) {
       if (16 * t + i >= kr) sc[t][0][i] = sc[t][1][i] = kNegBig;
 }
 
-// Integer running max, rescale factor and ExpCast codes for one tile.
-__device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma, SoftState& st, float (&alpha)[2],
-                                             v8i (&P)[2]) {
+// Integer running max and ExpCast codes of the first tile.
+__device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma, SoftState& st, v8i (&P)[2]) {
   const float s8 = cast_scale(sigma);
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
@@ -384,7 +436,6 @@ __device__ __forceinline__ void softmax_tile(const v4f (&sc)[8][2], float sigma,
     for (int t = 1; t < 8; ++t) mx = fmaxf(mx, max4(sc[t][qi]));
     mx = max_over_rows(mx);
     const float mn = fmaxf(st.M[qi], ceilf(mx * sigma));
-    alpha[qi] = st.M[qi] == kNegBig ? 0.0f : ldexpf(1.0f, static_cast<int>(fmaxf(st.M[qi] - mn, -160.0f)));
     st.M[qi] = mn;
     st.cq[qi] = cast_const(mn);
     const float c = st.cq[qi];
@@ -412,6 +463,9 @@ struct TileAcc {
   float rr[4][2];  // deferred restore weights: lane group g, slot j holds the
                    // row sum of tile 16G+4g+j of the current group G
   SoftState st;
+  v4f sh[8][2];    // raw scores of the next tile (cast in the next step)
+  float mh[2];     // their per-lane partial maxima
+  float sig;       // their sigma (log2-domain score scale)
 };
 
 // The copies of one step: K(tk) with its scale into kfree, V(tv) into vfree,
@@ -538,89 +592,56 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane16, 
 }
 
 // One tile step kb (J = kb mod 4): the interleaved MFMA phase (scores of
-// tile kb+1 with K in kcur, P.V and row sums of tile kb with V in vcur),
-// the step barrier, the maximum check per query sub-tile (codes recomputed
-// from the kept scores where the tile raised the maximum, and for ragged
-// tiles), tile kb's row sum into l and into the deferred restore weights,
-// and the rescale of O, l and the weights of a sub-tile whose maximum rose
-// (MXFP4: only when the anchor moves).  After the last tile of a group of
-// 16 the group's restore runs.  Copies run three steps ahead: this step
-// copies K(kb+4) into kfree, V(kb+3) into vfree and restore-operand row
-// kb+3 (distinct LDS arrays, so the copies overlap the reads of this step
-// and the next two), as its last vector-memory instructions (see
-// step_barrier).  Everything after the barrier works in registers or on a
-// restore-operand group copied at least three steps before and not
-// refilled for another thirteen, so it needs no barrier of its own.  Tile
-// indices past the
-// last tile are clamped to it and a score tile past the end is masked out
-// entirely, which leaves the state unchanged (alpha = 1, codes 0): every
-// step runs the same code.
+// tile kb+2 with K in kcur, P.V and row sums of tile kb with V in vcur,
+// codes of tile kb+1 against the maximum after it), the step barrier, the
+// masking of a ragged score tile, tile kb's row sum into l and into the
+// deferred restore weights, and the rescale of O, l and the weights of a
+// query sub-tile whose maximum tile kb+1 raised (MXFP4: only when the
+// anchor moves).  After the last tile of a group of 16 the group's restore
+// runs.  Copies run ahead: this step copies K(kb+5) into kfree, V(kb+3) into
+// vfree and restore-operand row kb+3 (distinct LDS arrays, so the copies
+// overlap the reads of this step and the next two), as its last
+// vector-memory instructions (see step_barrier).  Everything after the
+// barrier works in registers or on a restore-operand group copied at least
+// three steps before and not refilled for another thirteen, so it needs no
+// barrier of its own.  Tile indices past the last tile are clamped to it
+// and a score tile past the end is masked out entirely, which leaves the
+// state unchanged (no rise, codes 0): every step runs the same code.
 template <int VF, int J>
 __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
                                           const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2], TileAcc& acc) {
-  const int nblk = c.nblk, last = nblk - 1, lane = c.lane, g = c.g;
-  const float ks_next = *reinterpret_cast<const float*>(kcur + kTileBytes);
-  const StepCopies<VF> cp(c, kb + kStages < last ? kb + kStages : last, kb + kStages - 1 < last ? kb + kStages - 1 : last,
-                      kb + kStages - 1, kfree, vfree);
+  const int nblk = c.nblk, last = nblk - 1, g = c.g;
+  const StepCopies<VF> cp(c, kb + kStages + 1 < last ? kb + kStages + 1 : last,
+                          kb + kStages - 1 < last ? kb + kStages - 1 : last, kb + kStages - 1, kfree, vfree);
   static_assert(2 * kDmaPerTile + 2 == 6, "six copy parts, one per sub-tile");
-  const float sigma = ((c.sqs * ks_next) * c.sm_scale) * kLog2e;
-  const float s8 = cast_scale(sigma);
   v8i Pn[2];
-  float alpha[2], r[2];
-  bool resc[2] = {false, false};
+  float d[2], r[2], ks_new;
   {
-    v4f sc[8][2];
-    float mx[2];
-    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, s8, acc.st.cq, sc, Pn, mx, acc.O, r, acc.st.se, cp);
-    // the step's LDS reads and copies are all issued: the rest of the step
-    // works in registers (and on restore operands copied long before), so
-    // a wave that recasts or restores runs on while the others start the
-    // next step
+    v4f sn[8][2];
+    float mn[2];
+    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, acc.sig, acc.st, d, acc.sh, acc.mh, sn, Pn, mn, acc.O, r, cp);
+    // K(kb+2)'s scale (replicated per lane after the tile), read before the
+    // barrier: the next step refills this buffer.  Wave-uniform, so it is
+    // kept in a scalar register.
+    ks_new = __int_as_float(__builtin_amdgcn_readfirstlane(
+        *reinterpret_cast<const int*>(kcur + kTileBytes + (c.lane16 >> 2))));
     step_barrier<VF>();
-    const bool ragged = kb + 2 >= nblk;
-    // Did any row's maximum rise?  ceil(fl(m*sigma)) > M for an integer M
-    // exactly when fl(m*sigma) > M, and fl(m*sigma) is monotone in m, so
-    // each lane's partial maximum decides without the cross-row combine.
-    // Decided per query sub-tile: only a sub-tile whose maximum rose is
-    // recast (and rescaled).
-    bool ch[2];
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi) ch[qi] = ragged || __any(mx[qi] * sigma > acc.st.M[qi]);
-    if (__builtin_expect(ch[0] || ch[1], 0)) {
-      if (ragged) {
-        mask_tile(sc, g, kb + 2 == nblk ? c.kval_last : 0);
-#pragma unroll
-        for (int qi = 0; qi < 2; ++qi) {
-          mx[qi] = max4(sc[0][qi]);
-#pragma unroll
-          for (int t = 1; t < 8; ++t) mx[qi] = max_acc4(mx[qi], sc[t][qi]);
-        }
-      }
+    if (__builtin_expect(kb + 3 >= nblk, 0)) {
+      // tile kb+2 is the last tile (keys past S masked) or past it (all masked)
+      mask_tile(sn, g, kb + 2 == last ? c.kval_last : 0);
 #pragma unroll
       for (int qi = 0; qi < 2; ++qi) {
-        if (!ch[qi]) continue;
-        const float mn = fmaxf(acc.st.M[qi], ceilf(max_over_rows(mx[qi]) * sigma));
-        if (VF == 0) {
-          // codes and accumulators against M: rescale by 2^(M - M')
-          alpha[qi] = ldexpf(1.0f, static_cast<int>(fmaxf(acc.st.M[qi] - mn, -160.0f)));
-        } else {
-          // the anchor scale of the new codes, 127 + (M' - A); past the span
-          // the anchor moves up to M' and the accumulators are rescaled by
-          // 2^(A - M')
-          const int e = static_cast<int>((acc.st.se >> (8 * qi)) & 0xFF) - 127 +
-                        static_cast<int>(fminf(mn - acc.st.M[qi], 2.0f * kAnchorSpan));
-          const bool far = e > kAnchorSpan;
-          alpha[qi] = far ? ldexpf(1.0f, -e) : 1.0f;
-          acc.st.se = (acc.st.se & ~(0xFF << (8 * qi))) | ((far ? 127 : 127 + e) << (8 * qi));
-        }
-        resc[qi] = __any(alpha[qi] != 1.0f);
-        acc.st.M[qi] = mn;
-        acc.st.cq[qi] = cast_const(mn);
+        mn[qi] = max4(sn[0][qi]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) Pn[qi][t] = static_cast<int>(expcast4(sc[t][qi], s8, acc.st.cq[qi]));
+        for (int t = 1; t < 8; ++t) mn[qi] = max_acc4(mn[qi], sn[t][qi]);
       }
     }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc.sh[t][0] = sn[t][0], acc.sh[t][1] = sn[t][1];
+    acc.mh[0] = mn[0];
+    acc.mh[1] = mn[1];
   }
+  acc.sig = ((c.sqs * ks_new) * c.sm_scale) * kLog2e;
   // tile kb's row sum: into l, and restore weight (tile kb%16 of its group)
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) acc.st.l[qi] += r[qi];
@@ -628,14 +649,33 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
     acc.rr[J][0] = r[0];
     acc.rr[J][1] = r[1];
   }
+  // the maximum rose by d from tile kb to tile kb+1
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
-    if (__builtin_expect(resc[qi], 0)) {
-      acc.st.l[qi] *= alpha[qi];
+    if (__builtin_expect(__any(d[qi] != 0.0f), 0)) {
+      float alpha;
+      bool resc = true;
+      if (VF == 0) {
+        // codes and accumulators against M: rescale by 2^-d
+        alpha = ldexpf(1.0f, -static_cast<int>(fminf(d[qi], 160.0f)));
+      } else {
+        // the anchor scale of the next codes, 127 + (M' - A); past the span
+        // the anchor moves up to M' and the accumulators are rescaled by
+        // 2^(A - M')
+        const int e = static_cast<int>((acc.st.se >> (8 * qi)) & 0xFF) - 127 +
+                      static_cast<int>(fminf(d[qi], 2.0f * kAnchorSpan));
+        const bool far = e > kAnchorSpan;
+        alpha = far ? ldexpf(1.0f, -e) : 1.0f;
+        acc.st.se = (acc.st.se & ~(0xFF << (8 * qi))) | ((far ? 127 : 127 + e) << (8 * qi));
+        resc = __any(far);
+      }
+      if (resc) {
+        acc.st.l[qi] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc.O[dt][qi] *= alpha[qi];
+        for (int dt = 0; dt < 8; ++dt) acc.O[dt][qi] *= alpha;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc.rr[j][qi] *= alpha[qi];
+        for (int j = 0; j < 4; ++j) acc.rr[j][qi] *= alpha;
+      }
     }
   }
   acc.P[0] = Pn[0];
@@ -740,7 +780,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   for (int j = 0; j < 4; ++j) acc.rr[j][0] = acc.rr[j][1] = 0.0f;
 
   // ---- prologue: K(0..3) with scales, V(0..2) and restore-operand rows
-  // 0..2 into LDS; scores and codes of tile 0 ----
+  // 0..2 into LDS; scores and codes of tile 0, scores of tile 1; then K(4)
+  // into the slot of K(0) ----
   const int last = nblk - 1;
 #pragma unroll
   for (int j = 0; j + 1 < kStages; ++j)
@@ -756,26 +797,41 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
     v4f sc[8][2];
     score_tile(kbuf0, lane, qop, sc);
     if (nblk == 1 && c.kval_last < kBlock) mask_tile(sc, g, c.kval_last);
-    float alpha[2];
-    softmax_tile(sc, ((sqs * c.ks[0]) * a.sm_scale) * kLog2e, acc.st, alpha, acc.P);
+    softmax_tile(sc, ((sqs * c.ks[0]) * a.sm_scale) * kLog2e, acc.st, acc.P);
   }
-  __syncthreads();   // kring[0] (K(0)) is refilled in the first step
+  // scores of tile 1 (a copy of tile 0, masked out, when there is none):
+  // their codes are cast in the first step
+  score_tile(kbuf1, lane, qop, acc.sh);
+  if (nblk <= 2) mask_tile(acc.sh, g, nblk == 2 ? c.kval_last : 0);
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    acc.mh[qi] = max4(acc.sh[0][qi]);
+#pragma unroll
+    for (int t = 1; t < 8; ++t) acc.mh[qi] = max_acc4(acc.mh[qi], acc.sh[t][qi]);
+  }
+  acc.sig = ((sqs * c.ks[last < 1 ? last : 1]) * a.sm_scale) * kLog2e;
+  __syncthreads();   // kring[0] and kring[1] are refilled from here on
+  {
+    const StepCopies<VF> cp(c, kStages < last ? kStages : last, 0, 0, kring[0], vring[0]);
+#pragma unroll
+    for (int p = 0; p <= kDmaPerTile; ++p) cp.issue(p);
+  }
 
-  // Step kb reads K(kb+1) from kring[(kb+1)%S] and V(kb) from vring[kb%S]
-  // (S = kStages), and refills kring[kb%S] with K(kb+S) and
+  // Step kb reads K(kb+2) from kring[(kb+2)%S] and V(kb) from vring[kb%S]
+  // (S = kStages), and refills kring[(kb+1)%S] with K(kb+S+1) and
   // vring[(kb+S-1)%S] with V(kb+S-1).  The loop is unrolled S times so that
   // every buffer is a fixed array.
   static_assert(kStages == 4, "tile_step<J> takes J = kb mod 4");
   int kb = 0;
   for (; kb + kStages <= nblk; kb += kStages) {
-    tile_step<VF, 0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, acc);
-    tile_step<VF, 1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, acc);
-    tile_step<VF, 2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, acc);
-    tile_step<VF, 3>(c, kb + 3, kbuf0, kbuf3, vbuf3, vbuf2, qop, acc);
+    tile_step<VF, 0>(c, kb, kbuf2, kbuf1, vbuf0, vbuf3, qop, acc);
+    tile_step<VF, 1>(c, kb + 1, kbuf3, kbuf2, vbuf1, vbuf0, qop, acc);
+    tile_step<VF, 2>(c, kb + 2, kbuf0, kbuf3, vbuf2, vbuf1, qop, acc);
+    tile_step<VF, 3>(c, kb + 3, kbuf1, kbuf0, vbuf3, vbuf2, qop, acc);
   }
-  if (kb < nblk) tile_step<VF, 0>(c, kb, kbuf1, kbuf0, vbuf0, vbuf3, qop, acc);
-  if (kb + 1 < nblk) tile_step<VF, 1>(c, kb + 1, kbuf2, kbuf1, vbuf1, vbuf0, qop, acc);
-  if (kb + 2 < nblk) tile_step<VF, 2>(c, kb + 2, kbuf3, kbuf2, vbuf2, vbuf1, qop, acc);
+  if (kb < nblk) tile_step<VF, 0>(c, kb, kbuf2, kbuf1, vbuf0, vbuf3, qop, acc);
+  if (kb + 1 < nblk) tile_step<VF, 1>(c, kb + 1, kbuf3, kbuf2, vbuf1, vbuf0, qop, acc);
+  if (kb + 2 < nblk) tile_step<VF, 2>(c, kb + 2, kbuf0, kbuf3, vbuf2, vbuf1, qop, acc);
   // drain the copies still in flight before the workgroup retires
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
