@@ -181,11 +181,14 @@ __device__ __forceinline__ uint32_t pcast2(float x0, float x1, float a, float b,
   return static_cast<uint32_t>(h ? __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, static_cast<int>(w), true)
                                  : __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, static_cast<int>(w), false));
 }
-// one score into byte i of w (keys with their own scale: the repair tiles)
-__device__ __forceinline__ uint32_t pcast1(float x, float a, float b, int i, uint32_t w) {
-  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(x, a, b)), 0.0f,
-                                                                          0, false)) & 0xFFu;
-  return (w & ~(0xFFu << (8 * i))) | (c << (8 * i));
+// two scores with their own scales and constants (the repair tiles, whose
+// keys each carry a scale) into bytes 2h, 2h+1 of w
+__device__ __forceinline__ uint32_t pcast2v(float x0, float x1, const float (&a)[2], const float (&b)[2], int h,
+                                            uint32_t w) {
+  const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, a[0], b[0]));
+  const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, a[1], b[1]));
+  return static_cast<uint32_t>(h ? __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, static_cast<int>(w), true)
+                                 : __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, static_cast<int>(w), false));
 }
 // cast constant that sends a score to code 0 (masked repair slots)
 constexpr float kCastOff = -200.0f;
@@ -299,8 +302,8 @@ template <int VF, typename Copies>
 __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* vt, int lane, const v8i (&qop)[2],
                                            const v8i (&P)[2], float sig, SoftState& st, float (&d)[2],
                                            const v4f (&sh)[8][2], const float (&mh)[2], v4f (&sn)[8][2],
-                                           v8i (&Pn)[2], float (&mn)[2], v4f (&O)[8][2], float (&r)[2],
-                                           const Copies& cp) {
+                                           v8i (&Pn)[2], float (&mn)[2], v4f (&O)[8][2], float (&rr)[2],
+                                           bool rsel, const Copies& cp) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const v8i ones = {kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4, kOnes4};
   const uint8_t* kl = ktile + lane;   // lane = the lane's byte offset (16 * lane id)
@@ -378,8 +381,6 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
   half(17);
   half(18);
   __builtin_amdgcn_sched_barrier(0);
-  r[0] = r0[0];
-  r[1] = r1[0];
   // ---- second half: 16 slots ----
   mn[0] = mn[1] = kNegBig;
 #pragma unroll
@@ -399,6 +400,17 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
       asm volatile("" : "+v"(mn[1]));
     }
     if (2 * t + 1 < 13) half(20 + 2 * t);
+    if (t == 0) {
+      // tile kb's row sums (ready two MFMAs after the second one): into l,
+      // and into restore-weight slot rr where this lane group holds it
+      st.l[0] += r0[0];
+      st.l[1] += r1[0];
+      if (rsel) {
+        rr[0] = r0[0];
+        rr[1] = r1[0];
+      }
+      asm volatile("" : "+v"(st.l[0]), "+v"(st.l[1]), "+v"(rr[0]), "+v"(rr[1]));
+    }
     if (t + 2 < 8) kop[t & 1] = ld_op_lds_at(kl, t + 2);
     if ((t & 1) && t < 6) cp.issue(3 + (t >> 1));   // parts 3, 4, 5
     __builtin_amdgcn_sched_barrier(0);
@@ -615,11 +627,14 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
                           kb + kStages - 1 < last ? kb + kStages - 1 : last, kb + kStages - 1, kfree, vfree);
   static_assert(2 * kDmaPerTile + 2 == 6, "six copy parts, one per sub-tile");
   v8i Pn[2];
-  float d[2], r[2], ks_new;
+  float d[2], ks_new;
   {
     v4f sn[8][2];
     float mn[2];
-    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, acc.sig, acc.st, d, acc.sh, acc.mh, sn, Pn, mn, acc.O, r, cp);
+    // tile kb's row sum goes to l and to the restore weight of tile kb%16
+    // of its group, held by lane group (kb/4)%4 in slot J
+    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, acc.sig, acc.st, d, acc.sh, acc.mh, sn, Pn, mn, acc.O,
+                   acc.rr[J], (c.lane16 >> 8) == ((kb >> 2) & 3), cp);
     // K(kb+2)'s scale (replicated per lane after the tile), read before the
     // barrier: the next step refills this buffer.  Wave-uniform, so it is
     // kept in a scalar register.
@@ -642,13 +657,6 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
     acc.mh[1] = mn[1];
   }
   acc.sig = ((c.sqs * ks_new) * c.sm_scale) * kLog2e;
-  // tile kb's row sum: into l, and restore weight (tile kb%16 of its group)
-#pragma unroll
-  for (int qi = 0; qi < 2; ++qi) acc.st.l[qi] += r[qi];
-  if ((c.lane16 >> 8) == ((kb >> 2) & 3)) {   // lane group g = lane / 16
-    acc.rr[J][0] = r[0];
-    acc.rr[J][1] = r[1];
-  }
   // the maximum rose by d from tile kb to tile kb+1
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
@@ -869,12 +877,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
         const v4f s0 = mfma_fp8(kop, qop[0], zero);
         const v4f s1 = mfma_fp8(kop, qop[1], zero);
         uint32_t w0 = 0, w1 = 0;
+        // slots past the repair set cast to code 0
+#ifndef VC_ABLATION_EXP_CAST
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = rt * kBlock + 16 * t + 4 * g + i;
           const float sig = ((sqs * rks[j]) * a.sm_scale) * kLog2e;
-          // slots past the repair set cast to code 0
-#ifndef VC_ABLATION_EXP_CAST
           // (the ExpCast constants written out: as calls of cast_scale and
           // cast_const the register allocation of the whole kernel spills)
           const float s8j = j < nrep ? 8.0f * sig : 0.0f;
@@ -882,14 +890,24 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
           const float c1 = j < nrep ? 120.0f - 8.0f * st.M[1] : -1.0f;
           w0 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[i], s8j, c0), i, w0);
           w1 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[i], s8j, c1), i, w1);
-#else
-          const float s8j = j < nrep ? cast_scale(sig) : 0.0f;
-          const float c0 = j < nrep ? cast_const(st.M[0]) : kCastOff;
-          const float c1 = j < nrep ? cast_const(st.M[1]) : kCastOff;
-          w0 = pcast1(s0[i], s8j, c0, i, w0);
-          w1 = pcast1(s1[i], s8j, c1, i, w1);
-#endif
         }
+#else
+        // pairs of keys: two exponentials and one packed conversion each
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          float sa[2], b0[2], b1[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int j = rt * kBlock + 16 * t + 4 * g + i + k;
+            const float sig = ((sqs * rks[j]) * a.sm_scale) * kLog2e;
+            sa[k] = j < nrep ? cast_scale(sig) : 0.0f;
+            b0[k] = j < nrep ? cast_const(st.M[0]) : kCastOff;
+            b1[k] = j < nrep ? cast_const(st.M[1]) : kCastOff;
+          }
+          w0 = pcast2v(s0[i], s0[i + 1], sa, b0, i >> 1, w0);
+          w1 = pcast2v(s1[i], s1[i + 1], sa, b1, i >> 1, w1);
+        }
+#endif
         Pr[0][t] = static_cast<int>(w0);
         Pr[1][t] = static_cast<int>(w1);
       }
