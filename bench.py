@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--ablation-exp", action="store_true",
                     help="also time the attention kernel of libvc_ablation_exp.so (FP32 exponential + E4M3 cast "
                          "instead of ExpCast) on the same prepared workspace")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the full call once into a HIP graph (the library allocates, clears and "
+                         "synchronises nothing, so it captures as is) and time its replays")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_fwd_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -226,6 +229,8 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    if args.graph:
+        res["graph"] = graph_replay(w, vd, qd, kd, opts, ws, out, args.steps)
     if args.ablation_exp:
         main_lib = vc.lib_path
         vc.use_library(vc.ablation_exp_lib_path)
@@ -266,6 +271,41 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def graph_replay(w, vd, qd, kd, opts, ws, out, steps: int) -> dict:
+    """The full call recorded once into a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: the launch gaps between the ~15 kernels of a short call go away.
+    The replay's output is compared bit for bit with the eager call's."""
+    import torch
+    import bit_attention_video_vc_amd as vc
+    eager = out.clone()
+
+    def full_call(s):
+        vc.vc_prepare_v(vd, opts, ws, s)
+        vc.vc_prepare_qk(qd, kd, opts, ws, s)
+        vc.vc_attention_fwd(out, opts, ws, 0.0, s)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        full_call(side)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        full_call(torch.cuda.current_stream())
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    log(f"graph replay: {ms:.3f} ms per full call")
+    return {"what": "the same full call captured once into a HIP graph and replayed",
+            "ms_per_step": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2),
+            "identical_to_eager": bool(torch.equal(out, eager))}
 
 
 if __name__ == "__main__":
