@@ -326,6 +326,37 @@ def test_zero_value_head_and_zero_blocks():
                          exact_tol=TOL_EXACT_ZERO_MEAN_V)
 
 
+@pytest.mark.parametrize("v_format", ["e4m3", "mxfp4"])
+@pytest.mark.parametrize("smooth", [False, True])
+def test_steep_maximum_rises(v_format, smooth):
+    """Spike keys along one direction c: even queries (+4c) see their running
+    maximum rise by ~30, ~100 and ~104 octaves at three tiles (the last one
+    ragged), odd queries (-4c) see the spikes far below their maximum.  So
+    within one wave some lanes rescale and others do not; the 100-octave rise
+    moves the MXFP4 anchor (rises past 64 octaves) and takes the E4M3 rescale
+    to 2^-100.  With smooth=False the key order is the original one, so the
+    rises land at the tiles chosen here."""
+    S, H = 1000, 2
+    g = torch.Generator().manual_seed(77)
+    c = torch.randn(128, generator=g)
+    c = c / c.norm()
+    sign = torch.where(torch.arange(S) % 2 == 0, 1.0, -1.0)
+    q = torch.randn(1, S, H, 128, generator=g) + 4.0 * sign[None, :, None, None] * c
+    k = torch.randn(1, S, H, 128, generator=g)
+    v = torch.randn(1, S, H, 128, generator=g) + 2 * torch.randn(1, 1, H, 128, generator=g)
+    octave = 4.0 * float(O.DEFAULT_SM_SCALE) * float(np.log2(np.e))     # log2 units per unit of lam
+    for pos, octaves in ((130, 30.0), (400, 100.0), (990, 104.0)):
+        k[0, pos] = (octaves / octave) * c
+    # The even rows' attention collapses onto the two last spikes (weights
+    # 16:1), so their output is essentially one token's V and carries that
+    # token's full quantisation error, with no averaging: up to ~9% for the
+    # 4-bit residual.  The oracle parity (5e-3) is the gate here; the exact
+    # envelope only catches gross errors.
+    check_against_oracle(q.to(torch.bfloat16).cuda(), k.to(torch.bfloat16).cuda(), v.to(torch.bfloat16).cuda(),
+                         smooth=smooth, kc=4, iters=2, name=f"steep rises {v_format} smooth={smooth}",
+                         exact_tol=TOL_EXACT_ZERO_MEAN_V if v_format == "e4m3" else 0.15, v_format=v_format)
+
+
 # ---- 4-bit residual (MXFP4) ---------------------------------------------------
 # The 4-bit residual is coarser than E4M3 (the oracle itself sits up to ~4% from
 # exact attention on config 2), so its runs get the gross-error envelope.
