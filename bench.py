@@ -118,7 +118,7 @@ def cpu_baseline(w, q, k, v, rows_n: int) -> dict:
 def main() -> int:
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(attention heads would shard across GPUs with no exchange; that path is not built)", file=sys.stderr)
         return 2
     import torch
