@@ -34,12 +34,13 @@ def _whole_call_properties(run, name):
     say(f"{name}: all {BH} heads: perm/assign properties and finite output ok")
 
 
-def _run(cid, heads, exact_tol, **kw):
+def _run(cid, heads, exact_tol, v_format="e4m3", **kw):
     w = synth.workload(cid, **kw)
     q, k, v = (t.cuda() for t in synth.generate(w, "cpu"))
     rows = synth.sample_rows(w.S, ROWS_PER_HEAD).numpy()
     run = check_against_oracle(q, k, v, kc=w.k, iters=w.iters, beta=w.repair_budget, rows=rows, heads=heads,
-                               name=f"{w.name} B={w.B} H={w.H} S={w.S}", exact_tol=exact_tol)
+                               name=f"{w.name} B={w.B} H={w.H} S={w.S} {v_format}", exact_tol=exact_tol,
+                               v_format=v_format)
     _whole_call_properties(run, w.name)
 
 
@@ -61,3 +62,9 @@ def test_full_wan_720p():
 
 def test_full_batched_repair():
     _run(5, heads=[(0, 0), (1, 23)], exact_tol=0.10)
+
+
+def test_full_minimax_h14_mxfp4():
+    # the 4-bit residual at the benchmark's sequence length (its own kernel
+    # instance: FP4 P.V operands and the anchor maximum)
+    _run(4, heads=[(0, 0), (0, 13)], exact_tol=TOL_EXACT, v_format="mxfp4", H=14)
