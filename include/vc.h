@@ -31,7 +31,10 @@
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  The library enqueues kernels and never synchronises; kernel
- * faults surface at the caller's next synchronisation.
+ * faults surface at the caller's next synchronisation.  The three calls
+ * enqueue kernel launches only (no allocation, memset or copy, no host read
+ * of device memory), so a caller with fixed shapes may record them into a
+ * HIP graph and replay it; the graph keeps the buffers it was recorded with.
  *
  * Errors: every call validates its host-side arguments before it enqueues
  * any work; on failure it returns a non-zero vc_status, enqueues nothing,
