@@ -175,7 +175,6 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
   if (ACCUM)
     for (int i = tid; i < k * kSumPitch; i += 256) sums[i] = 0;
   if (tid < kMaxK) cnt[tid] = 0;
-  constexpr int nct = NCT;                     // 16-centroid tiles: ceil(k/16)
   // centroid operands (prepared with the centroids) and norms
   v8bf ca[NCT][4];
   const uint8_t* op = cent_op + static_cast<int64_t>(bh) * kCentOpBytes;
