@@ -204,8 +204,10 @@ __device__ __forceinline__ float max4(const v4f& s) { return fmaxf(fmaxf(s[0], s
 // running max over 4 more values as two 3-input maxima
 __device__ __forceinline__ float max_acc4(float m, const v4f& s) { return fmaxf(fmaxf(fmaxf(fmaxf(m, s[0]), s[1]), s[2]), s[3]); }
 
-// Large finite stand-in for -infinity (the kernel is built without NaN/IEEE
-// canonicalisation, so it avoids infinities altogether).
+// Large finite stand-in for -infinity for masked scores (the kernel is built
+// without NaN/IEEE canonicalisation and never forms a NaN; the maximum of a
+// fully masked tile times sigma may round to -infinity, which the comparisons
+// and fmaxf against a finite M handle).
 constexpr float kNegBig = -3.0e38f;
 
 // Per-wave online-softmax state for two 16-query sub-tiles.
@@ -289,8 +291,9 @@ __device__ __forceinline__ void new_max(SoftState& st, int qi, float mh, float s
 // with per-lane partial maxima mh), takes the maximum after tile kb+1 and
 // starts the ExpCast of those scores against it into Pn.  Then the score
 // MFMAs of tile kb+2 (K in LDS, both query sub-tiles) into sn; under them
-// the rest of the cast and the per-lane running max (mn) of the new scores
-// (sub-tile 7's max is left to the next step).  A tile's maximum is thus
+// the rest of the cast, the per-lane running max (mn) of the new scores
+// (sub-tile 7's max is left to the next step) and tile kb's row sums into l
+// and into its restore-weight slot rr.  A tile's maximum is thus
 // known before its codes are cast, so no cast is ever redone; and the held
 // scores are cast before the new ones arrive, so the two sets share
 // registers.  Each MFMA is followed by a few of these instructions (a score
