@@ -606,13 +606,13 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane16, 
       : "memory");
 }
 
-// One tile step kb (J = kb mod 4): the interleaved MFMA phase (scores of
-// tile kb+2 with K in kcur, P.V and row sums of tile kb with V in vcur,
-// codes of tile kb+1 against the maximum after it), the step barrier, the
-// masking of a ragged score tile, tile kb's row sum into l and into the
-// deferred restore weights, and the rescale of O, l and the weights of a
-// query sub-tile whose maximum tile kb+1 raised (MXFP4: only when the
-// anchor moves).  After the last tile of a group of 16 the group's restore
+// One tile step kb (J = kb mod 4): the MFMA phase (P.V and row sums of
+// tile kb with V in vcur -- the row sums going into l and the deferred
+// restore weights --, codes of tile kb+1 against the maximum after it,
+// scores of tile kb+2 with K in kcur), the step barrier, the masking of a
+// ragged score tile, and the rescale of O, l and the weights of a query
+// sub-tile whose maximum tile kb+1 raised (MXFP4: only when the anchor
+// moves).  After the last tile of a group of 16 the group's restore
 // runs.  Copies run ahead: this step copies K(kb+5) into kfree, V(kb+3) into
 // vfree and restore-operand row kb+3 (distinct LDS arrays, so the copies
 // overlap the reads of this step and the next two), as its last
