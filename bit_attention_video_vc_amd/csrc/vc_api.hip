@@ -32,6 +32,7 @@ vc_status ok() {
 
 constexpr int64_t kMaxS = 1 << 24;
 constexpr int64_t kMaxBH = 1 << 20;
+constexpr int kMaxGridYZ = 65535;
 
 vc_status check_desc(const vc_desc* d, const char* name) {
   if (!d) return fail(VC_ERR_ARG, "%s: descriptor is NULL", name);
@@ -40,6 +41,9 @@ vc_status check_desc(const vc_desc* d, const char* name) {
   if (d->dtype != VC_F16 && d->dtype != VC_BF16) return fail(VC_ERR_UNSUPPORTED, "%s: dtype must be VC_F16 or VC_BF16", name);
   if (d->S > kMaxS) return fail(VC_ERR_UNSUPPORTED, "%s: S = %d exceeds %lld", name, d->S, (long long)kMaxS);
   if (static_cast<int64_t>(d->B) * d->H > kMaxBH) return fail(VC_ERR_UNSUPPORTED, "%s: B*H exceeds %lld", name, (long long)kMaxBH);
+  // heads and batches index the second and third grid dimensions (<= 65535 each)
+  if (d->H > kMaxGridYZ || d->B > kMaxGridYZ)
+    return fail(VC_ERR_UNSUPPORTED, "%s: B and H must each be <= %d", name, kMaxGridYZ);
   if (d->sB < 0 || d->sS < 0 || d->sH < 0) return fail(VC_ERR_ARG, "%s: negative stride", name);
   if ((d->sB % 8) || (d->sS % 8) || (d->sH % 8)) return fail(VC_ERR_ARG, "%s: strides must be multiples of 8 elements (16 bytes)", name);
   return VC_OK;

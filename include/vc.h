@@ -68,7 +68,9 @@ typedef enum { VC_F16 = 0, VC_BF16 = 1 } vc_dtype;
 /* A [B,S,H,D] tensor view.  Element (b,s,h,d) is at
  * base + b*sB + s*sS + h*sH + d (strides in elements; D is contiguous).
  * D must be 128.  An [S,H,128] tensor is the view with B=1.
- * Base pointers and strides*2 bytes must be 16-byte aligned. */
+ * Base pointers and strides*2 bytes must be 16-byte aligned.  Supported
+ * sizes: S <= 2^24, B*H <= 2^20, B and H each <= 65535 (VC_ERR_UNSUPPORTED
+ * otherwise). */
 typedef struct {
   int32_t B, S, H, D;
   int32_t dtype;           /* vc_dtype */

@@ -103,6 +103,7 @@ def test_layout_regions_are_disjoint_and_sized():
     (dict(H=0), vc.VC_ERR_ARG),
     (dict(dtype=7), vc.VC_ERR_UNSUPPORTED),
     (dict(sS=129), vc.VC_ERR_ARG),
+    (dict(H=70000), vc.VC_ERR_UNSUPPORTED),          # past the launch grid's second dimension
 ])
 def test_layout_rejects_bad_descriptors(mut, code):
     d = _desc(**mut)
