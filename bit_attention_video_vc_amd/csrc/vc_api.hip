@@ -288,7 +288,9 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   if (!(sm >= 0.0f) || std::isinf(sm)) return fail(VC_ERR_ARG, "sm_scale must be finite and >= 0");
   if (sm == 0.0f) sm = static_cast<float>(1.0 / std::sqrt(128.0));
   const int64_t total = static_cast<int64_t>(p.B) * p.H * ((p.nblk + 1) / 2);   // one workgroup per query-block pair
-  if (total > (int64_t)1 << 31) return fail(VC_ERR_UNSUPPORTED, "too many query blocks");
+  if (total > vc::kMaxAttnWorkgroups)
+    return fail(VC_ERR_UNSUPPORTED, "B*H*ceil(S/256) = %lld exceeds %lld attention workgroups", (long long)total,
+                (long long)vc::kMaxAttnWorkgroups);
   if ((s = check_device()) != VC_OK) return s;
   const vc::WsPtrs w = ws_ptrs(p, const_cast<void*>(ws));
   vc::AttnArgs a;

@@ -53,7 +53,8 @@
 namespace vc {
 
 constexpr int kAttnWaves = 8;
-constexpr int kAttnThreads = 64 * kAttnWaves;   // 512: two 128-query blocks per workgroup
+constexpr int kAttnThreads = kAttnThreadsPerWg;   // two 128-query blocks per workgroup
+static_assert(kAttnThreads == 64 * kAttnWaves, "one workgroup is kAttnWaves waves");
 constexpr float kLog2e = 1.44269504088896340736f;
 // Four E4M3 1.0 codes: the ones operand of the row-sum MFMA.
 constexpr int kOnes4 = 0x38383838;

@@ -8,6 +8,11 @@
 
 namespace vc {
 
+// Threads per attention workgroup (8 waves, two 128-query blocks).  A launch
+// holds at most 2^32 - 1 threads, so at most kMaxAttnWorkgroups workgroups.
+constexpr int kAttnThreadsPerWg = 512;
+constexpr int64_t kMaxAttnWorkgroups = 0xFFFFFFFFll / kAttnThreadsPerWg;
+
 // A [B,S,H,128] fp16/bf16 view (element strides; D contiguous).
 struct TensorArg {
   const void* p;

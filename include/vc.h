@@ -69,7 +69,8 @@ typedef enum { VC_F16 = 0, VC_BF16 = 1 } vc_dtype;
  * base + b*sB + s*sS + h*sH + d (strides in elements; D is contiguous).
  * D must be 128.  An [S,H,128] tensor is the view with B=1.
  * Base pointers and strides*2 bytes must be 16-byte aligned.  Supported
- * sizes: S <= 2^24, B*H <= 2^20, B and H each <= 65535 (VC_ERR_UNSUPPORTED
+ * sizes: S <= 2^24, B*H <= 2^20, B and H each <= 65535, and
+ * B*H*ceil(S/256) <= 2^23 - 1 (one attention launch; VC_ERR_UNSUPPORTED
  * otherwise). */
 typedef struct {
   int32_t B, S, H, D;

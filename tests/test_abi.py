@@ -189,6 +189,21 @@ def test_attention_fwd_validation_paths():
                                None) == vc.VC_ERR_WORKSPACE
 
 
+def test_attention_fwd_rejects_a_grid_past_the_launch_limit():
+    # within every per-dimension limit (B*H = 1048560 <= 2^20, S = 2^24), but
+    # B*H*ceil(S/256) workgroups of 512 threads exceed one launch's 2^32 - 1
+    # threads; rejected before any device call
+    d = _desc(B=16, S=1 << 24, H=65535)
+    o = vc.v_opts(True, 4, 1)
+    st, L = _layout(d, o)
+    assert st == vc.VC_OK
+    L_ = vc.lib()
+    a = vc.VcAttnOpts(0.0, 0)
+    assert L_.vc_attention_fwd(ctypes.byref(d), FAKE, ctypes.byref(o), ctypes.byref(a), FAKE, L.total,
+                               None) == vc.VC_ERR_UNSUPPORTED
+    assert "attention workgroups" in L_.vc_last_error().decode()
+
+
 def test_status_strings():
     L_ = vc.lib()
     assert L_.vc_status_string(vc.VC_OK) == b"VC_OK"
