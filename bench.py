@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--seq", type=int, default=None, help="override S")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="cap the oracle's BLAS threads (default: all the host gives it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling HBM byte counters) and exit")
     ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
@@ -81,9 +84,12 @@ def traffic_bytes(path: str, key: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, rows_n: int) -> dict:
+def cpu_baseline(w, q, k, v, rows_n: int, threads_cap: int | None = None) -> dict:
     """The oracle, as is, on one head: full prepare plus a sample of query rows."""
-    import numpy as np
+    if threads_cap is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads_cap):
+            return cpu_baseline(w, q, k, v, rows_n)
     from threadpoolctl import threadpool_info
 
     from oracle import vc_oracle as O
@@ -113,6 +119,21 @@ def cpu_baseline(w, q, k, v, rows_n: int) -> dict:
                    f"value = 4*S^2*D / (t_prepare + t_rows*S/{rows.size}) (extrapolated to the full head)"),
         "host_cpus": os.cpu_count(),
     }
+
+
+def prepare_report(w, prep_v_ms: float, prep_qk_ms: float) -> dict:
+    """Prepare calls (HIP events on the launch stream, average over the timed
+    steps) with their algorithmic HBM bytes: per input element, Q and K are
+    read once (2 B) and written as E4M3 (1 B); V is read in each of the T+1
+    k-means assignment passes, by the block-mean pass and by the quantise
+    pass (2 B each) and written once (1 B): 2T+7 bytes."""
+    n = w.B * w.H * w.S * w.D
+    v_bytes = (2 * w.iters + 7) * n
+    qk_bytes = 6 * n
+    return {"prepare_v_ms": round(prep_v_ms, 4), "prepare_qk_ms": round(prep_qk_ms, 4),
+            "prepare_v_algorithmic_GBps": round(v_bytes / (prep_v_ms * 1e-3) / 1e9, 1),
+            "prepare_qk_algorithmic_GBps": round(qk_bytes / (prep_qk_ms * 1e-3) / 1e9, 1),
+            "bytes_model": "V (2T+7) B/element, Q and K 3 B/element each"}
 
 
 def main() -> int:
@@ -163,27 +184,35 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        vc.vc_prepare_v(vd, opts, ws, stream)
-        vc.vc_prepare_qk(qd, kd, opts, ws, stream)
+        # events (on the launch stream): before prepare_v, after it, after
+        # prepare_qk, after the attention kernel
         if ev is not None:
             ev[0].record(stream)
-        vc.vc_attention_fwd(out, opts, ws, 0.0, stream)
+        vc.vc_prepare_v(vd, opts, ws, stream)
         if ev is not None:
             ev[1].record(stream)
+        vc.vc_prepare_qk(qd, kd, opts, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        vc.vc_attention_fwd(out, opts, ws, 0.0, stream)
+        if ev is not None:
+            ev[3].record(stream)
 
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
         log(f"warmup {i + 1}/{args.warmup} done")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    prep_v_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+    prep_qk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
     log(f"timed {args.steps} steps in {t_total:.3f} s")
 
     ms_per_step = 1e3 * t_total / args.steps
@@ -217,8 +246,13 @@ def main() -> int:
         },
         "pct_of_fp8_peak_full_call": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "kernel_only": {"tflops": round(attn_tflops, 2), "avg_ms": round(attn_avg_ms, 4),
+                        "median_ms": round(statistics.median(attn_ms), 4), "min_ms": round(min(attn_ms), 4),
                         "pct_of_fp8_peak": round(100 * attn_tflops / PEAK_FP8_TFLOPS, 2)},
         "prepare_ms_per_step": round(ms_per_step - attn_avg_ms, 3),
+        "prepare": prepare_report(w, prep_v_ms, prep_qk_ms),
+        "device": {"name": torch.cuda.get_device_name(),
+                   "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+                   "compute_units": torch.cuda.get_device_properties(0).multi_processor_count},
         "roofline": {
             "kernel": "k_vc_attn_fwd",
             "bound": "mfma",
@@ -268,7 +302,7 @@ def main() -> int:
         res["hold"] = {"seconds": round(t_hold, 2), "launches": n_hold, "avg_ms": round(1e3 * t_hold / n_hold, 3)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, args.cpu_threads)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -138,9 +138,32 @@ def desc_of(t: torch.Tensor) -> VcDesc:
     return VcDesc(B, S, H, D, dt, 0, t.stride(0), t.stride(1), t.stride(2))
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _device_of(**tensors: torch.Tensor) -> torch.device:
+    """The one GPU that every tensor is on; raises before any library call
+    otherwise (the kernels dereference these pointers on the current device)."""
+    dev = None
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            where = t.device if isinstance(t, torch.Tensor) else type(t).__name__
+            raise ValueError(f"{name} must be a GPU tensor (got {where})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    return dev
+
+
+def _ws_bytes(ws: torch.Tensor) -> int:
+    if not ws.is_contiguous():
+        raise ValueError("the workspace must be a contiguous tensor")
+    return ws.numel() * ws.element_size()
+
+
+def _stream(stream, dev: torch.device) -> ctypes.c_void_p:
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif isinstance(stream, torch.cuda.Stream) and stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
@@ -157,25 +180,31 @@ def alloc_workspace(v_like: torch.Tensor, opts: VcVOpts) -> torch.Tensor:
 
 
 def vc_prepare_v(v: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, stream=None) -> None:
-    d = desc_of(v)
-    _check(lib().vc_prepare_v(ctypes.byref(d), ctypes.c_void_p(v.data_ptr()), ctypes.byref(opts),
-                              ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)))
+    dev = _device_of(v=v, ws=ws)
+    d, nbytes = desc_of(v), _ws_bytes(ws)
+    with torch.cuda.device(dev):
+        _check(lib().vc_prepare_v(ctypes.byref(d), ctypes.c_void_p(v.data_ptr()), ctypes.byref(opts),
+                                  ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(stream, dev)))
 
 
 def vc_prepare_qk(q: torch.Tensor, k: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, stream=None) -> None:
-    dq, dk = desc_of(q), desc_of(k)
-    _check(lib().vc_prepare_qk(ctypes.byref(dq), ctypes.c_void_p(q.data_ptr()), ctypes.byref(dk),
-                               ctypes.c_void_p(k.data_ptr()), ctypes.byref(opts), ctypes.c_void_p(ws.data_ptr()),
-                               ws.numel() * ws.element_size(), _stream(stream)))
+    dev = _device_of(q=q, k=k, ws=ws)
+    dq, dk, nbytes = desc_of(q), desc_of(k), _ws_bytes(ws)
+    with torch.cuda.device(dev):
+        _check(lib().vc_prepare_qk(ctypes.byref(dq), ctypes.c_void_p(q.data_ptr()), ctypes.byref(dk),
+                                   ctypes.c_void_p(k.data_ptr()), ctypes.byref(opts), ctypes.c_void_p(ws.data_ptr()),
+                                   nbytes, _stream(stream, dev)))
 
 
 def vc_attention_fwd(out: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, sm_scale: float = 0.0,
                      stream=None) -> None:
-    d = desc_of(out)
+    dev = _device_of(out=out, ws=ws)
+    d, nbytes = desc_of(out), _ws_bytes(ws)
     a = VcAttnOpts(float(sm_scale), 0)
-    _check(lib().vc_attention_fwd(ctypes.byref(d), ctypes.c_void_p(out.data_ptr()), ctypes.byref(opts),
-                                  ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
-                                  _stream(stream)))
+    with torch.cuda.device(dev):
+        _check(lib().vc_attention_fwd(ctypes.byref(d), ctypes.c_void_p(out.data_ptr()), ctypes.byref(opts),
+                                      ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), nbytes,
+                                      _stream(stream, dev)))
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, smooth: bool = True, clusters: int = 32,
@@ -184,6 +213,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, smooth: bool
               stream=None) -> torch.Tensor:
     """Full call: prepare_v, prepare_qk and the fused forward; returns bf16 [B,S,H,128] (or [S,H,128])."""
     o = v_opts(smooth, clusters, iters, seed, repair_budget, v_format)
+    _device_of(q=q, k=k, v=v)
     if ws is None:
         ws = alloc_workspace(v, o)
     if out is None:

@@ -259,6 +259,17 @@ def test_ragged_shapes(S, dtype):
     check_against_oracle(q, k, v, kc=min(5, S), iters=3, name=f"ragged S={S} {dtype}")
 
 
+@pytest.mark.parametrize("kc,iters,seed", [(33, 2, 0), (48, 0, 2**64 - 1), (64, 3, 12345), (1, 2, 0)],
+                         ids=["k33", "k48_T0_seed_max", "k64_seed", "k1"])
+def test_kmeans_options(kc, iters, seed):
+    # cluster counts that need 3 and 4 tiles of 16 centroids in the assignment
+    # pass, the largest k, no Lloyd iteration at all (initial centroids, then
+    # the final assignment), one cluster, and seeds other than 0 (the initial
+    # centroids' offset), on two batches of two heads
+    w, q, k, v = _cfg(2, B=2, H=2, S=1000)
+    check_against_oracle(q, k, v, kc=kc, iters=iters, seed=seed, name=f"k={kc} T={iters} seed={seed}")
+
+
 @pytest.mark.parametrize("smooth", [0, 1])
 def test_plain_and_smooth_on_outliers(smooth):
     w, q, k, v = _cfg(2, H=2, S=2048)
