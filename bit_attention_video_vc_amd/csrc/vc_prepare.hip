@@ -26,24 +26,40 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t value, int64_t n) {
     p[i] = value;
 }
 
-// max|v| over each (b,h).  grid (ceil(S/64), H, B), 256 threads.
+// max|v| over each (b,h).  grid (ceil(S/kAbsTok), H, B), 256 threads.
+// The maximum is taken on the magnitude bits: for finite fp16 and bf16
+// values, |x| orders as its 15 low bits do, so one conversion per workgroup
+// gives exactly max|v|.
+constexpr int kAbsTok = 256;          // tokens per workgroup (16 per pass of 256 threads)
 __global__ void __launch_bounds__(256) k_v_absmax(TensorArg v, int S, vc_head_hdr* hdr) {
-  __shared__ float red[16];
+  __shared__ uint32_t red[4];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y;
-  const int s0 = blockIdx.x * 64;
-  float m = 0.0f;
+  const int s0 = blockIdx.x * kAbsTok;
+  const uint16_t* base = reinterpret_cast<const uint16_t*>(v.p) + b * v.sB + h * v.sH + 8 * (threadIdx.x & 15);
+  // all loads first (rows past S re-read row S-1 of the same head, which
+  // leaves the maximum unchanged), then the maxima
+  uint4 raw[kAbsTok / 16];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int s = s0 + it * 16 + (threadIdx.x >> 4);
-    if (s < S) {
-      float x[8];
-      load8(v.p, b * v.sB + s * v.sS + h * v.sH + 8 * (threadIdx.x & 15), v.dtype, x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
-    }
+  for (int it = 0; it < kAbsTok / 16; ++it) {
+    const int s = min(s0 + it * 16 + static_cast<int>(threadIdx.x >> 4), S - 1);
+    raw[it] = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(s) * v.sS);
   }
-  m = block_max(m, red);
-  if (threadIdx.x == 0 && m > 0.0f) atomicMax(&hdr[b * H + h].v_amax_bits, __float_as_uint(m));
+  uint32_t m = 0;
+#pragma unroll
+  for (int it = 0; it < kAbsTok / 16; ++it) {
+    const uint32_t w[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o, 64)));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float a = v.dtype == VC_BF16 ? bf16_bits_to_f32(m) : f16_bits_to_f32(m);
+    if (a > 0.0f) atomicMax(&hdr[b * H + h].v_amax_bits, __float_as_uint(a));
+  }
 }
 
 __device__ __forceinline__ float sketch1(float x, int shift) {
@@ -297,24 +313,37 @@ __global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int
 }
 
 // Per-cluster start offsets and per-chunk offsets for the stable scatter.
-// grid (BH), 64 threads (thread = cluster).
-__global__ void __launch_bounds__(64) k_cluster_scan(int S, int k, int asg, const int32_t* chunk_hist,
-                                                     int32_t* chunk_off) {
+// grid (BH), 64 * kScanRows threads: thread (r, c) = (tid / 64, tid % 64)
+// walks row r, one contiguous range of chunks, for cluster c -- once to total
+// it, once to write the offsets; integer sums, so any split gives the same
+// offsets as one walk over all chunks.
+constexpr int kScanRows = 16;
+__global__ void __launch_bounds__(64 * kScanRows) k_cluster_scan(int S, int k, int asg, const int32_t* chunk_hist,
+                                                                 int32_t* chunk_off) {
+  __shared__ int32_t part[kScanRows][kMaxK];
   __shared__ int32_t tot[kMaxK];
-  const int bh = blockIdx.x, c = threadIdx.x;
+  const int bh = blockIdx.x, c = threadIdx.x & 63, r = threadIdx.x >> 6;
   const int nchunk = (S + asg - 1) / asg;
+  const int per = (nchunk + kScanRows - 1) / kScanRows;
+  const int j0 = min(r * per, nchunk), j1 = min(j0 + per, nchunk);
   const int32_t* hst = chunk_hist + static_cast<int64_t>(bh) * nchunk * k;
   int32_t* off = chunk_off + static_cast<int64_t>(bh) * nchunk * k;
   int32_t t = 0;
   if (c < k)
-    for (int j = 0; j < nchunk; ++j) t += hst[j * k + c];
-  tot[c] = t;
+    for (int j = j0; j < j1; ++j) t += hst[j * k + c];
+  part[r][c] = t;
   __syncthreads();
-  int32_t start = 0;
-  for (int j = 0; j < c && j < k; ++j) start += tot[j];
+  if (r == 0) {
+    int32_t sum = 0;
+    for (int i = 0; i < kScanRows; ++i) sum += part[i][c];
+    tot[c] = sum;
+  }
+  __syncthreads();
   if (c < k) {
-    int32_t run = start;
-    for (int j = 0; j < nchunk; ++j) {
+    int32_t run = 0;
+    for (int j = 0; j < c; ++j) run += tot[j];          // clusters before c
+    for (int i = 0; i < r; ++i) run += part[i][c];      // earlier rows of cluster c
+    for (int j = j0; j < j1; ++j) {
       off[j * k + c] = run;
       run += hst[j * k + c];
     }
@@ -849,7 +878,7 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
   if (o.smooth) {
     const int asg = asg_tokens(BH, S);
     const int nch = (S + asg - 1) / asg;
-    hipLaunchKernelGGL(k_v_absmax, dim3((S + 63) / 64, H, B), dim3(256), 0, st, v, S, ws.hdr);
+    hipLaunchKernelGGL(k_v_absmax, dim3((S + kAbsTok - 1) / kAbsTok, H, B), dim3(256), 0, st, v, S, ws.hdr);
     VC_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_kmeans_init, dim3(BH), dim3(256), 0, st, v, S, H, k, o.seed, ws.hdr, ws.cent, ws.csum,
                        ws.ccount, ws.cent_op, ws.cnorm);
@@ -864,7 +893,8 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
     }
     launch_assign<false, true>(dim3(nch, H, B), st, v, S, k, asg, ws);
     VC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_cluster_scan, dim3(BH), dim3(64), 0, st, S, k, asg, ws.chunk_hist, ws.chunk_off);
+    hipLaunchKernelGGL(k_cluster_scan, dim3(BH), dim3(64 * kScanRows), 0, st, S, k, asg, ws.chunk_hist,
+                       ws.chunk_off);
     VC_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_cluster_scatter, dim3(nch, H, B), dim3(256), 0, st, S, k, asg, ws.assign, ws.chunk_off,
                        ws.perm);
