@@ -660,48 +660,74 @@ __global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const in
 // ---------------------------------------------------------------------------
 // Residual repair ("Open VC Attention", Description): the quantisation error
 // e = fp32(R - fp32(s_v * dec(code))) of the worst-rounded value tokens.
+// The codes come from the conversion instruction, exactly as the residual
+// quantiser makes them (|r * inv| <= 448 up to one rounding, where it gives
+// e4m3_encode's bytes), and go back to fp32 with the widening conversion,
+// which is exact.
 __device__ __forceinline__ void resid_err(const float* xv /*8*/, const float* mu /*8*/, float s_v, float inv,
                                           float* e /*8*/) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = xv[i] - mu[i];
+  const int c0 = static_cast<int>(e4m3_pack4(r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv));
+  const int c1 = static_cast<int>(e4m3_pack4(r[4] * inv, r[5] * inv, r[6] * inv, r[7] * inv));
+  const v2f d[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(c0, false), __builtin_amdgcn_cvt_pk_f32_fp8(c0, true),
+                    __builtin_amdgcn_cvt_pk_f32_fp8(c1, false), __builtin_amdgcn_cvt_pk_f32_fp8(c1, true)};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float r = xv[i] - mu[i];
-    const float deq = s_v * e4m3_decode(e4m3_encode(r * inv));
-    e[i] = r - deq;
+    const float deq = s_v * d[i >> 1][i & 1];
+    e[i] = r[i] - deq;
   }
 }
 
 // Squared error norm per permuted position (sequential fp64 sum over d).
-// grid (nblk, H, B), 128 threads (one key per thread).
+// The block's gathered rows are staged in LDS first, 16 lanes per row (whole
+// rows per load instruction), at a padded pitch; then thread j sums row j in
+// channel order.  grid (nblk, H, B), 128 threads.
+constexpr int kNormPitch = kD / 8 + 1;   // 16-byte units per LDS row
 __global__ void __launch_bounds__(128) k_repair_norm(TensorArg v, int S, const int32_t* perm, const float* v_mean,
                                                      const vc_head_hdr* hdr, double* norm) {
   __shared__ float mu[kD];
+  __shared__ int32_t pp[kBlock];
+  __shared__ uint4 rows[kBlock * kNormPitch];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x;
-  mu[threadIdx.x] = v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + threadIdx.x];
+  const int tid = threadIdx.x;
+  const int p0 = blk * kBlock;
+  const int n = S - p0 < kBlock ? S - p0 : kBlock;
+  mu[tid] = v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + tid];
+  if (tid < n) pp[tid] = perm[static_cast<int64_t>(bh) * S + p0 + tid];
   __syncthreads();
-  const int p = blk * kBlock + threadIdx.x;
-  if (p >= S) return;
-  const int s = perm[static_cast<int64_t>(bh) * S + p];
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(v.p) + b * v.sB + h * v.sH;
+  for (int t = tid; t < n * (kD / 8); t += blockDim.x) {
+    const int j = t >> 4, c = t & 15;
+    rows[j * kNormPitch + c] = *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(pp[j]) * v.sS + 8 * c);
+  }
+  __syncthreads();
+  if (tid >= n) return;
   float s_v, inv;
   v_scales(hdr[bh], &s_v, &inv);
   double acc = 0.0;
-  for (int c8 = 0; c8 < kD; c8 += 8) {
+  for (int c = 0; c < kD / 8; ++c) {
     float x[8], e[8];
-    load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
-    resid_err(x, mu + c8, s_v, inv, e);
+    load8(&rows[tid * kNormPitch + c], 0, v.dtype, x);
+    resid_err(x, mu + 8 * c, s_v, inv, e);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = acc + static_cast<double>(e[i]) * static_cast<double>(e[i]);
   }
-  norm[static_cast<int64_t>(bh) * S + p] = acc;
+  norm[static_cast<int64_t>(bh) * S + p0 + tid] = acc;
 }
 
 // Top-nrep positions by error norm (ties to the smaller position), written in
 // ascending position order; radix select on the fp64 bit patterns (the norms
 // are >= 0, so their bits order like the values).  grid (BH), 256 threads.
+constexpr int kSelUnroll = 8;
 __global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep_pad, const double* norm,
                                                        int32_t* rep_pos, vc_head_hdr* hdr) {
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t suf[256];
   __shared__ uint64_t sh_prefix;
-  __shared__ int32_t sh_remaining;
+  __shared__ int32_t sh_remaining, sh_sel, sh_cum;
   __shared__ int32_t wsum[2][4];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint64_t* key = reinterpret_cast<const uint64_t*>(norm) + static_cast<int64_t>(bh) * S;
@@ -715,23 +741,56 @@ __global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep
     hist[tid] = 0;
     __syncthreads();
     const uint64_t prefix = sh_prefix;
-    for (int p = tid; p < S; p += 256) {
-      const uint64_t u = key[p];
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> (8 * pos)) & 255u], 1u);
+    for (int p0 = 0; p0 < S; p0 += 256 * kSelUnroll) {
+      // kSelUnroll keys per thread per memory round trip (the loop bound is
+      // uniform, so every lane reaches the ballots)
+      uint64_t uu[kSelUnroll];
+#pragma unroll
+      for (int i = 0; i < kSelUnroll; ++i) {
+        const int p = p0 + tid + 256 * i;
+        uu[i] = key[min(p, S - 1)];
+      }
+#pragma unroll
+      for (int i = 0; i < kSelUnroll; ++i) {
+        const uint64_t u = uu[i];
+        const bool act = p0 + tid + 256 * i < S && (u & mask) == prefix;
+        const uint32_t bin = static_cast<uint32_t>(u >> (8 * pos)) & 255u;
+        // the first active lane's bin takes one add for every lane that
+        // shares it (most keys share a few bins in the leading bytes); the
+        // rest add 1
+        const uint64_t am = __ballot(act);
+        if (am) {
+          const int leader = __ffsll(static_cast<unsigned long long>(am)) - 1;
+          const uint32_t lb = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
+          const uint64_t same = __ballot(act && bin == lb);
+          if (lane == leader) atomicAdd(&hist[lb], static_cast<uint32_t>(__popcll(same)));
+          else if (act && bin != lb) atomicAdd(&hist[bin], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    // suffix[t] = keys in bins t..255; the selected bin is the highest t with
+    // suffix[t] >= remaining (bins above it are all taken)
+    suf[tid] = hist[tid];
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const uint32_t add = tid + d < 256 ? suf[tid + d] : 0u;
+      __syncthreads();
+      suf[tid] += add;
+      __syncthreads();
+    }
+    {
+      const int32_t rem = sh_remaining;
+      const uint32_t above = tid < 255 ? suf[tid + 1] : 0u;
+      if (static_cast<int32_t>(suf[tid]) >= rem && static_cast<int32_t>(above) < rem) {
+        sh_sel = tid;
+        sh_cum = static_cast<int32_t>(above);
+      }
     }
     __syncthreads();
     if (tid == 0) {
-      int32_t rem = sh_remaining, cum = 0;
-      int sel = 0;
-      for (int bin = 255; bin >= 0; --bin) {
-        if (cum + static_cast<int32_t>(hist[bin]) >= rem) {
-          sel = bin;
-          break;
-        }
-        cum += hist[bin];
-      }
-      sh_remaining = rem - cum;
-      sh_prefix = prefix | (static_cast<uint64_t>(sel) << (8 * pos));
+      sh_remaining -= sh_cum;
+      sh_prefix = prefix | (static_cast<uint64_t>(sh_sel) << (8 * pos));
     }
     mask |= 0xFFull << (8 * pos);
     __syncthreads();
@@ -741,9 +800,17 @@ __global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep
   int32_t carry_eq = 0, carry_out = 0;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* out = rep_pos + static_cast<int64_t>(bh) * nrep_pad;
+  uint64_t uu[kSelUnroll];
   for (int base = 0; base < S; base += 256) {
+    const int it = (base >> 8) % kSelUnroll;
+    if (it == 0) {
+#pragma unroll
+      for (int i = 0; i < kSelUnroll; ++i) uu[i] = key[min(base + tid + 256 * i, S - 1)];
+    }
     const int p = base + tid;
-    const uint64_t u = p < S ? key[p] : 0;
+    uint64_t u = uu[0];
+#pragma unroll
+    for (int i = 1; i < kSelUnroll; ++i) u = it == i ? uu[i] : u;
     const bool eq = p < S && u == T;
     const uint64_t meq = __ballot(eq);
     if (lane == 0) wsum[0][w] = __popcll(meq);
