@@ -722,13 +722,15 @@ __global__ void __launch_bounds__(128) k_repair_norm(TensorArg v, int S, const i
 // ascending position order; radix select on the fp64 bit patterns (the norms
 // are >= 0, so their bits order like the values).  grid (BH), 256 threads.
 constexpr int kSelUnroll = 8;
-__global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep_pad, const double* norm,
+constexpr int kSelThreads = 1024;     // one workgroup per head
+constexpr int kSelWaves = kSelThreads / 64;
+__global__ void __launch_bounds__(kSelThreads) k_repair_select(int S, int nrep, int nrep_pad, const double* norm,
                                                        int32_t* rep_pos, vc_head_hdr* hdr) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t suf[256];
   __shared__ uint64_t sh_prefix;
   __shared__ int32_t sh_remaining, sh_sel, sh_cum;
-  __shared__ int32_t wsum[2][4];
+  __shared__ int32_t wsum[2][kSelWaves];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint64_t* key = reinterpret_cast<const uint64_t*>(norm) + static_cast<int64_t>(bh) * S;
   if (tid == 0) {
@@ -738,22 +740,22 @@ __global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep
   }
   uint64_t mask = 0;
   for (int pos = 7; pos >= 0; --pos) {
-    hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
     const uint64_t prefix = sh_prefix;
-    for (int p0 = 0; p0 < S; p0 += 256 * kSelUnroll) {
+    for (int p0 = 0; p0 < S; p0 += kSelThreads * kSelUnroll) {
       // kSelUnroll keys per thread per memory round trip (the loop bound is
       // uniform, so every lane reaches the ballots)
       uint64_t uu[kSelUnroll];
 #pragma unroll
       for (int i = 0; i < kSelUnroll; ++i) {
-        const int p = p0 + tid + 256 * i;
+        const int p = p0 + tid + kSelThreads * i;
         uu[i] = key[min(p, S - 1)];
       }
 #pragma unroll
       for (int i = 0; i < kSelUnroll; ++i) {
         const uint64_t u = uu[i];
-        const bool act = p0 + tid + 256 * i < S && (u & mask) == prefix;
+        const bool act = p0 + tid + kSelThreads * i < S && (u & mask) == prefix;
         const uint32_t bin = static_cast<uint32_t>(u >> (8 * pos)) & 255u;
         // the first active lane's bin takes one add for every lane that
         // shares it (most keys share a few bins in the leading bytes); the
@@ -771,15 +773,15 @@ __global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep
     __syncthreads();
     // suffix[t] = keys in bins t..255; the selected bin is the highest t with
     // suffix[t] >= remaining (bins above it are all taken)
-    suf[tid] = hist[tid];
+    if (tid < 256) suf[tid] = hist[tid];
     __syncthreads();
     for (int d = 1; d < 256; d <<= 1) {
       const uint32_t add = tid + d < 256 ? suf[tid + d] : 0u;
       __syncthreads();
-      suf[tid] += add;
+      if (tid < 256) suf[tid] += add;
       __syncthreads();
     }
-    {
+    if (tid < 256) {
       const int32_t rem = sh_remaining;
       const uint32_t above = tid < 255 ? suf[tid + 1] : 0u;
       if (static_cast<int32_t>(suf[tid]) >= rem && static_cast<int32_t>(above) < rem) {
@@ -801,11 +803,11 @@ __global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* out = rep_pos + static_cast<int64_t>(bh) * nrep_pad;
   uint64_t uu[kSelUnroll];
-  for (int base = 0; base < S; base += 256) {
-    const int it = (base >> 8) % kSelUnroll;
+  for (int base = 0; base < S; base += kSelThreads) {
+    const int it = (base / kSelThreads) % kSelUnroll;
     if (it == 0) {
 #pragma unroll
-      for (int i = 0; i < kSelUnroll; ++i) uu[i] = key[min(base + tid + 256 * i, S - 1)];
+      for (int i = 0; i < kSelUnroll; ++i) uu[i] = key[min(base + tid + kSelThreads * i, S - 1)];
     }
     const int p = base + tid;
     uint64_t u = uu[0];
@@ -824,13 +826,13 @@ __global__ void __launch_bounds__(256) k_repair_select(int S, int nrep, int nrep
     int32_t idx = carry_out + __popcll(mt & lt);
     for (int j = 0; j < w; ++j) idx += wsum[1][j];
     if (take) out[idx] = p;
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kSelWaves; ++j) {
       carry_eq += wsum[0][j];
       carry_out += wsum[1][j];
     }
     __syncthreads();
   }
-  for (int i = nrep + tid; i < nrep_pad; i += 256) out[i] = -1;
+  for (int i = nrep + tid; i < nrep_pad; i += kSelThreads) out[i] = -1;
 }
 
 // Largest |e| over the repaired rows.  grid (nrep_pad/128, H, B), 128 threads.
@@ -986,7 +988,7 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
     const dim3 grep(ws.nrep_pad / kBlock, H, B);
     hipLaunchKernelGGL(k_repair_norm, gblk, dim3(128), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.rep_norm);
     VC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_repair_select, dim3(BH), dim3(256), 0, st, S, ws.nrep, ws.nrep_pad, ws.rep_norm,
+    hipLaunchKernelGGL(k_repair_select, dim3(BH), dim3(kSelThreads), 0, st, S, ws.nrep, ws.nrep_pad, ws.rep_norm,
                        ws.rep_pos, ws.hdr);
     VC_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_repair_eamax, grep, dim3(128), 0, st, v, S, ws.nrep_pad, ws.perm, ws.v_mean, ws.rep_pos,
