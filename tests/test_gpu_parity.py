@@ -287,6 +287,25 @@ def test_repair(beta):
     assert np.mean(run.err_exact) < np.mean(base.err_exact)
 
 
+@pytest.mark.parametrize("S,beta,dups", [(9000, 0.3, True), (9000, 1e-4, False), (300, 0.9, True)],
+                         ids=["S9000_beta0.3_ties", "S9000_one_token", "S300_beta0.9_ties"])
+def test_repair_select_edges(S, beta, dups):
+    # the top-k select over a key count that leaves its 8 x 1024-key chunks
+    # ragged, a repair set of one token, a budget of 90%, and many equal error
+    # norms: with every token a copy of one of 50 rows, copies in one block
+    # have the same error, so the set among ties goes by position
+    g = torch.Generator().manual_seed(31 + S)
+    B, H = 1, 2
+    q = torch.randn(B, S, H, 128, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, S, H, 128, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, S, H, 128, generator=g)
+    if dups:
+        v = v[:, torch.randint(0, 50, (S,), generator=g)]
+    v = v.to(torch.bfloat16)
+    check_against_oracle(q.cuda(), k.cuda(), v.cuda(), kc=4, iters=2, beta=beta, name=f"repair edges S={S} beta={beta}",
+                         rows=np.arange(0, S, max(1, S // 64)), exact_tol=TOL_EXACT_ZERO_MEAN_V)
+
+
 def test_strided_views_and_3d_input():
     g = torch.Generator().manual_seed(5)
     S, H = 700, 2
