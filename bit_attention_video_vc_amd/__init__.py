@@ -213,7 +213,12 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, smooth: bool
               stream=None) -> torch.Tensor:
     """Full call: prepare_v, prepare_qk and the fused forward; returns bf16 [B,S,H,128] (or [S,H,128])."""
     o = v_opts(smooth, clusters, iters, seed, repair_budget, v_format)
-    _device_of(q=q, k=k, v=v)
+    # the three calls share one workspace laid out for v's shape: refuse any
+    # other shape before the first call
+    for name, t in (("q", q), ("k", k)) + ((("out", out),) if out is not None else ()):
+        if isinstance(t, torch.Tensor) and isinstance(v, torch.Tensor) and t.shape != v.shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, v has {tuple(v.shape)}; all must match")
+    _device_of(q=q, k=k, v=v, **({} if out is None else {"out": out}))
     if ws is None:
         ws = alloc_workspace(v, o)
     if out is None:

@@ -156,7 +156,7 @@ vc::WsPtrs ws_ptrs(const Plan& p, void* ws) {
   w.cent = reinterpret_cast<int32_t*>(scr + p.scr.cent);
   w.cent_op = scr + p.scr.cent_op;
   w.cnorm = reinterpret_cast<int32_t*>(scr + p.scr.cnorm);
-  w.csum = reinterpret_cast<int32_t*>(scr + p.scr.csum);
+  w.csum = reinterpret_cast<int64_t*>(scr + p.scr.csum);
   w.ccount = reinterpret_cast<int32_t*>(scr + p.scr.ccount);
   w.chunk_hist = reinterpret_cast<int32_t*>(scr + p.scr.chunk_hist);
   w.chunk_off = reinterpret_cast<int32_t*>(scr + p.scr.chunk_off);
@@ -269,7 +269,7 @@ vc_status vc_prepare_qk(const vc_desc* qd, const void* q, const vc_desc* kd, con
   if ((s = check_ptr(k, "k")) != VC_OK) return s;
   if ((s = check_ws(p, ws, ws_bytes)) != VC_OK) return s;
   if ((s = check_device()) != VC_OK) return s;
-  const hipError_t e = vc::launch_prepare_qk(targ(qd, q), targ(kd, k), p.B, p.S, p.H, ws_ptrs(p, ws),
+  const hipError_t e = vc::launch_prepare_qk(targ(qd, q), targ(kd, k), p.B, p.S, p.H, opts->v_format, ws_ptrs(p, ws),
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(VC_ERR_DEVICE, "prepare_qk launch: %s", hipGetErrorString(e));
   return ok();

@@ -432,14 +432,20 @@ __device__ __forceinline__ void score_tile(const uint8_t* ktile, int lane, const
   }
 }
 
-// Mask keys >= kval in a ragged last tile (lane group g holds keys 16t+4g+i).
+// Mask the key slots whose permuted position in the tile is >= kval (a
+// ragged last tile).  Lane group g of score sub-tile t holds slots 16t+4g+i;
+// E4M3 workspaces store position j in slot j, MXFP4 workspaces position
+// mx_pos_of_slot(slot) = 64(t/4) + 16g + 4(t%4) + i.
+template <int VF>
 __device__ __forceinline__ void mask_tile(v4f (&sc)[8][2], int g, int kval) {
-  const int kr = kval - 4 * g;   // compare 16t+i against it: no per-key registers
+  // compare the lane-independent part against kval minus the lane group's
+  // part: no per-key registers
+  const int kr = kval - (VF ? 16 : 4) * g;
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (16 * t + i >= kr) sc[t][0][i] = sc[t][1][i] = kNegBig;
+      if ((VF ? 64 * (t >> 2) + 4 * (t & 3) : 16 * t) + i >= kr) sc[t][0][i] = sc[t][1][i] = kNegBig;
 }
 
 // Integer running max and ExpCast codes of the first tile.
@@ -647,7 +653,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
     step_barrier<VF>();
     if (__builtin_expect(kb + 3 >= nblk, 0)) {
       // tile kb+2 is the last tile (keys past S masked) or past it (all masked)
-      mask_tile(sn, g, kb + 2 == last ? c.kval_last : 0);
+      mask_tile<VF>(sn, g, kb + 2 == last ? c.kval_last : 0);
 #pragma unroll
       for (int qi = 0; qi < 2; ++qi) {
         mn[qi] = max4(sn[0][qi]);
@@ -808,13 +814,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   {
     v4f sc[8][2];
     score_tile(kbuf0, lane, qop, sc);
-    if (nblk == 1 && c.kval_last < kBlock) mask_tile(sc, g, c.kval_last);
+    if (nblk == 1 && c.kval_last < kBlock) mask_tile<VF>(sc, g, c.kval_last);
     softmax_tile(sc, ((sqs * c.ks[0]) * a.sm_scale) * kLog2e, acc.st, acc.P);
   }
   // scores of tile 1 (a copy of tile 0, masked out, when there is none):
   // their codes are cast in the first step
   score_tile(kbuf1, lane, qop, acc.sh);
-  if (nblk <= 2) mask_tile(acc.sh, g, nblk == 2 ? c.kval_last : 0);
+  if (nblk <= 2) mask_tile<VF>(acc.sh, g, nblk == 2 ? c.kval_last : 0);
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
     acc.mh[qi] = max4(acc.sh[0][qi]);

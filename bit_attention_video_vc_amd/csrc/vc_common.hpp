@@ -120,6 +120,16 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 __device__ __forceinline__ int row_tile_off(int r, int d) {
   return ((((r >> 4) * 2 + ((d & 31) >> 4)) * 64 + (r & 15) + 16 * (d >> 5)) << 4) + (d & 15);
 }
+// MXFP4 workspaces relabel the keys of every tile so that each FP4 operand
+// lane group of the P.V product holds one MXFP4 scale group, a run of 32
+// consecutive permuted positions: key slot r = 16t + 4g + i (row r of the K
+// tile, key i of lane group g in score sub-tile t) holds permuted position
+// 64(t/4) + 16g + 4(t%4) + i of the tile.  Non-causal attention does not
+// depend on the order of keys within a tile, so only the storage changes.
+__host__ __device__ inline int mx_pos_of_slot(int r) {
+  const int t = r >> 4, g = (r >> 2) & 3, i = r & 3;
+  return 64 * (t >> 2) + 16 * g + 4 * (t & 3) + i;
+}
 // Transposed tile: key j and channel d, in the P^T slot order of the score
 // accumulator (16x16 MFMA output rows 4g..4g+3 of key sub-tile t).
 __device__ __forceinline__ int tr_tile_off(int j, int d) {
@@ -183,7 +193,7 @@ __host__ __device__ inline Scratch scratch_layout(int64_t BH, int S, int k, int 
   s.cent = o;        o = align256(o + sizeof(int32_t) * BH * k * kD);
   s.cent_op = o;     o = align256(o + static_cast<size_t>(BH) * kCentOpBytes);
   s.cnorm = o;       o = align256(o + sizeof(int32_t) * BH * kMaxK);
-  s.csum = o;        o = align256(o + sizeof(int32_t) * BH * k * kD);
+  s.csum = o;        o = align256(o + sizeof(int64_t) * BH * k * kD);
   s.ccount = o;      o = align256(o + sizeof(int32_t) * BH * k);
   s.chunk_hist = o;  o = align256(o + sizeof(int32_t) * BH * nchunk * k);
   s.chunk_off = o;   o = align256(o + sizeof(int32_t) * BH * nchunk * k);

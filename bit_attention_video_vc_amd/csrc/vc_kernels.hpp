@@ -26,7 +26,9 @@ struct WsPtrs {
   float *q_scale, *k_scale, *v_mean, *rep_ks;
   vc_head_hdr* hdr;
   int32_t *assign, *perm, *rep_pos;
-  int32_t *cent, *csum, *ccount, *chunk_hist, *chunk_off, *cnorm;
+  int32_t* cent;
+  int64_t* csum;    // per-cluster sketch sums: up to 255 * S in magnitude
+  int32_t *ccount, *chunk_hist, *chunk_off, *cnorm;
   uint8_t* cent_op;
   double* rep_norm;
   int nblk, nrep, nrep_pad;
@@ -52,8 +54,8 @@ struct AttnArgs {
 
 hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_opts& o, const WsPtrs& ws,
                             hipStream_t st);
-hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& k, int B, int S, int H, const WsPtrs& ws,
-                             hipStream_t st);
+hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& k, int B, int S, int H, int v_format,
+                             const WsPtrs& ws, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int BH, hipStream_t st);
 
 }  // namespace vc

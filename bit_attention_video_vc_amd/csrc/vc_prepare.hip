@@ -103,7 +103,7 @@ __device__ void write_cent_ops(int bh, int k, const int32_t* cg, uint8_t* cent_o
 
 // Sketch shift and seeded strided initial centroids.  grid (BH), 256 threads.
 __global__ void __launch_bounds__(256) k_kmeans_init(TensorArg v, int S, int H, int k, uint64_t seed,
-                                                     vc_head_hdr* hdr, int32_t* cent, int32_t* csum,
+                                                     vc_head_hdr* hdr, int32_t* cent, int64_t* csum,
                                                      int32_t* ccount, uint8_t* cent_op, int32_t* cnorm) {
   const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
   const float a = __uint_as_float(hdr[bh].v_amax_bits);
@@ -181,7 +181,7 @@ __device__ __forceinline__ uint32_t sketch_bits(uint32_t e16, int dtype, int shi
 template <bool ACCUM, bool FINAL, int NCT>
 __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k, int asg, const vc_head_hdr* hdr,
                                                        const uint8_t* cent_op, const int32_t* cnorm,
-                                                       int32_t* csum, int32_t* ccount, int32_t* assign,
+                                                       int64_t* csum, int32_t* ccount, int32_t* assign,
                                                        int32_t* chunk_hist) {
   __shared__ int32_t sums[ACCUM ? kMaxK * kSumPitch : 1];
   __shared__ int32_t cnt[kMaxK];
@@ -273,10 +273,13 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
   }
   __syncthreads();
   if (ACCUM) {
-    int32_t* gs = csum + static_cast<int64_t>(bh) * k * kD;
+    // a workgroup's sums fit int32 (asg <= 1024 tokens of |x| <= 255); the
+    // head's can reach 255 * S (> 2^31 for S > 2^23): 64-bit adds (two's
+    // complement, so an unsigned add accumulates signed values)
+    unsigned long long* gs = reinterpret_cast<unsigned long long*>(csum + static_cast<int64_t>(bh) * k * kD);
     for (int i = tid; i < k * kD; i += 256) {
       const int32_t val = sums[(i / kD) * kSumPitch + (i % kD)];
-      if (val != 0) atomicAdd(&gs[i], val);
+      if (val != 0) atomicAdd(&gs[i], static_cast<unsigned long long>(static_cast<long long>(val)));
     }
     if (tid < k && cnt[tid] != 0) atomicAdd(&ccount[bh * k + tid], cnt[tid]);
   }
@@ -293,16 +296,16 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
 // (|q| <= 255 and a non-integer quotient is >= 1/(2n) >= 2^-25 from one).
 // grid (BH, ceil(k/8)), 256 threads; a workgroup owns 8 centroids.
 constexpr int kUpdCent = 8;
-__global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int32_t* csum, int32_t* ccount,
+__global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int64_t* csum, int32_t* ccount,
                                                       uint8_t* cent_op, int32_t* cnorm) {
   const int bh = blockIdx.x;
   const int c0 = blockIdx.y * kUpdCent, c1 = c0 + kUpdCent < k ? c0 + kUpdCent : k;
   int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
-  int32_t* sg = csum + static_cast<int64_t>(bh) * k * kD;
+  int64_t* sg = csum + static_cast<int64_t>(bh) * k * kD;
   for (int i = c0 * kD + threadIdx.x; i < c1 * kD; i += blockDim.x) {
     const int32_t n = ccount[bh * k + i / kD];
     if (n > 0) {
-      const int64_t num = 2 * static_cast<int64_t>(sg[i]) + n;
+      const int64_t num = 2 * sg[i] + n;
       cg[i] = static_cast<int32_t>(floor(static_cast<double>(num) / static_cast<double>(2 * n)));
     }
     sg[i] = 0;
@@ -523,10 +526,13 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
 
 // MXFP4 residual ("Nunchux AI lanza VC-Attention kernel ...", paragraph 2:
 // a 4-bit residual beside E4M3; taken as OCP MXFP4 for the gfx950 matrix
-// core): R = fp32(v - mu), one E8M0 scale per channel and group of 32 keys
-// -- the keys one matrix-core lane holds as an FP4 operand -- chosen as the
-// smallest power of two X with max|R|/X <= 6, and E2M1 codes of R/X (round
-// half to even, sign from R).  No per-head scale (s_v = 1, mu' = mu).
+// core): R = fp32(v - mu), one E8M0 scale per channel and group of 32
+// consecutive permuted positions of the tile, chosen as the smallest power of
+// two X with max|R|/X <= 6, and E2M1 codes of R/X (round half to even, sign
+// from R).  No per-head scale (s_v = 1, mu' = mu).  Group u (positions
+// 32u .. 32u+31) is exactly the 32 values that FP4 operand lane group u of
+// the P.V product holds, nibble n being position 32u + n: the key slots of
+// the tile are relabelled to match (mx_pos_of_slot; the K rows follow).
 // grid (nblk, H, B), 256 threads; thread = 2 (channel, group) pairs.
 __device__ __forceinline__ uint32_t e2m1_encode(float y) {
   const float a = fabsf(y);
@@ -586,21 +592,16 @@ __global__ void __launch_bounds__(256) k_v_quant_pack_fp4(TensorArg v, int S, co
   __syncthreads();
   uint8_t* tile = v8 + (static_cast<int64_t>(bh) * nblk + blk) * kTileBytes;
   for (int task = threadIdx.x; task < kD * 4; task += blockDim.x) {
-    const int d = task & (kD - 1), u = task >> 7;     // channel, lane group
-    // nibble n of lane group u holds P-operand K index kb, which is key
-    // 16*((kb%32)/4) + 4*(kb/32) + kb%4
+    const int d = task & (kD - 1), u = task >> 7;     // channel, group = lane group
+    // nibble n of lane group u holds permuted position 32u + n of the tile
     float amax = 0.0f;
 #pragma unroll 8
-    for (int n = 0; n < 32; ++n) {
-      const int kb = 64 * (u & 1) + 16 * (u >> 1) + 32 * (n >> 4) + (n & 15);
-      amax = fmaxf(amax, fabsf(res[16 * ((kb & 31) >> 2) + 4 * (kb >> 5) + (kb & 3)][d]));
-    }
+    for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(res[32 * u + n][d]));
     const int e = mx_exponent(amax);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll 8
     for (int n = 0; n < 32; ++n) {
-      const int kb = 64 * (u & 1) + 16 * (u >> 1) + 32 * (n >> 4) + (n & 15);
-      const float y = ldexpf(res[16 * ((kb & 31) >> 2) + 4 * (kb >> 5) + (kb & 3)][d], -e);
+      const float y = ldexpf(res[32 * u + n][d], -e);
       w[n >> 3] |= e2m1_encode(y) << (4 * (n & 7));
     }
     const int lane = u * 16 + (d & 15), dt = d >> 4;
@@ -610,11 +611,15 @@ __global__ void __launch_bounds__(256) k_v_quant_pack_fp4(TensorArg v, int S, co
 }
 
 // Per-block amax E4M3 quantisation of 128 rows into a row tile.  GATHER: row
-// p is token perm[p] (K); otherwise row p is token p (Q).
+// r holds permuted position p = 128*blk + r, i.e. token perm[p] (K; with
+// `relabel`, the MXFP4 key slots, position 128*blk + mx_pos_of_slot(r));
+// otherwise row r is token 128*blk + r (Q).  A permutation entry outside
+// [0, S) -- a workspace that vc_prepare_v did not write for this shape --
+// reads as a zero row instead of an address outside the tensor.
 // grid (nblk, H, B), 256 threads; 4 (row, 16-channel) tasks per thread.
 template <bool GATHER>
-__global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const int32_t* perm, uint8_t* out8,
-                                                    float* scale) {
+__global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const int32_t* perm, int relabel,
+                                                    uint8_t* out8, float* scale) {
   __shared__ float red[16];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
   float val[4][16];
@@ -623,9 +628,14 @@ __global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const in
   for (int it = 0; it < 4; ++it) {
     const int task = threadIdx.x + 256 * it;
     const int r = task >> 3, c16 = (task & 7) * 16;
-    const int p = blk * kBlock + r;
-    if (p < S) {
-      const int s = GATHER ? perm[static_cast<int64_t>(bh) * S + p] : p;
+    const int p = blk * kBlock + (GATHER && relabel ? mx_pos_of_slot(r) : r);
+    int s = p;
+    bool live = p < S;
+    if (GATHER && live) {
+      s = perm[static_cast<int64_t>(bh) * S + p];
+      live = static_cast<unsigned>(s) < static_cast<unsigned>(S);
+    }
+    if (live) {
       const int64_t off = b * x.sB + s * x.sS + h * x.sH + c16;
       load8(x.p, off, x.dtype, &val[it][0]);
       load8(x.p, off + 8, x.dtype, &val[it][8]);
@@ -720,7 +730,8 @@ __global__ void __launch_bounds__(128) k_repair_norm(TensorArg v, int S, const i
 
 // Top-nrep positions by error norm (ties to the smaller position), written in
 // ascending position order; radix select on the fp64 bit patterns (the norms
-// are >= 0, so their bits order like the values).  grid (BH), 256 threads.
+// are >= 0, so their bits order like the values).  grid (BH), kSelThreads
+// (1024) threads.
 constexpr int kSelUnroll = 8;
 constexpr int kSelThreads = 1024;     // one workgroup per head
 constexpr int kSelWaves = kSelThreads / 64;
@@ -906,13 +917,16 @@ __global__ void __launch_bounds__(256) k_repair_kpack(int S, int nrep_pad, const
     const int r = t >> 3, c16 = (t & 7) * 16;
     const int i = blockIdx.x * kBlock + r;
     const int p = rep_pos[static_cast<int64_t>(bh) * nrep_pad + i];
+    // pad slots hold -1; a position outside [0, S) (a workspace that
+    // vc_prepare_v did not write for this shape) reads as a zero row
+    const bool live = static_cast<unsigned>(p) < static_cast<unsigned>(S);
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (p >= 0) {
+    if (live) {
       const uint8_t* src = k8 + (static_cast<int64_t>(bh) * nblk + p / kBlock) * kTileBytes;
       val = *reinterpret_cast<const uint4*>(src + row_tile_off(p % kBlock, c16));
     }
     *reinterpret_cast<uint4*>(dst + row_tile_off(r, c16)) = val;
-    if (c16 == 0) rep_ks[static_cast<int64_t>(bh) * nrep_pad + i] = p >= 0 ? k_scale[static_cast<int64_t>(bh) * nblk + p / kBlock] : 0.0f;
+    if (c16 == 0) rep_ks[static_cast<int64_t>(bh) * nrep_pad + i] = live ? k_scale[static_cast<int64_t>(bh) * nblk + p / kBlock] : 0.0f;
   }
 }
 
@@ -1001,13 +1015,14 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
   return hipSuccess;
 }
 
-hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& kt, int B, int S, int H, const WsPtrs& ws,
-                             hipStream_t st) {
+hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& kt, int B, int S, int H, int v_format,
+                             const WsPtrs& ws, hipStream_t st) {
   const int nblk = (S + kBlock - 1) / kBlock;
   const dim3 gblk(nblk, H, B);
-  hipLaunchKernelGGL((k_quant_rows<false>), gblk, dim3(256), 0, st, q, S, ws.perm, ws.q8, ws.q_scale);
+  hipLaunchKernelGGL((k_quant_rows<false>), gblk, dim3(256), 0, st, q, S, ws.perm, 0, ws.q8, ws.q_scale);
   VC_LAUNCH_CHECK();
-  hipLaunchKernelGGL((k_quant_rows<true>), gblk, dim3(256), 0, st, kt, S, ws.perm, ws.k8, ws.k_scale);
+  hipLaunchKernelGGL((k_quant_rows<true>), gblk, dim3(256), 0, st, kt, S, ws.perm, v_format == VC_V_MXFP4 ? 1 : 0,
+                     ws.k8, ws.k_scale);
   VC_LAUNCH_CHECK();
   if (ws.nrep > 0) {
     hipLaunchKernelGGL(k_repair_kpack, dim3(ws.nrep_pad / kBlock, H, B), dim3(256), 0, st, S, ws.nrep_pad,

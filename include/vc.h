@@ -84,8 +84,8 @@ typedef struct {
 typedef enum {
   VC_V_E4M3 = 0,           /* E4M3 codes with one scale per (b,h)                 */
   VC_V_MXFP4 = 1           /* OCP MXFP4 on gfx950: E2M1 codes, one power-of-two
-                              (E8M0) scale per channel and group of 32 keys of a
-                              128-key tile; no repair                            */
+                              (E8M0) scale per channel and run of 32 consecutive
+                              permuted positions of a 128-key tile; no repair   */
 } vc_v_format;
 
 /* V-Smooth options. */
@@ -112,7 +112,8 @@ typedef struct {
  * nrep_pad = 128*ceil(nrep/128).
  *   q8      u8  [BH][nblk] tiles of 16384 B: Q codes, original token order
  *   q_scale f32 [BH][nblk]
- *   k8      u8  [BH][nblk] tiles: K codes, PERMUTED order (row p = token perm[p])
+ *   k8      u8  [BH][nblk] tiles: K codes, PERMUTED order (row p = token perm[p];
+ *               VC_V_MXFP4: row r of tile b holds position 128b + mx(r), see below)
  *   k_scale f32 [BH][nblk]
  *   v8      u8  [BH][nblk] tiles: residual codes, permuted order, transposed
  *               (VC_V_MXFP4: the tile slot holds the E2M1 tile and its scales,
@@ -137,12 +138,15 @@ typedef struct {
  *   transposed tile (v8, rep_e8): the byte for (key j, channel d) is at
  *     ((((d/16)*2 + i/16)*64 + (d%16) + 16*g) * 16) + i%16,
  *     with g = (j%16)/4 and i = 4*(j/16) + j%4.
- *   MXFP4 tile (v8 with VC_V_MXFP4; 8704 of the slot's 16384 bytes): with
- *     kb = 32*g + i (g, i as above), lane group u = kb/64 + 2*((kb%64)/16 % 2)
- *     and nibble n = 16*((kb%64)/32) + kb%16, the E2M1 code of (key j,
- *     channel d) is nibble n%2 (low first) of byte
- *     ((d/16)*64 + u*16 + d%16) * 16 + n/2; the E8M0 exponent byte (scale
- *     2^(byte-127)) of the group (tile, d, u) is at 8192 + (u*16 + d%16)*8 + d/16.
+ *   MXFP4 tile (v8 with VC_V_MXFP4; 8704 of the slot's 16384 bytes): the
+ *     permuted positions 32u .. 32u+31 of the tile form scale group u; the
+ *     E2M1 code of (position j = 32u + n, channel d) is nibble n%2 (low
+ *     first) of byte ((d/16)*64 + u*16 + d%16) * 16 + n/2, and the E8M0
+ *     exponent byte (scale 2^(byte-127)) of the group (tile, d, u) is at
+ *     8192 + (u*16 + d%16)*8 + d/16.  The K rows of an MXFP4 workspace are
+ *     relabelled to match: row r = 16t + 4g + i of a k8 tile holds position
+ *     mx(r) = 64*(t/4) + 16*g + 4*(t%4) + i of the tile (rows whose position
+ *     is past S are zero).
  */
 typedef struct {
   size_t total;

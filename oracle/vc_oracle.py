@@ -47,9 +47,9 @@ Where the pages leave a step open, the reading taken is stated at the step
      the row sum a second time.
  R11 Softmax scale defaults to fp32(1/sqrt(128)); output is bf16 (RNE).
  R15 4-bit residual ([NUN] paragraph 2 names NVFP4 beside E4M3), taken as
-     OCP MXFP4: E2M1 codes, one power-of-two (E8M0) scale per group of 32
-     keys of one channel within a 128-key tile -- the 32 keys that one
-     matrix-core lane holds (see mx_group_of_key) -- the scale being the
+     OCP MXFP4: E2M1 codes, one power-of-two (E8M0) scale per channel and
+     group of 32 consecutive permuted positions within a 128-key tile
+     (positions 32u .. 32u+31 of the tile form group u), the scale being the
      smallest power of two X with max|R|/X <= 6, so nothing is clipped;
      values round half to even; no per-head scale (s_v = 1, mu' = mu).
 
@@ -145,16 +145,13 @@ def e2m1_encode(x) -> np.ndarray:
     return (code | np.where(np.signbit(x), 8, 0)).astype(np.int64)
 
 
+MX_GROUP = 32     # permuted positions per MXFP4 scale group (R15)
+
+
 def mx_group_of_key(j) -> np.ndarray:
-    """Group (0..3) of key j (0..127) of a tile: the matrix-core lane group g
-    that holds it as an FP4 operand.  The product O^T += V^T . P^T pairs
-    key 16t + 4u + i with the P operand's K index 32u + 4t + i; with FP4
-    operands lane group g holds the K indices 64*(g&1) + 16*(g>>1) + [0,16)
-    and the same + 32 (measured on the device)."""
-    j = np.asarray(j, dtype=np.int64)
-    t, u, i = j // 16, (j % 16) // 4, j % 4
-    kb = 32 * u + 4 * t + i
-    return kb // 64 + 2 * (((kb % 64) // 16) % 2)
+    """Group (0..3) of permuted position j within its 128-key tile: the runs
+    of 32 consecutive positions 32u .. 32u+31 form group u (R15)."""
+    return (np.asarray(j, dtype=np.int64) % BLOCK) // MX_GROUP
 
 
 def mx_scale_exponent(amax) -> np.ndarray:
@@ -297,7 +294,8 @@ def kmeans_update(x: np.ndarray, assign: np.ndarray, cent: np.ndarray) -> np.nda
     n = np.bincount(assign, minlength=k).astype(np.int64)
     onehot = np.zeros((x.shape[0], k), dtype=np.float64)
     onehot[np.arange(x.shape[0]), assign] = 1.0
-    # integer sums below 2^25 in magnitude: exact in float64 in any order
+    # integer sums of at most S terms of magnitude <= 255 (below 2^32 for
+    # S <= 2^24): exact in float64 in any order
     sums = np.rint(onehot.T @ x.astype(np.float64)).astype(np.int64)
     new = cent.copy()
     nz = n > 0

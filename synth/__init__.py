@@ -9,7 +9,9 @@ The shapes and value structure follow the video-DiT workloads the pages
 describe; no captured tensors, datasets or model weights are used.
 
 * "VC-Attention: Value Smoothing and Softmax Casting for Low-bit Attention",
-  Abstract: value outliers follow no fixed channel or spatiotemporal layout.
+  Abstract: the large values of V are not tied to particular channels or to
+  particular places in space or time, so the generator draws their token
+  positions at random per head.
 * "Nunchux AI lanza VC-Attention kernel ..." (reditua.com), paragraph 1: a
   5 s 720p clip from a 14B model is about 70k tokens; paragraph 2: value
   outliers sit in a few tokens and move between layers, heads and steps.

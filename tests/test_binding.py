@@ -53,3 +53,16 @@ def test_descriptor_of_unbatched_and_strided_views():
     assert (d.sB, d.sS, d.sH) == (3 * 300 * 128, 128, 300 * 128)
     with pytest.raises(ValueError):
         vc.desc_of(torch.zeros((4, 128, 2), dtype=torch.bfloat16).permute(0, 2, 1))   # D not contiguous
+
+
+def test_attention_refuses_mismatched_shapes():
+    # the workspace is laid out for v's shape; q, k or out of another shape
+    # are refused before any library call (the check needs no GPU)
+    v = _cpu((1, 256, 2, 128))
+    for bad in ((1, 128, 2, 128), (1, 256, 3, 128), (2, 256, 2, 128)):
+        with pytest.raises(ValueError, match="all must match"):
+            vc.attention(_cpu(bad), _cpu(), v)
+        with pytest.raises(ValueError, match="all must match"):
+            vc.attention(_cpu(), _cpu(bad), v)
+        with pytest.raises(ValueError, match="all must match"):
+            vc.attention(_cpu(), _cpu(), v, out=_cpu(bad))

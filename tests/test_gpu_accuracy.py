@@ -8,14 +8,17 @@ the original bf16/fp16 inputs) for three settings of the same call:
 * V-Smooth off (plain per-head E4M3 V, identity order, no block means),
 * for the repair workload, V-Smooth on without the repair.
 
-Each run is also checked against the oracle as in the parity tests.  Beside
-the errors the report gives the residual-energy ratio of the clustering,
-sum R^2 over sum (V - mean of its unsorted 128-token block)^2, from the
-oracle's own prepare: below 1 when the reorder groups similar tokens (a
-reported figure, not a gate).
-
-The gates are loose on purpose (the envelopes of the parity tests); the
-numbers themselves are the report.
+Each run is also checked against the oracle as in the parity tests, and the
+oracle's own rel-L2 against exact attention on the same rows is reported
+beside the GPU's: the GPU may exceed it by at most 2% (plus 1e-3), so any
+error above the 4% accuracy target is shown to be the method's, not the
+kernel's.  The 4% target is gated where the method meets it; the workloads
+whose names say "north_star_4pct_not_met" are those where the oracle itself
+is above it (zero-mean V), and there the test checks that it is.  Beside the
+errors the report gives the residual-energy ratio of the clustering, sum R^2
+over sum (V - mean of its unsorted 128-token block)^2, from the oracle's own
+prepare: below 1 when the reorder groups similar tokens (a reported figure,
+not a gate).
 """
 import numpy as np
 import pytest
@@ -24,7 +27,7 @@ import torch
 import bit_attention_video_vc_amd as vc
 import synth
 from oracle import vc_oracle as O
-from test_gpu_parity import TOL_ORACLE, GpuRun, say
+from test_gpu_parity import EXACT_RATIO, EXACT_SLACK, TOL_EXACT, TOL_ORACLE, GpuRun, say
 
 pytestmark = pytest.mark.gpu
 
@@ -55,25 +58,32 @@ def _errors(q, k, v, w, heads, rows, beta, smooth):
         got = run.out[b, :, h].float().cpu().numpy()[rows].astype(np.float64)
         ex = O.attention_exact(qn, kn, vn, rows=rows)
         e_or = O.rel_l2(got, ref)
-        assert e_or <= TOL_ORACLE, f"{w.name} (b={b},h={h}) smooth={smooth} beta={beta}: rel-L2 vs oracle {e_or:.3e}"
-        out.append((O.rel_l2(got, ex), _residual_energy_ratio(vn, hv) if smooth else None))
+        tag = f"{w.name} (b={b},h={h}) smooth={smooth} beta={beta}"
+        assert e_or <= TOL_ORACLE, f"{tag}: rel-L2 vs oracle {e_or:.3e}"
+        e_ex, e_or_ex = O.rel_l2(got, ex), O.rel_l2(ref, ex)
+        assert e_ex <= EXACT_RATIO * e_or_ex + EXACT_SLACK, f"{tag}: vs exact {e_ex:.3e}, oracle's own {e_or_ex:.3e}"
+        out.append((e_ex, _residual_energy_ratio(vn, hv) if smooth else None, e_or_ex))
     del run
     torch.cuda.empty_cache()
     return out
 
 
 CASES = [
-    # (config, overrides, heads, repair workload, bound on the smoothed error vs exact)
-    (1, {}, [(0, 0)], False, 0.04),
-    (2, {}, [(0, 0), (0, 7)], False, 0.04),
-    (4, {"H": 7}, [(0, 0), (0, 6)], False, 0.04),
-    (3, {}, [(0, 0), (0, 39)], False, 0.10),
-    (5, {}, [(0, 0), (1, 23)], True, 0.10),
+    # (config, overrides, heads, repair workload, the 4% target met by the method on these rows)
+    (1, {}, [(0, 0)], False, True),
+    (2, {}, [(0, 0), (0, 7)], False, True),
+    (4, {"H": 7}, [(0, 0), (0, 6)], False, True),
+    (3, {}, [(0, 0), (0, 39)], False, False),
+    (5, {}, [(0, 0), (1, 23)], True, False),
 ]
 
 
-@pytest.mark.parametrize("cid,kw,heads,repair,bound", CASES, ids=[f"config{c[0]}" for c in CASES])
-def test_accuracy_report(cid, kw, heads, repair, bound):
+def _case_id(c):
+    return f"config{c[0]}" + ("" if c[4] else "_north_star_4pct_not_met_method_on_zero_mean_v")
+
+
+@pytest.mark.parametrize("cid,kw,heads,repair,meets", CASES, ids=[_case_id(c) for c in CASES])
+def test_accuracy_report(cid, kw, heads, repair, meets):
     w = synth.workload(cid, **kw)
     q, k, v = (t.cuda() for t in synth.generate(w, "cpu"))
     rows = synth.sample_rows(w.S, min(ROWS, w.S)).numpy()
@@ -81,16 +91,21 @@ def test_accuracy_report(cid, kw, heads, repair, bound):
     plain = _errors(q, k, v, w, heads, rows, w.repair_budget, False)
     norep = _errors(q, k, v, w, heads, rows, 0.0, True) if repair else None
     for i, (b, h) in enumerate(heads):
-        e_s, ratio = smooth[i]
-        e_p = plain[i][0]
-        line = (f"{w.name} B={w.B} H={w.H} S={w.S} (b={b},h={h}): rel-L2 vs exact: V-Smooth {e_s:.3e}, "
-                f"plain E4M3 V {e_p:.3e}")
+        e_s, ratio, e_s_or = smooth[i]
+        e_p, _, e_p_or = plain[i]
+        line = (f"{w.name} B={w.B} H={w.H} S={w.S} (b={b},h={h}): rel-L2 vs exact: V-Smooth {e_s:.3e} "
+                f"(oracle {e_s_or:.3e}), plain E4M3 V {e_p:.3e} (oracle {e_p_or:.3e})")
         if norep is not None:
-            line += f", V-Smooth without repair {norep[i][0]:.3e}"
+            line += f", V-Smooth without repair {norep[i][0]:.3e} (oracle {norep[i][2]:.3e})"
         line += f"; residual energy ratio {ratio:.3f}"
         say(line)
-        assert e_s <= bound, line
         assert ratio > 0.0, line
+        if meets:
+            assert e_s <= TOL_EXACT, line
+        else:
+            # the miss is the method's: the oracle itself is above the target
+            assert e_s_or > TOL_EXACT, "labelled not met, but the oracle meets 4%: " + line
+            say(f"north_star 4%: not met ({w.name}, b={b}, h={h}): method {e_s_or:.3e}, GPU {e_s:.3e}")
         if norep is not None:
             # the repair adds back part of the residual's quantisation error;
             # it must not make the output measurably worse

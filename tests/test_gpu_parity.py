@@ -19,11 +19,19 @@ from oracle import vc_oracle as O
 pytestmark = pytest.mark.gpu
 
 TOL_ORACLE = 5e-3
+# every query row on its own, relative L2 against the oracle's row: a head can
+# meet the per-head bound with one 16-query sub-tile far off (at S=4096 a
+# 5% error in 16 rows adds only ~0.3% to the head's norm)
+TOL_ROW = 2e-2
+# the accuracy target against exact fp64 attention
 TOL_EXACT = 0.04
-# Zero-mean V (no channel offset) makes the output a small average of noise
-# (|out| ~ 2% of |v|), and then E4M3 Q, K, V and ExpCast each cost ~2.5-3%
-# relative error in the oracle itself; such cases get a gross-error bound.
-TOL_EXACT_ZERO_MEAN_V = 0.08
+# The kernel must add nothing to the method's own error: its rel-L2 against
+# exact attention is at most 1.02x the oracle's on the same rows plus 1e-3.
+# Where the oracle itself (the method) is above 4% on a case's rows -- zero-
+# mean V makes the output a small average of noise (|out| ~ 2% of |v|) and
+# E4M3 Q, K, V and ExpCast then cost ~2.5-3% each -- the 4% target is
+# reported as not met for that case instead of being gated.
+EXACT_RATIO, EXACT_SLACK = 1.02, 1e-3
 
 
 def say(msg):
@@ -51,13 +59,12 @@ TR_IDX = _tr_tile_index()
 
 
 def _mxfp4_tile_index():
-    """Byte, nibble shift and scale byte of (key j, channel d) in an MXFP4 tile
-    slot, from the layout documented with the C ABI."""
+    """Byte, nibble shift and scale byte of (position j, channel d) in an MXFP4
+    tile slot, from the layout documented with the C ABI: positions 32u..32u+31
+    form group u, position 32u + n is nibble n of lane group u."""
     j = np.arange(128)[:, None]
     d = np.arange(128)[None, :]
-    kb = 32 * ((j % 16) // 4) + 4 * (j // 16) + j % 4
-    u = kb // 64 + 2 * (((kb % 64) // 16) % 2)
-    n = 16 * ((kb % 64) // 32) + kb % 16
+    u, n = j // 32, j % 32
     lane = u * 16 + d % 16
     byte = ((d // 16) * 64 + lane) * 16 + n // 2
     shift = 4 * (n % 2)
@@ -65,6 +72,22 @@ def _mxfp4_tile_index():
     dd = np.arange(128)[:, None, None]
     sbyte = (8192 + (uu * 16 + dd % 16) * 8 + dd // 16)[:, :, 0]        # [d, u]
     return byte, shift, sbyte
+
+
+def _mx_row_of_position():
+    """Row of a k8 tile that holds permuted position p in an MXFP4 workspace:
+    the inverse of the documented mx(r) = 64(t/4) + 16g + 4(t%4) + i for row
+    r = 16t + 4g + i."""
+    r = np.arange(128)
+    t, g, i = r // 16, (r % 16) // 4, r % 4
+    pos = 64 * (t // 4) + 16 * g + 4 * (t % 4) + i
+    assert np.array_equal(np.sort(pos), np.arange(128))
+    row = np.empty(128, np.int64)
+    row[pos] = r
+    return row
+
+
+MX_ROW_OF_POS = _mx_row_of_position()
 
 
 MX_BYTE, MX_SHIFT, MX_SBYTE = _mxfp4_tile_index()
@@ -161,8 +184,17 @@ def _np(t):
 
 
 def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0.0, rows=None, heads=None,
-                         sm_scale=0.0, name="", exact_tol=TOL_EXACT, v_format="e4m3"):
-    """Run the GPU path and compare every prepared product and the output with the oracle."""
+                         sm_scale=0.0, name="", north_star_met=None, v_format="e4m3"):
+    """Run the GPU path and compare every prepared product and the output with the oracle.
+
+    Output gates per head: rel-L2 vs the oracle <= TOL_ORACLE, every row's
+    rel-L2 vs the oracle's row <= TOL_ROW, and rel-L2 vs exact fp64 attention
+    <= EXACT_RATIO x the oracle's own + EXACT_SLACK.  The 4% target vs exact
+    is gated on every head where the oracle meets it; a head where the oracle
+    itself is above it is a miss of the method, listed in run.north_star_misses.
+    north_star_met=True asserts there is no such miss, False that the case
+    does miss (so a case labelled "not met" is one where the method is above
+    4%), None reports only."""
     say(f"{name}: shape={tuple(q.shape)} dtype={q.dtype} smooth={smooth} k={kc} T={iters} beta={beta} "
         f"v_format={v_format}")
     fmt = vc.VC_V_MXFP4 if v_format == "mxfp4" else vc.VC_V_E4M3
@@ -172,7 +204,7 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
     q4, k4, v4, o4 = (t if t.dim() == 4 else t[None] for t in (q, k, v, run.out))
     sm = O.DEFAULT_SM_SCALE if sm_scale == 0.0 else np.float32(sm_scale)
     heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    errs, errs_ex = [], []
+    errs, errs_ex, errs_or_ex, row_errs, misses = [], [], [], [], []
     for (b, h) in heads:
         bh = b * H + h
         qn, kn, vn = (_np(t[b, :, h]) for t in (q4, k4, v4))     # this head only, as float64
@@ -187,18 +219,22 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
         assert np.array_equal(gv["q8"][:S], hq.q8), tag + " q8"
         assert not gv["q8"][S:].any(), tag + " q8 padding"
         assert np.array_equal(gv["q_scale"], hq.q_scale), tag + " q_scale"
-        assert np.array_equal(gv["k8"][:S], hq.k8), tag + " k8"
+        k8 = gv["k8"]
+        if v_format == "mxfp4":
+            # rows relabelled so every FP4 lane group holds one 32-position group
+            k8 = k8.reshape(nb, 128, 128)[:, MX_ROW_OF_POS].reshape(nb * 128, 128)
+        assert np.array_equal(k8[:S], hq.k8), tag + " k8"
+        assert not k8[S:].any(), tag + " k8 padding"
         assert np.array_equal(gv["k_scale"], hq.k_scale), tag + " k_scale"
         if v_format == "mxfp4":
             codes, expo = unpack_mxfp4(run.head_region("v8", torch.uint8, nb * 16384, bh), nb)
             assert np.array_equal(codes[:S], hv.v4), tag + " E2M1 codes"
             assert not codes[S:].any(), tag + " E2M1 padding"
             # groups with no real key (past S in the last tile) carry no defined scale
-            grp = O.mx_group_of_key(np.arange(128))
             last_real = S - 128 * (nb - 1)
             live = np.ones((nb, 128, 4), bool)
             for u in range(4):
-                live[nb - 1, :, u] = np.any(grp[:last_real] == u)
+                live[nb - 1, :, u] = 32 * u < last_real
             assert np.array_equal(expo[live], hv.v4_exp[live]), tag + " E8M0 scales"
         else:
             assert np.array_equal(gv["v8"][:S], hv.v8), tag + " v8"
@@ -221,14 +257,33 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
         got = o4[b, :, h].float().cpu().numpy()[r].astype(np.float64)
         assert np.all(np.isfinite(got)), tag + " non-finite output"
         e = O.rel_l2(got, ref)
+        row_e = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
         ex = O.attention_exact(qn, kn, vn, sm_scale=sm, rows=r)
         e_ex = O.rel_l2(got, ex)
+        e_or_ex = O.rel_l2(ref, ex)
         errs.append(e)
         errs_ex.append(e_ex)
+        errs_or_ex.append(e_or_ex)
+        row_errs.append(float(row_e.max()))
         assert e <= TOL_ORACLE, f"{tag}: rel-L2 vs oracle {e:.3e}"
-        assert e_ex <= exact_tol, f"{tag}: rel-L2 vs exact {e_ex:.3e}"
-    say(f"{name}: max rel-L2 vs oracle {max(errs):.3e}, vs exact fp64 {max(errs_ex):.3e}")
+        assert row_e.max() <= TOL_ROW, f"{tag}: row {int(r[np.argmax(row_e)])} rel-L2 vs oracle {row_e.max():.3e}"
+        assert e_ex <= EXACT_RATIO * e_or_ex + EXACT_SLACK, \
+            f"{tag}: rel-L2 vs exact {e_ex:.3e}, the oracle's own {e_or_ex:.3e}"
+        if e_or_ex <= TOL_EXACT:
+            assert e_ex <= TOL_EXACT, f"{tag}: rel-L2 vs exact {e_ex:.3e} (oracle {e_or_ex:.3e})"
+        else:
+            misses.append((tag, e_ex, e_or_ex))
+    say(f"{name}: max rel-L2 vs oracle {max(errs):.3e} (worst row {max(row_errs):.3e}), vs exact fp64 "
+        f"{max(errs_ex):.3e} (oracle's own {max(errs_or_ex):.3e})")
+    for tag, e_ex, e_or_ex in misses:
+        say(f"{tag}: 4% target vs exact not met by the method: GPU {e_ex:.3e}, oracle {e_or_ex:.3e}")
+    if north_star_met is True:
+        assert not misses, f"{name}: the 4% target is missed: {misses}"
+    elif north_star_met is False:
+        assert misses, f"{name}: labelled 4% not met, but every head meets it"
     run.err_exact = errs_ex
+    run.err_oracle_exact = errs_or_ex
+    run.north_star_misses = misses
     return run
 
 
@@ -279,10 +334,8 @@ def test_plain_and_smooth_on_outliers(smooth):
 @pytest.mark.parametrize("beta", [0.005, 0.05])
 def test_repair(beta):
     w, q, k, v = _cfg(5, B=2, H=2, S=2048)
-    run = check_against_oracle(q, k, v, kc=8, iters=3, beta=beta, name=f"repair beta={beta}",
-                               exact_tol=TOL_EXACT_ZERO_MEAN_V)
-    base = check_against_oracle(q, k, v, kc=8, iters=3, beta=0.0, name="repair baseline beta=0",
-                                exact_tol=TOL_EXACT_ZERO_MEAN_V)
+    run = check_against_oracle(q, k, v, kc=8, iters=3, beta=beta, name=f"repair beta={beta}")
+    base = check_against_oracle(q, k, v, kc=8, iters=3, beta=0.0, name="repair baseline beta=0")
     # re-adding the worst-rounded tokens' residual lowers the error vs exact attention
     assert np.mean(run.err_exact) < np.mean(base.err_exact)
 
@@ -303,7 +356,7 @@ def test_repair_select_edges(S, beta, dups):
         v = v[:, torch.randint(0, 50, (S,), generator=g)]
     v = v.to(torch.bfloat16)
     check_against_oracle(q.cuda(), k.cuda(), v.cuda(), kc=4, iters=2, beta=beta, name=f"repair edges S={S} beta={beta}",
-                         rows=np.arange(0, S, max(1, S // 64)), exact_tol=TOL_EXACT_ZERO_MEAN_V)
+                         rows=np.arange(0, S, max(1, S // 64)))
 
 
 def test_strided_views_and_3d_input():
@@ -312,7 +365,7 @@ def test_strided_views_and_3d_input():
     big = torch.randn(S, H, 3, 128, generator=g).to(torch.bfloat16).cuda()   # packed qkv
     q, k, v = big[:, :, 0], big[:, :, 1], big[:, :, 2]                        # [S,H,128] strided views
     assert not q.is_contiguous()
-    run = check_against_oracle(q, k, v, kc=4, iters=2, name="strided 3d", exact_tol=TOL_EXACT_ZERO_MEAN_V)
+    run = check_against_oracle(q, k, v, kc=4, iters=2, name="strided 3d")
     # output into a strided buffer gives the same bytes
     out2 = torch.zeros(S, H, 2, 128, dtype=torch.bfloat16, device="cuda")[:, :, 1]
     opts = vc.v_opts(True, 4, 2)
@@ -352,8 +405,7 @@ def test_zero_value_head_and_zero_blocks():
     v[:, :, 0] = 0                      # all-zero V head
     q[:, 128:256] = 0                   # all-zero Q block
     k[:, 0:128, 1] = 0                  # zero K rows (join whichever permuted block they land in)
-    check_against_oracle(q.cuda(), k.cuda(), v.cuda(), kc=3, iters=2, name="zero head/blocks",
-                         exact_tol=TOL_EXACT_ZERO_MEAN_V)
+    check_against_oracle(q.cuda(), k.cuda(), v.cuda(), kc=3, iters=2, name="zero head/blocks")
 
 
 @pytest.mark.parametrize("v_format", ["e4m3", "mxfp4"])
@@ -383,8 +435,7 @@ def test_steep_maximum_rises(v_format, smooth):
     # 4-bit residual.  The oracle parity (5e-3) is the gate here; the exact
     # envelope only catches gross errors.
     check_against_oracle(q.to(torch.bfloat16).cuda(), k.to(torch.bfloat16).cuda(), v.to(torch.bfloat16).cuda(),
-                         smooth=smooth, kc=4, iters=2, name=f"steep rises {v_format} smooth={smooth}",
-                         exact_tol=TOL_EXACT_ZERO_MEAN_V if v_format == "e4m3" else 0.15, v_format=v_format)
+                         smooth=smooth, kc=4, iters=2, name=f"steep rises {v_format} smooth={smooth}", v_format=v_format)
 
 
 # ---- 4-bit residual (MXFP4) ---------------------------------------------------
@@ -392,8 +443,7 @@ def test_steep_maximum_rises(v_format, smooth):
 # exact attention on config 2), so its runs get the gross-error envelope.
 def test_mxfp4_config2():
     w, q, k, v = _cfg(2)
-    check_against_oracle(q, k, v, kc=w.k, iters=w.iters, name="config2 mxfp4", v_format="mxfp4",
-                         exact_tol=TOL_EXACT_ZERO_MEAN_V)
+    check_against_oracle(q, k, v, kc=w.k, iters=w.iters, name="config2 mxfp4", v_format="mxfp4")
 
 
 @pytest.mark.parametrize("S", [1, 129, 1000])
@@ -404,15 +454,13 @@ def test_mxfp4_ragged(S, dtype):
     q = torch.randn(B, S, H, 128, generator=g).to(dtype).cuda()
     k = (1.5 * torch.randn(B, S, H, 128, generator=g)).to(dtype).cuda()
     v = (torch.randn(B, S, H, 128, generator=g) + 3 * torch.randn(B, 1, H, 128, generator=g)).to(dtype).cuda()
-    check_against_oracle(q, k, v, kc=min(5, S), iters=3, name=f"mxfp4 ragged S={S} {dtype}",
-                         exact_tol=TOL_EXACT_ZERO_MEAN_V, v_format="mxfp4")
+    check_against_oracle(q, k, v, kc=min(5, S), iters=3, name=f"mxfp4 ragged S={S} {dtype}", v_format="mxfp4")
 
 
 def test_mxfp4_smooth_off_and_zero_head():
     w, q, k, v = _cfg(2, H=2, S=700)
     v[:, :, 1] = 0                      # an all-zero head: scales 2^0, codes 0
-    check_against_oracle(q, k, v, smooth=False, kc=4, iters=2, name="mxfp4 smooth=0", v_format="mxfp4",
-                         exact_tol=TOL_EXACT_ZERO_MEAN_V)
+    check_against_oracle(q, k, v, smooth=False, kc=4, iters=2, name="mxfp4 smooth=0", v_format="mxfp4")
 
 
 def test_mxfp4_rejects_repair():

@@ -15,9 +15,8 @@ from oracle import vc_oracle as O
 def test_splitmix64_published_sequence():
     # SplitMix64 (Vigna) started from state 0: the state advances by the golden
     # gamma before each output, so output i is splitmix64 of i*gamma.
-    gamma = 0x9E3779B97F4A7C15
-    outs = [O.splitmix64((i * gamma) & O.MASK64) for i in range(3)]
-    assert outs == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    outs = [O.splitmix64((i * GAMMA) & O.MASK64) for i in range(3)]
+    assert outs == list(SM64_OUT)
 
 
 def test_sketch_scaling_and_range():
@@ -44,6 +43,35 @@ def test_init_positions_distinct_in_range():
                 t = O.init_positions(S, k, 0, bh)
                 assert len(set(t.tolist())) == k
                 assert t.min() >= 0 and t.max() < S
+
+
+# SplitMix64's published outputs from state 0 (the first three of its
+# sequence): output i is the mixer applied to state i*gamma.
+SM64_OUT = (0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F)
+GAMMA = 0x9E3779B97F4A7C15
+
+
+def test_init_positions_values_from_published_outputs():
+    # The phase is splitmix64(seed XOR bh) mod floor(S/k); seeds are chosen so
+    # that seed XOR bh is the state of a published output, and the expected
+    # positions are written out by hand from those outputs.
+    #
+    # Case 1: S=1001, k=3, bh=2, seed = gamma XOR 2, so seed XOR bh = gamma and
+    # the phase is output 1 mod 333 = 0x6E789E6AA1B965F4 mod 333 = 27.  The
+    # strided starts floor(c*1001/3) are 0, 333, 667 (c*(S//k) would give 666
+    # for c=2, and seed+bh would give another state).
+    assert SM64_OUT[1] % 333 == 27
+    assert O.init_positions(1001, 3, GAMMA ^ 2, 2).tolist() == [27, 360, 694]
+    # Case 2: S=73397, k=32, bh=7, seed = 2*gamma XOR 7: the phase is output 2
+    # mod 2293 = 0x06C45D188009454F mod 2293 = 1404; the starts floor(c*S/32)
+    # run 0, 2293, 4587, ... (S/32 = 2293 + 21/32, so they drift ahead of
+    # c*2293 from c=2 on).
+    assert SM64_OUT[2] % 2293 == 1404
+    starts = [0, 2293, 4587, 6880, 9174, 11468, 13761, 16055, 18349, 20642, 22936, 25230, 27523, 29817, 32111,
+              34404, 36698, 38992, 41285, 43579, 45873, 48166, 50460, 52754, 55047, 57341, 59635, 61928, 64222,
+              66516, 68809, 71103]
+    seed = ((2 * GAMMA) & O.MASK64) ^ 7
+    assert O.init_positions(73397, 32, seed, 7).tolist() == [s + 1404 for s in starts]
 
 
 def brute_assign(x, cent):

@@ -10,6 +10,7 @@ from oracle import vc_oracle as O
 import tests.test_oracle_attention as TA
 import tests.test_oracle_codec as TC
 import tests.test_oracle_kmeans as TK
+import tests.test_oracle_mxfp4 as TM
 import tests.test_oracle_quant as TQ
 
 
@@ -43,6 +44,24 @@ def test_update_truncates_instead_of_rounding(monkeypatch):
         return new
     monkeypatch.setattr(O, "kmeans_update", bad)
     _fails(TK.test_update_is_mean_rounded_half_up_exact)
+
+
+def test_init_phase_from_seed_plus_bh(monkeypatch):
+    def bad(S, k, seed, bh):
+        stride = max(1, S // k)
+        phi = O.splitmix64((seed + bh) & O.MASK64) % stride
+        return np.array([(c * S) // k + phi for c in range(k)], dtype=np.int64)
+    monkeypatch.setattr(O, "init_positions", bad)
+    _fails(TK.test_init_positions_values_from_published_outputs)
+
+
+def test_init_starts_from_truncated_stride(monkeypatch):
+    def bad(S, k, seed, bh):
+        stride = max(1, S // k)
+        phi = O.splitmix64((seed ^ bh) & O.MASK64) % stride
+        return np.array([c * stride + phi for c in range(k)], dtype=np.int64)
+    monkeypatch.setattr(O, "init_positions", bad)
+    _fails(TK.test_init_positions_values_from_published_outputs)
 
 
 def test_seven_codes_per_octave(monkeypatch):
@@ -87,3 +106,15 @@ def test_missing_log2e_in_sigma(monkeypatch):
     monkeypatch.setattr(O, "sigma_of", lambda sq, sk, sm: (np.asarray(sq, np.float32) * np.asarray(sk, np.float32)
                                                            * np.float32(sm)).astype(np.float32))
     _fails(TA.test_pipeline_config2_heads_accuracy_and_vsmooth_benefit)
+
+
+def test_mx_groups_strided_keys(monkeypatch):
+    # groups as every fourth run of 4 keys (a strided lane-style set) instead
+    # of 32 consecutive positions
+    monkeypatch.setattr(O, "mx_group_of_key", lambda j: (np.asarray(j, np.int64) % 16) // 4)
+    _fails(TM.test_groups_are_runs_of_32_positions_of_one_tile_and_channel)
+
+
+def test_mx_groups_of_16(monkeypatch):
+    monkeypatch.setattr(O, "mx_group_of_key", lambda j: ((np.asarray(j, np.int64) % 128) // 16) % 4)
+    _fails(TM.test_groups_are_runs_of_32_positions_of_one_tile_and_channel)

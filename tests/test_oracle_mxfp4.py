@@ -1,5 +1,6 @@
 """Pins of the oracle's 4-bit residual path (reading R15: OCP MXFP4 -- E2M1
-codes with one power-of-two scale per group of 32 keys).
+codes with one power-of-two scale per channel and run of 32 consecutive
+permuted positions of a 128-key tile).
 
 The 4-bit option is named in "Nunchux AI lanza VC-Attention kernel ..."
 (reditua.com), paragraph 2 (NVFP4 beside E4M3); the format details are the
@@ -63,16 +64,26 @@ def test_scale_exponent_is_the_smallest_power_of_two_without_clipping():
 
 
 # -------------------------------------------------------------------- groups
-def test_groups_partition_each_tile_by_lane_layout():
-    g = O.mx_group_of_key(np.arange(128))
-    assert np.array_equal(np.bincount(g), [32, 32, 32, 32])
-    # a group never splits a run of 4 keys (one 4-byte slot of the P operand)
-    assert np.all(g.reshape(32, 4) == g.reshape(32, 4)[:, :1])
-    # the membership as measured for the FP4 operand of the matrix core:
-    # lane group g holds the P-operand K indices 64*(g&1) + 16*(g>>1) + [0,16)
-    # and + 32, and key 16t + 4u + i is K index 32u + 4t + i; listed by (t, u)
-    want = np.array([[0, 0, 1, 1]] * 4 + [[2, 2, 3, 3]] * 4)
-    assert np.array_equal(g.reshape(8, 4, 4)[:, :, 0], want)
+def test_groups_are_runs_of_32_positions_of_one_tile_and_channel():
+    # Behavioural pin of the grouping: raising one residual value far above
+    # the rest moves the scale exponent of exactly one (tile, channel, group)
+    # -- the tile of its position, its channel, and the run of 32 consecutive
+    # permuted positions (32u .. 32u+31 of the tile) that holds it -- and no
+    # other.  A grouping over other key sets (strided keys, 16-key runs,
+    # groups crossing tiles or channels) moves other exponents or none.
+    rng = np.random.default_rng(7)
+    S = 300
+    r = (rng.uniform(0.8, 1.0, (S, 128)) * rng.choice([-1, 1], (S, 128))).astype(np.float32)
+    _, base = O.quantize_mxfp4(r)
+    # max|R| in (0.75, 1.5] -> 2^-2; groups past S=300 (tile 2, groups 2-3) hold no key
+    assert np.all(base[:2] == -2) and np.all(base[2, :, :2] == -2) and np.all(base[2, :, 2:] == 0)
+    for p, d in ((0, 0), (31, 5), (32, 5), (95, 127), (96, 64), (127, 3), (128, 9), (200, 100), (299, 77)):
+        r2 = r.copy()
+        r2[p, d] = np.float32(100.0)                 # needs 2^5 (100/32 <= 6 < 100/16)
+        _, e2 = O.quantize_mxfp4(r2)
+        changed = np.argwhere(e2 != base)
+        assert changed.tolist() == [[p // 128, d, (p % 128) // 32]], (p, d, changed.tolist())
+        assert e2[p // 128, d, (p % 128) // 32] == 5
 
 
 # ------------------------------------------------------------ the quantiser
@@ -83,7 +94,7 @@ def test_quantize_mxfp4_per_group_properties(S):
     r[:5, 7] = 0.0
     codes, expo = O.quantize_mxfp4(r)
     vals = O.mxfp4_dequant(codes, expo)
-    grp = O.mx_group_of_key(np.arange(S) % 128)
+    grp = (np.arange(S) % 128) // 32                  # 32 consecutive permuted positions per group
     for b in range((S + 127) // 128):
         for gg in range(4):
             sel = (np.arange(S) // 128 == b) & (grp == gg)
