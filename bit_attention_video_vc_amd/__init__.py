@@ -8,6 +8,7 @@ the library; the first call does, and raises if it has not been built.
 Entry points (same names as the C ABI):
   vc_workspace_layout(v_like, opts)                 -> VcWsLayout
   vc_prepare_v(v, opts, ws)
+  vc_prepare_v_noalloc(v, opts, ws)                 (scratch in a static device array)
   vc_prepare_qk(q, k, opts, ws)
   vc_attention_fwd(out, opts, ws, sm_scale=0.0)
 plus the convenience ``attention(q, k, v, ...)`` that runs all three.
@@ -23,7 +24,8 @@ import torch
 __all__ = [
     "VcDesc", "VcVOpts", "VcAttnOpts", "VcWsLayout", "VcHeadHdr", "VCError", "lib", "lib_path",
     "ablation_exp_lib_path", "use_library",
-    "v_opts", "VC_V_E4M3", "VC_V_MXFP4", "desc_of", "vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd",
+    "v_opts", "VC_V_E4M3", "VC_V_MXFP4", "desc_of", "vc_workspace_layout", "vc_prepare_v", "vc_prepare_v_noalloc",
+    "vc_prepare_qk", "vc_attention_fwd", "NOALLOC_SCRATCH_BYTES",
     "alloc_workspace", "attention", "EXPORTS",
 ]
 
@@ -36,8 +38,10 @@ VC_OK, VC_ERR_ARG, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_DEVICE = range(5
 VC_F16, VC_BF16 = 0, 1
 
 # symbols the header declares (checked by the ABI tests)
-EXPORTS = ("vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd",
+EXPORTS = ("vc_workspace_layout", "vc_prepare_v", "vc_prepare_v_noalloc", "vc_prepare_qk", "vc_attention_fwd",
            "vc_status_string", "vc_last_error", "vc_version")
+# bytes of the static scratch array behind vc_prepare_v_noalloc (vc.h)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class VcDesc(ctypes.Structure):
@@ -90,11 +94,12 @@ def lib() -> ctypes.CDLL:
         L.vc_workspace_layout.argtypes = [P(VcDesc), P(VcVOpts), P(VcWsLayout)]
         L.vc_prepare_v.argtypes = [P(VcDesc), ctypes.c_void_p, P(VcVOpts), ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_void_p]
+        L.vc_prepare_v_noalloc.argtypes = L.vc_prepare_v.argtypes
         L.vc_prepare_qk.argtypes = [P(VcDesc), ctypes.c_void_p, P(VcDesc), ctypes.c_void_p, P(VcVOpts),
                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.vc_attention_fwd.argtypes = [P(VcDesc), ctypes.c_void_p, P(VcVOpts), P(VcAttnOpts), ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p]
-        for f in ("vc_workspace_layout", "vc_prepare_v", "vc_prepare_qk", "vc_attention_fwd"):
+        for f in ("vc_workspace_layout", "vc_prepare_v", "vc_prepare_v_noalloc", "vc_prepare_qk", "vc_attention_fwd"):
             getattr(L, f).restype = ctypes.c_int
         L.vc_status_string.argtypes = [ctypes.c_int]
         for f in ("vc_status_string", "vc_last_error", "vc_version"):
@@ -185,6 +190,16 @@ def vc_prepare_v(v: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, stream=None) 
     with torch.cuda.device(dev):
         _check(lib().vc_prepare_v(ctypes.byref(d), ctypes.c_void_p(v.data_ptr()), ctypes.byref(opts),
                                   ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(stream, dev)))
+
+
+def vc_prepare_v_noalloc(v: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, stream=None) -> None:
+    """vc_prepare_v with its scratch in the library's static device array;
+    `ws` needs only layout.scratch bytes."""
+    dev = _device_of(v=v, ws=ws)
+    d, nbytes = desc_of(v), _ws_bytes(ws)
+    with torch.cuda.device(dev):
+        _check(lib().vc_prepare_v_noalloc(ctypes.byref(d), ctypes.c_void_p(v.data_ptr()), ctypes.byref(opts),
+                                          ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(stream, dev)))
 
 
 def vc_prepare_qk(q: torch.Tensor, k: torch.Tensor, opts: VcVOpts, ws: torch.Tensor, stream=None) -> None:

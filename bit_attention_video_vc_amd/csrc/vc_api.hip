@@ -120,11 +120,12 @@ vc_status make_plan(const vc_desc* vd, const vc_v_opts* o, Plan* p) {
   return VC_OK;
 }
 
-vc_status check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+// `need`: the bytes a call touches -- the whole layout for vc_prepare_v, the
+// regions before the scratch region for every other call.
+vc_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
   if (!ws) return fail(VC_ERR_ARG, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(VC_ERR_ARG, "workspace must be 256-byte aligned");
-  if (ws_bytes < p.lay.total)
-    return fail(VC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.lay.total);
+  if (ws_bytes < need) return fail(VC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   return VC_OK;
 }
 
@@ -134,10 +135,12 @@ vc_status check_ptr(const void* ptr, const char* name) {
   return VC_OK;
 }
 
-vc::WsPtrs ws_ptrs(const Plan& p, void* ws) {
+// Typed pointers into a workspace; the scratch region is at `scr` (the
+// workspace's own scratch region unless given).
+vc::WsPtrs ws_ptrs(const Plan& p, void* ws, uint8_t* scr = nullptr) {
   uint8_t* base = static_cast<uint8_t*>(ws);
   const vc_ws_layout& L = p.lay;
-  uint8_t* scr = base + L.scratch;
+  if (!scr) scr = base + L.scratch;
   vc::WsPtrs w;
   w.q8 = base + L.q8;
   w.k8 = base + L.k8;
@@ -210,6 +213,35 @@ vc_status check_device() {
 
 bool same_shape(const vc_desc* a, const vc_desc* b) { return a->B == b->B && a->S == b->S && a->H == b->H; }
 
+// The scratch of vc_prepare_v_noalloc: a file-scope device array, one copy per
+// GPU (each at its own address), held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in):
+// the device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and kept per device.
+static __device__ __align__(256) uint8_t scratch[VC_NOALLOC_SCRATCH_BYTES];
+std::once_flag g_scr_once[kMaxDev];
+uint8_t* g_scr_ptr[kMaxDev];
+hipError_t g_scr_err[kMaxDev];
+
+// Device address of this device's copy (check_device has validated the
+// current device index).
+vc_status static_scratch(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VC_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  std::call_once(g_scr_once[dev], [dev]() {
+    void* ptr = nullptr;
+    g_scr_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scr_ptr[dev] = static_cast<uint8_t*>(ptr);
+  });
+  if (g_scr_err[dev] != hipSuccess)
+    return fail(VC_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(g_scr_err[dev]));
+  if (!g_scr_ptr[dev] || reinterpret_cast<uintptr_t>(g_scr_ptr[dev]) % 256)
+    return fail(VC_ERR_DEVICE, "static scratch has no 256-byte aligned device address");
+  *out = g_scr_ptr[dev];
+  return VC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,9 +281,29 @@ vc_status vc_prepare_v(const vc_desc* vd, const void* v, const vc_v_opts* opts, 
   vc_status s = make_plan(vd, opts, &p);
   if (s != VC_OK) return s;
   if ((s = check_ptr(v, "v")) != VC_OK) return s;
-  if ((s = check_ws(p, ws, ws_bytes)) != VC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, p.lay.total)) != VC_OK) return s;
   if ((s = check_device()) != VC_OK) return s;
   const hipError_t e = vc::launch_prepare_v(targ(vd, v), p.B, p.S, p.H, *opts, ws_ptrs(p, ws),
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VC_ERR_DEVICE, "prepare_v launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+vc_status vc_prepare_v_noalloc(const vc_desc* vd, const void* v, const vc_v_opts* opts, void* ws, size_t ws_bytes,
+                               void* stream) {
+  Plan p;
+  vc_status s = make_plan(vd, opts, &p);
+  if (s != VC_OK) return s;
+  if ((s = check_ptr(v, "v")) != VC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, p.lay.scratch)) != VC_OK) return s;
+  const size_t need = p.lay.total - p.lay.scratch;
+  if (need > VC_NOALLOC_SCRATCH_BYTES)
+    return fail(VC_ERR_UNSUPPORTED, "this shape needs %zu bytes of scratch, the static array holds %zu", need,
+                static_cast<size_t>(VC_NOALLOC_SCRATCH_BYTES));
+  if ((s = check_device()) != VC_OK) return s;
+  uint8_t* scr = nullptr;
+  if ((s = static_scratch(&scr)) != VC_OK) return s;
+  const hipError_t e = vc::launch_prepare_v(targ(vd, v), p.B, p.S, p.H, *opts, ws_ptrs(p, ws, scr),
                                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(VC_ERR_DEVICE, "prepare_v launch: %s", hipGetErrorString(e));
   return ok();
@@ -267,7 +319,7 @@ vc_status vc_prepare_qk(const vc_desc* qd, const void* q, const vc_desc* kd, con
   if ((s = make_plan(kd, opts, &p)) != VC_OK) return s;
   if ((s = check_ptr(q, "q")) != VC_OK) return s;
   if ((s = check_ptr(k, "k")) != VC_OK) return s;
-  if ((s = check_ws(p, ws, ws_bytes)) != VC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, p.lay.scratch)) != VC_OK) return s;
   if ((s = check_device()) != VC_OK) return s;
   const hipError_t e = vc::launch_prepare_qk(targ(qd, q), targ(kd, k), p.B, p.S, p.H, opts->v_format, ws_ptrs(p, ws),
                                              static_cast<hipStream_t>(stream));
@@ -283,7 +335,7 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   Plan p;
   if ((s = make_plan(od, opts, &p)) != VC_OK) return s;
   if ((s = check_ptr(out, "out")) != VC_OK) return s;
-  if ((s = check_ws(p, ws, ws_bytes)) != VC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, p.lay.scratch)) != VC_OK) return s;
   float sm = aopts ? aopts->sm_scale : 0.0f;
   if (!(sm >= 0.0f) || std::isinf(sm)) return fail(VC_ERR_ARG, "sm_scale must be finite and >= 0");
   if (sm == 0.0f) sm = static_cast<float>(1.0 / std::sqrt(128.0));

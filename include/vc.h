@@ -26,7 +26,9 @@
  * owned by the caller; the library never allocates or frees device memory
  * and keeps no state between calls.  All intermediate results live in one
  * caller-provided workspace whose size and internal offsets come from
- * vc_workspace_layout (a host-only computation).  Descriptors and option
+ * vc_workspace_layout (a host-only computation): vc_prepare_v needs
+ * layout.total bytes, the other calls read only the regions before the
+ * scratch region and need layout.scratch bytes.  Descriptors and option
  * structs are host memory, read during the call only.
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
@@ -183,6 +185,23 @@ vc_status vc_workspace_layout(const vc_desc* vd, const vc_v_opts* opts, vc_ws_la
  * Writes assign, perm, v8, v_mean, v_muop, hdr and the repair set. */
 vc_status vc_prepare_v(const vc_desc* vd, const void* v, const vc_v_opts* opts,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free V prepare, for callers that cannot allocate device memory
+ * (code being recorded into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as vc_prepare_v, but the
+ * internal scratch (k-means centroids and sums, sort counters, repair
+ * scores: layout.total - layout.scratch bytes) is a static device array of
+ * VC_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, so `ws` needs only layout.scratch bytes -- the
+ * prepared products, which is all vc_prepare_qk and vc_attention_fwd read.
+ * Returns VC_ERR_UNSUPPORTED when the shape needs more scratch than the
+ * array holds.  Calls no hipMalloc or hipFree.  Every call on one GPU shares
+ * that GPU's array and each call initialises the parts it reads: calls that
+ * overlap on one GPU (other streams or threads) race, so the caller
+ * serialises them. */
+#define VC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+vc_status vc_prepare_v_noalloc(const vc_desc* vd, const void* v, const vc_v_opts* opts, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* Q/K prepare ("Open VC Attention", Description: per-block Q/K scales).
  * Q is quantised in its original order; K is gathered through perm (written
