@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--ablation-exp", action="store_true",
                     help="also time the attention kernel of libvc_ablation_exp.so (FP32 exponential + E4M3 cast "
                          "instead of ExpCast) on the same prepared workspace")
+    ap.add_argument("--library", choices=["main", "ablation-exp"], default="main",
+                    help="run every call through libvc.so (the default) or through the measurement build "
+                         "libvc_ablation_exp.so (FP32 exponential + E4M3 cast in place of ExpCast), e.g. to "
+                         "collect its instruction counters")
     ap.add_argument("--graph", action="store_true",
                     help="also capture the full call once into a HIP graph (the library allocates, clears and "
                          "synchronises nothing, so it captures as is) and time its replays")
@@ -150,6 +154,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.library == "ablation-exp":
+        vc.use_library(vc.ablation_exp_lib_path)
+        log(f"library: {vc.lib().vc_version().decode()} (measurement build, not the method)")
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

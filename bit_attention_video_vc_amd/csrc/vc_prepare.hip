@@ -406,13 +406,18 @@ __global__ void k_identity_perm(int S, int32_t* assign, int32_t* perm) {
 }
 
 // Block means over permuted positions and the residual amax per head.
-// mu = fp32(fp64(sum) / n), the sum in position order; R = fp32(v - mu).
-// The block's gathered rows are read once, 16 bytes per load, into LDS.
-// grid (nblk, H, B), 256 threads.
+// mu = fp32(fp64(sum) / n); R = fp32(v - mu).  The block's gathered rows are
+// read once, 16 bytes per load, into LDS.  Each channel's sum is split over
+// the two halves of the block and four accumulators per thread: the fp64 sum
+// of at most 128 fp16/bf16 values is exact while they span less than 2^38
+// (every fp16 tensor; bf16 values within 38 binades of each other), so any
+// order gives the same mu as the sequential sum.
+// grid (nblk, H, B), 256 threads: thread = (channel tid%128, half tid/128).
 __global__ void __launch_bounds__(256) k_v_block_stats(TensorArg v, int S, int smooth, const int32_t* perm,
                                                        float* v_mean, vc_head_hdr* hdr) {
   __shared__ uint4 rows[kBlock][kD / 8];      // raw 16-bit values of the block's rows
   __shared__ int32_t pp[kBlock];
+  __shared__ double part[2][kD];
   __shared__ float red[16];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x;
   const int tid = threadIdx.x;
@@ -426,25 +431,34 @@ __global__ void __launch_bounds__(256) k_v_block_stats(TensorArg v, int S, int s
                                                       static_cast<int64_t>(pp[j]) * v.sS + h * v.sH + c8);
   }
   __syncthreads();
-  float m = 0.0f;
-  if (tid < kD) {
-    const int d = tid;
-    const uint16_t* col = reinterpret_cast<const uint16_t*>(&rows[0][0]) + d;
-    float mu = 0.0f;
-    if (smooth) {
-      double sum = 0.0;
-      for (int j = 0; j < n; ++j) {
-        const uint32_t e = col[j * kD];
-        sum += static_cast<double>(v.dtype == VC_BF16 ? bf16_bits_to_f32(e) : f16_bits_to_f32(e));
+  const int d = tid & (kD - 1), half = tid >> 7;
+  const int j0 = half * (kBlock / 2), j1 = min(n, j0 + kBlock / 2);
+  const uint16_t* col = reinterpret_cast<const uint16_t*>(&rows[0][0]) + d;
+  const bool bf = v.dtype == VC_BF16;
+  if (smooth) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    int j = j0;
+    for (; j + 4 <= j1; j += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t e = col[(j + u) * kD];
+        acc[u] += static_cast<double>(bf ? bf16_bits_to_f32(e) : f16_bits_to_f32(e));
       }
-      mu = static_cast<float>(sum / static_cast<double>(n));
     }
-    v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + d] = mu;
-    for (int j = 0; j < n; ++j) {
+    for (; j < j1; ++j) {
       const uint32_t e = col[j * kD];
-      const float x = v.dtype == VC_BF16 ? bf16_bits_to_f32(e) : f16_bits_to_f32(e);
-      m = fmaxf(m, fabsf(x - mu));
+      acc[0] += static_cast<double>(bf ? bf16_bits_to_f32(e) : f16_bits_to_f32(e));
     }
+    part[half][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+  __syncthreads();
+  const float mu = smooth ? static_cast<float>((part[0][d] + part[1][d]) / static_cast<double>(n)) : 0.0f;
+  if (half == 0) v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + d] = mu;
+  float m = 0.0f;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t e = col[j * kD];
+    const float x = bf ? bf16_bits_to_f32(e) : f16_bits_to_f32(e);
+    m = fmaxf(m, fabsf(x - mu));
   }
   m = block_max(m, red);
   if (tid == 0 && m > 0.0f) atomicMax(&hdr[bh].r_amax_bits, __float_as_uint(m));
