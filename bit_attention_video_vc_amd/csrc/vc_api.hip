@@ -51,6 +51,7 @@ vc_status check_desc(const vc_desc* d, const char* name) {
 
 struct Plan {
   int B, S, H, k, nblk, nrep, nrep_pad;
+  vc::AttnSplit split;
   vc_ws_layout lay;
   vc::Scratch scr;
 };
@@ -111,6 +112,8 @@ vc_status make_plan(const vc_desc* vd, const vc_v_opts* o, Plan* p) {
   L.rep_k8 = take(static_cast<size_t>(BH) * p->nrep_pad * vc::kD);
   L.rep_ks = take(sizeof(float) * BH * p->nrep_pad);
   L.rep_e8 = take(static_cast<size_t>(BH) * p->nrep_pad * vc::kD);
+  p->split = vc::attn_split(BH, p->nblk, p->nrep);
+  L.attn_part = take(static_cast<size_t>(2) * p->split.tail_wg * vc::kPartBytes);
   p->scr = vc::scratch_layout(BH, p->S, p->k, p->nrep);
   L.scratch = take(p->scr.total);
   L.total = off;
@@ -339,7 +342,7 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   float sm = aopts ? aopts->sm_scale : 0.0f;
   if (!(sm >= 0.0f) || std::isinf(sm)) return fail(VC_ERR_ARG, "sm_scale must be finite and >= 0");
   if (sm == 0.0f) sm = static_cast<float>(1.0 / std::sqrt(128.0));
-  const int64_t total = static_cast<int64_t>(p.B) * p.H * ((p.nblk + 1) / 2);   // one workgroup per query-block pair
+  const int64_t total = p.split.whole + p.split.tail_wg;   // whole items, then the tail workgroups
   if (total > vc::kMaxAttnWorkgroups)
     return fail(VC_ERR_UNSUPPORTED, "B*H*ceil(S/256) = %lld exceeds %lld attention workgroups", (long long)total,
                 (long long)vc::kMaxAttnWorkgroups);
@@ -364,10 +367,16 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   a.H = p.H;
   a.nblk = p.nblk;
   a.nrep_pad = p.nrep_pad;
-  a.total_wg = static_cast<int>(total);
+  a.whole = static_cast<int>(p.split.whole);
+  vc::AttnTail tl;
+  tl.tail = p.split.tail;
+  tl.tail_wg = p.split.tail_wg;
+  tl.per = p.split.per;
+  tl.ngrp = p.split.ngrp;
+  tl.part = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(ws)) + p.lay.attn_part);
   a.sm_scale = sm;
   a.v_format = opts->v_format;
-  const hipError_t e = vc::launch_attention(a, p.B * p.H, static_cast<hipStream_t>(stream));
+  const hipError_t e = vc::launch_attention(a, tl, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(VC_ERR_DEVICE, "attention launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -632,7 +632,7 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane16, 
 template <int VF, int J>
 __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
                                           const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2], TileAcc& acc) {
-  const int nblk = c.nblk, last = nblk - 1, g = c.g;
+  const int nblk = c.nblk, last = nblk - 1, g = c.lane16 >> 8;   // lane group, from the kept 16*lane
   const StepCopies<VF> cp(c, kb + kStages + 1 < last ? kb + kStages + 1 : last,
                           kb + kStages - 1 < last ? kb + kStages - 1 : last, kb + kStages - 1, kfree, vfree);
   static_assert(2 * kDmaPerTile + 2 == 6, "six copy parts, one per sub-tile");
@@ -714,61 +714,69 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
   }
 }
 
-template <int VF>
-__global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
-  // distinct arrays for the ring slots: a copy into one provably does not
-  // alias reads of another
-  static_assert(kStages == 4, "buffer declarations below");
-  __shared__ __align__(16) uint8_t kbuf0[kKBufBytes];   // K codes + the tile's scale
-  __shared__ __align__(16) uint8_t kbuf1[kKBufBytes];
-  __shared__ __align__(16) uint8_t kbuf2[kKBufBytes];
-  __shared__ __align__(16) uint8_t kbuf3[kKBufBytes];
-  __shared__ __align__(16) uint8_t vbuf0[VTile<VF>::kBytes];
-  __shared__ __align__(16) uint8_t vbuf1[VTile<VF>::kBytes];
-  __shared__ __align__(16) uint8_t vbuf2[VTile<VF>::kBytes];
-  __shared__ __align__(16) uint8_t vbuf3[VTile<VF>::kBytes];
-  __shared__ __align__(16) uint8_t grp0[kGrpBytes];     // restore operands, even groups
-  __shared__ __align__(16) uint8_t grp1[kGrpBytes];     // odd groups
+// LDS buffers of one workgroup (distinct arrays for the ring slots: a copy
+// into one provably does not alias reads of another).
+struct AttnLds {
+  uint8_t *kbuf0, *kbuf1, *kbuf2, *kbuf3, *vbuf0, *vbuf1, *vbuf2, *vbuf3, *grp0, *grp1;
+};
+
+// One piece of a work item: the queries of (b,h) = bh's pair of query blocks
+// qp against key tiles [kv0, kv1) (kv0 a multiple of 16, the whole range for
+// a whole item); REPAIR: the repair tiles follow (whole items only).  part == nullptr: the item is whole and its bf16 output is
+// written; otherwise the piece's unnormalised O, row sums and reference
+// exponents go to the partial slot `part` for the merge kernel.
+template <int VF, bool REPAIR>
+__device__ __forceinline__ void attn_piece(const AttnArgs& a, int bh, int qp, int kv0, int kv1, float* part,
+                                           const AttnLds& L) {
+  uint8_t* const kbuf0 = L.kbuf0;
+  uint8_t* const kbuf1 = L.kbuf1;
+  uint8_t* const kbuf2 = L.kbuf2;
+  uint8_t* const kbuf3 = L.kbuf3;
+  uint8_t* const vbuf0 = L.vbuf0;
+  uint8_t* const vbuf1 = L.vbuf1;
+  uint8_t* const vbuf2 = L.vbuf2;
+  uint8_t* const vbuf3 = L.vbuf3;
   uint8_t* const kring[kStages] = {kbuf0, kbuf1, kbuf2, kbuf3};
   uint8_t* const vring[kStages] = {vbuf0, vbuf1, vbuf2, vbuf3};
-
-  // XCD-aware order: hardware deals workgroup ids round-robin over 8 XCDs;
-  // give XCD x a contiguous range of (head, query-block pair) work items.
-  const int total = a.total_wg;
-  const int wg = blockIdx.x, xcd = wg & 7, idx = wg >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int logical = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  const int nblk = a.nblk;
-  const int npair = (nblk + 1) >> 1;
-  const int bh = logical / npair, qp = logical - bh * npair;
+  const int nfull = a.nblk;                        // tiles of the head
   const int b = bh / a.H, h = bh - b * a.H;
 
-  // wave index made provably wave-uniform (scalar branches on it)
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // wave index made provably wave-uniform (scalar branches on it).  The
+  // thread id passes through an empty asm first, so that nothing derived
+  // from it can be hoisted out of a loop over pieces and held across one.
+  int tid_raw = threadIdx.x;
+  asm volatile("" : "+v"(tid_raw));
+  const int tid = tid_raw, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int S = a.S;
   // waves 0-3 own query block 2*qp, waves 4-7 block 2*qp+1 (a missing second
   // block of an odd count is computed on a copy of the first and not stored)
   const int qb = 2 * qp + (w >> 2);
-  const bool q_valid = qb < nblk;
-  const int qbl = q_valid ? qb : nblk - 1;
+  const bool q_valid = qb < nfull;
+  const int qbl = q_valid ? qb : nfull - 1;
+  const int nblk = kv1 - kv0;                     // tiles of this piece
   const int wq = w & 3;                           // 32-query slice within the block
 
   TileCtx c;
+  // the piece's tiles seen as a head of nblk tiles: resources start at tile
+  // kv0 (restore-operand rows too: kv0 is a multiple of the 16-block group);
   // nblk <= 2^17 (S <= 2^24), so a head's tiles span less than 4 GB
-  c.kr = head_rsrc(a.k8 + static_cast<int64_t>(bh) * nblk * kTileBytes, static_cast<uint32_t>(nblk) * kTileBytes);
-  c.vr = head_rsrc(a.v8 + static_cast<int64_t>(bh) * nblk * kTileBytes, static_cast<uint32_t>(nblk) * kTileBytes);
-  const int nrows = muop_rows(nblk);
-  c.muop = a.v_muop + static_cast<int64_t>(bh) * nrows * kMuOpRowBytes;
-  c.mr = head_rsrc(c.muop, static_cast<uint32_t>(nrows) * kMuOpRowBytes);
-  c.ks = a.k_scale + static_cast<int64_t>(bh) * nblk;
+  c.kr = head_rsrc(a.k8 + (static_cast<int64_t>(bh) * nfull + kv0) * kTileBytes,
+                   static_cast<uint32_t>(nblk) * kTileBytes);
+  c.vr = head_rsrc(a.v8 + (static_cast<int64_t>(bh) * nfull + kv0) * kTileBytes,
+                   static_cast<uint32_t>(nblk) * kTileBytes);
+  const int nrows = muop_rows(nfull);
+  c.muop = a.v_muop + (static_cast<int64_t>(bh) * nrows + kv0) * kMuOpRowBytes;
+  c.mr = head_rsrc(c.muop, static_cast<uint32_t>(nrows - kv0) * kMuOpRowBytes);
+  c.ks = a.k_scale + static_cast<int64_t>(bh) * nfull + kv0;
   c.sr = head_rsrc(c.ks, static_cast<uint32_t>(nblk) * 4);
-  c.grp0 = grp0;
-  c.grp1 = grp1;
-  c.sqs = a.q_scale[static_cast<int64_t>(bh) * nblk + qbl];
+  c.grp0 = L.grp0;
+  c.grp1 = L.grp1;
+  c.sqs = a.q_scale[static_cast<int64_t>(bh) * nfull + qbl];
   c.sm_scale = a.sm_scale;
   c.nblk = nblk;
-  c.kval_last = S - (nblk - 1) * kBlock;          // real keys in the last tile
+  // real keys in the piece's last tile
+  c.kval_last = kv1 == nfull ? S - (nfull - 1) * kBlock : kBlock;
   c.tid = tid;
   c.w = w;
   c.lane = lane;
@@ -781,7 +789,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   c.l16 = l16;
   const float sqs = c.sqs;
 
-  const uint8_t* qtile = a.q8 + (static_cast<int64_t>(bh) * nblk + qbl) * kTileBytes;
+  const uint8_t* qtile = a.q8 + (static_cast<int64_t>(bh) * nfull + qbl) * kTileBytes;
   v8i qop[2];
   qop[0] = ld_op_global(qtile, 2 * wq, lane);
   qop[1] = ld_op_global(qtile, 2 * wq + 1, lane);
@@ -852,12 +860,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   if (kb + 2 < nblk) tile_step<VF, 2>(c, kb + 2, kbuf0, kbuf3, vbuf2, vbuf1, qop, acc);
   // drain the copies still in flight before the workgroup retires
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the lane's index values again, from the one register the tile loop kept
+  // (16 * lane), instead of keeping the originals live across it
+  const int lane_p = c.lane16 >> 4, g_p = lane_p >> 4, l16_p = lane_p & 15;
 
   // restore of the last, partial group (its operand rows may not all have
   // been copied; read them from global memory).  Weight slots of tiles past
   // the last hold stale sums but meet zero operands.
   if ((last & (kMuOpGroup - 1)) != kMuOpGroup - 1) {
-    const uint8_t* rows = c.muop + static_cast<int64_t>(last / kMuOpGroup) * kMuOpGroup * kMuOpRowBytes + lane * 8;
+    const uint8_t* rows = c.muop + static_cast<int64_t>(last / kMuOpGroup) * kMuOpGroup * kMuOpRowBytes + lane_p * 8;
     v4s A[8][2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -873,7 +884,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   const vc_head_hdr hd = a.hdr[bh];
 
   // ---- residual repair tiles (codes against the final maximum) ----
-  if (a.nrep_pad > 0) {
+  if (REPAIR && a.nrep_pad > 0) {
     const int nrep = hd.nrep;
     const float fe = hd.rep_scale / hd.v_scale;
     const uint8_t* rk = a.rep_k8 + static_cast<int64_t>(bh) * a.nrep_pad * kD;
@@ -883,7 +894,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
       v8i Pr[2];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const v8i kop = ld_op_global(rk + static_cast<int64_t>(rt) * kTileBytes, t, lane);
+        const v8i kop = ld_op_global(rk + static_cast<int64_t>(rt) * kTileBytes, t, lane_p);
         const v4f s0 = mfma_fp8(kop, qop[0], zero);
         const v4f s1 = mfma_fp8(kop, qop[1], zero);
         uint32_t w0 = 0, w1 = 0;
@@ -891,7 +902,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
 #ifndef VC_ABLATION_EXP_CAST
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = rt * kBlock + 16 * t + 4 * g + i;
+          const int j = rt * kBlock + 16 * t + 4 * g_p + i;
           const float sig = ((sqs * rks[j]) * a.sm_scale) * kLog2e;
           // (the ExpCast constants written out: as calls of cast_scale and
           // cast_const the register allocation of the whole kernel spills)
@@ -908,7 +919,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
           float sa[2], b0[2], b1[2];
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
-            const int j = rt * kBlock + 16 * t + 4 * g + i + k;
+            const int j = rt * kBlock + 16 * t + 4 * g_p + i + k;
             const float sig = ((sqs * rks[j]) * a.sm_scale) * kLog2e;
             sa[k] = j < nrep ? cast_scale(sig) : 0.0f;
             b0[k] = j < nrep ? cast_const(st.M[0]) : kCastOff;
@@ -923,7 +934,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
       }
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const v8i eop = ld_op_global(re + static_cast<int64_t>(rt) * kTileBytes, dt, lane);
+        const v8i eop = ld_op_global(re + static_cast<int64_t>(rt) * kTileBytes, dt, lane_p);
         // codes against M, accumulators against the anchor
         const v4f o0 = mfma_fp8_sb<0>(eop, Pr[0], zero, st.se);
         const v4f o1 = mfma_fp8_sb<1>(eop, Pr[1], zero, st.se);
@@ -936,10 +947,26 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
     }
   }
 
+  if (part) {
+    // ---- a piece: unnormalised O, row sums and the exponent they are
+    // relative to (M, or the MXFP4 anchor A = M - (se byte - 127)) ----
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      const int r = (w >> 2) * kBlock + 16 * (2 * wq + qi) + l16_p;   // query row within the pair
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<v4f*>(part + r * kD + 16 * dt + 4 * g_p) = O[dt][qi];
+      if (g_p == 0) {
+        part[256 * kD + r] = st.l[qi];
+        part[256 * kD + 256 + r] = st.M[qi] - static_cast<float>(static_cast<int>((st.se >> (8 * qi)) & 0xFF) - 127);
+      }
+    }
+    return;
+  }
   // ---- epilogue: out = bf16(s_v * O / l), original query order ----
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
-    const int q = qb * kBlock + 16 * (2 * wq + qi) + l16;
+    const int q = qb * kBlock + 16 * (2 * wq + qi) + l16_p;
     if (q_valid && q < S) {
       const float f = hd.v_scale / st.l[qi];
       uint16_t* orow = a.out + b * a.osB + static_cast<int64_t>(q) * a.osS + h * a.osH;
@@ -947,18 +974,154 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
       for (int dt = 0; dt < 8; ++dt) {
         const uint32_t lo = f32_to_bf16_bits(O[dt][qi][0] * f) | (f32_to_bf16_bits(O[dt][qi][1] * f) << 16);
         const uint32_t hi = f32_to_bf16_bits(O[dt][qi][2] * f) | (f32_to_bf16_bits(O[dt][qi][3] * f) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g_p) = make_uint2(lo, hi);
       }
     }
   }
 }
 
-hipError_t launch_attention(const AttnArgs& a, int BH, hipStream_t st) {
-  (void)BH;
-  if (a.v_format == VC_V_MXFP4)
-    hipLaunchKernelGGL(k_vc_attn_fwd<VC_V_MXFP4>, dim3(a.total_wg), dim3(kAttnThreads), 0, st, a);
+// Workgroup id -> work index, XCD-aware: the hardware deals workgroup ids
+// round-robin over the 8 XCDs; XCD x gets a contiguous range of the `total`
+// work indices (consecutive query blocks of one head share its L2).
+__device__ __forceinline__ int xcd_order(int total, int wg) {
+  const int xcd = wg & 7, idx = wg >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+#define VC_ATTN_LDS_DECL(VF)                                                       \
+  static_assert(kStages == 4, "buffer declarations below");                         \
+  __shared__ __align__(16) uint8_t kbuf0[kKBufBytes]; /* K codes + tile scale */    \
+  __shared__ __align__(16) uint8_t kbuf1[kKBufBytes];                               \
+  __shared__ __align__(16) uint8_t kbuf2[kKBufBytes];                               \
+  __shared__ __align__(16) uint8_t kbuf3[kKBufBytes];                               \
+  __shared__ __align__(16) uint8_t vbuf0[VTile<VF>::kBytes];                        \
+  __shared__ __align__(16) uint8_t vbuf1[VTile<VF>::kBytes];                        \
+  __shared__ __align__(16) uint8_t vbuf2[VTile<VF>::kBytes];                        \
+  __shared__ __align__(16) uint8_t vbuf3[VTile<VF>::kBytes];                        \
+  __shared__ __align__(16) uint8_t grp0[kGrpBytes]; /* restore operands, even */    \
+  __shared__ __align__(16) uint8_t grp1[kGrpBytes]; /* and odd groups */            \
+  const AttnLds L = {kbuf0, kbuf1, kbuf2, kbuf3, vbuf0, vbuf1, vbuf2, vbuf3, grp0, grp1}
+
+// Whole work items: (b,h) and query-block pair, in XCD-aware order.
+template <int VF>
+__global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
+  VC_ATTN_LDS_DECL(VF);
+  const int npair = (a.nblk + 1) >> 1;
+  const int item = xcd_order(a.whole, blockIdx.x);
+  attn_piece<VF, true>(a, item / npair, item - (item / npair) * npair, 0, a.nblk, nullptr, L);
+}
+
+// The cut items, launched after the whole ones: workgroup t runs groups
+// [t*per, t*per + per) of the cut items' (item, 16-tile group) sequence, as
+// one or two pieces (the run crosses at most one item boundary); a piece that
+// is a whole item writes its output directly.
+struct AttnTailArgs {
+  AttnArgs a;
+  AttnTail tl;
+};
+template <int VF>
+__global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_tail(AttnTailArgs args) {
+  VC_ATTN_LDS_DECL(VF);
+  const AttnArgs& a = args.a;
+  const AttnTail& tl = args.tl;
+  const int npair = (a.nblk + 1) >> 1, ngrp = tl.ngrp;
+  const int t = xcd_order(tl.tail_wg, blockIdx.x);
+  int g = t * tl.per;
+  const int gend = min(g + tl.per, tl.tail * ngrp);
+#pragma nounroll
+  for (int j = 0; j < 2 && g < gend; ++j) {
+    const int i = g / ngrp, g0 = g - i * ngrp, g1 = min(ngrp, g0 + (gend - g));
+    const int item = a.whole + i;
+    float* part = g0 == 0 && g1 == ngrp ? nullptr : tl.part + static_cast<int64_t>(2 * t + j) * kPartFloats;
+    if (j) __syncthreads();   // every wave is done with the previous piece's LDS
+    // (no repair tiles: workspaces with a repair set are never cut)
+    attn_piece<VF, false>(a, item / npair, item - (item / npair) * npair, kAttnGroup * g0,
+                          min(a.nblk, kAttnGroup * g1), part, L);
+    g += g1 - g0;
+  }
+}
+
+// Merge of the pieces of a cut item (grid: cut items x 8 blocks of 32 query
+// rows; 256 threads): with e_i the pieces' reference exponents, E = max e_i
+// and w_i = 2^(e_i - E), out = bf16(s_v * sum_i w_i O_i / sum_i w_i l_i).
+// Every factor is a power of two, so this is the online softmax's own
+// rescale.  Thread t moves 16 B of 4 rows (lanes t%32 cover a row's 128
+// channels); all its loads of one pass are independent.
+constexpr int kMergeRowBlocks = 8;
+__global__ void __launch_bounds__(256) k_vc_attn_merge(AttnArgs a, AttnTail tl) {
+  const int i = blockIdx.x, ngrp = tl.ngrp, per = tl.per;
+  const int wf = (i * ngrp) / per, wl = ((i + 1) * ngrp - 1) / per;
+  if (wf == wl) return;                     // the item ran whole in one workgroup
+  const int item = a.whole + i;
+  const int npair = (a.nblk + 1) >> 1;
+  const int bh = item / npair, qp = item - bh * npair;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const float sv = a.hdr[bh].v_scale;
+  const int c4 = threadIdx.x & 31;
+  const int r0 = blockIdx.y * (256 / kMergeRowBlocks) + (threadIdx.x >> 5);
+  // slot of workgroup wv's piece of item i: its first piece if its run starts inside the item
+  auto slot = [&](int wv) {
+    return tl.part + static_cast<int64_t>(2 * wv + (wv * per >= i * ngrp ? 0 : 1)) * kPartFloats;
+  };
+  constexpr int kRows = 256 / kMergeRowBlocks / 8;
+  float e[kRows];
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) e[k] = -3.0e38f;
+  for (int wv = wf; wv <= wl; ++wv) {
+    const float* p = slot(wv) + 256 * kD + 256;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) e[k] = fmaxf(e[k], p[r0 + 8 * k]);
+  }
+  float l[kRows];
+  v4f o[kRows];
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    l[k] = 0.0f;
+    o[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  for (int wv = wf; wv <= wl; ++wv) {
+    const float* p = slot(wv);
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int r = r0 + 8 * k;
+      const float sc = ldexpf(1.0f, static_cast<int>(fmaxf(p[256 * kD + 256 + r] - e[k], -200.0f)));
+      l[k] += sc * p[256 * kD + r];
+      o[k] += sc * *reinterpret_cast<const v4f*>(p + r * kD + 4 * c4);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const int q = qp * 256 + r0 + 8 * k;
+    if (q < a.S) {
+      const float f = sv / l[k];
+      const uint32_t lo = f32_to_bf16_bits(o[k][0] * f) | (f32_to_bf16_bits(o[k][1] * f) << 16);
+      const uint32_t hi = f32_to_bf16_bits(o[k][2] * f) | (f32_to_bf16_bits(o[k][3] * f) << 16);
+      *reinterpret_cast<uint2*>(a.out + b * a.osB + static_cast<int64_t>(q) * a.osS + h * a.osH + 4 * c4) =
+          make_uint2(lo, hi);
+    }
+  }
+}
+
+hipError_t launch_attention(const AttnArgs& a, const AttnTail& tl, hipStream_t st) {
+  const bool fp4 = a.v_format == VC_V_MXFP4;
+  if (a.whole > 0) {
+    if (fp4)
+      hipLaunchKernelGGL(k_vc_attn_fwd<VC_V_MXFP4>, dim3(a.whole), dim3(kAttnThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_vc_attn_fwd<VC_V_E4M3>, dim3(a.whole), dim3(kAttnThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (tl.tail == 0) return hipSuccess;
+  const AttnTailArgs ta = {a, tl};
+  if (fp4)
+    hipLaunchKernelGGL(k_vc_attn_tail<VC_V_MXFP4>, dim3(tl.tail_wg), dim3(kAttnThreads), 0, st, ta);
   else
-    hipLaunchKernelGGL(k_vc_attn_fwd<VC_V_E4M3>, dim3(a.total_wg), dim3(kAttnThreads), 0, st, a);
+    hipLaunchKernelGGL(k_vc_attn_tail<VC_V_E4M3>, dim3(tl.tail_wg), dim3(kAttnThreads), 0, st, ta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_vc_attn_merge, dim3(tl.tail, kMergeRowBlocks), dim3(256), 0, st, a, tl);
   return hipGetLastError();
 }
 

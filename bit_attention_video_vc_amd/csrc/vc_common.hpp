@@ -39,6 +39,57 @@ __host__ __device__ inline int asg_tokens(int64_t BH, int S) {
   return t;
 }
 
+// Work split of one attention launch.  A work item is one (b,h) and pair of
+// 128-query blocks; one workgroup holds a compute unit (its LDS), so a launch
+// runs in rounds of kAttnSlots items.  With items = q*kAttnSlots + R, the
+// first q*kAttnSlots items run whole, and the last R (0 < R < kAttnSlots,
+// the partial last round -- or all items when there are fewer than
+// kAttnSlots) are cut along the key axis into runs of 16-tile groups
+// (ngrp = ceil(nblk/16) per item) spread evenly over tail_wg <= kAttnSlots
+// workgroups of `per` groups each, so that the last round takes about R/kAttnSlots
+// of a whole item's time instead of all of it.  A workgroup's run crosses at
+// most one item boundary (per < ngrp), so it holds at most two pieces; a piece
+// that is not a whole item leaves its unnormalised O, row sum and reference
+// exponent in a partial slot and the merge kernel combines the pieces of an
+// item exactly in powers of two.  The repair tiles need every item's final
+// maximum, so workspaces with a repair set are not split.
+constexpr int kAttnSlots = 256;           // MI355X compute units
+constexpr int kAttnGroup = 16;            // tiles per piece-boundary group
+struct AttnSplit {
+  int64_t items;      // work items
+  int64_t whole;      // items run whole (a multiple of kAttnSlots, or all)
+  int tail;           // items cut into pieces
+  int tail_wg;        // workgroups over the cut items
+  int per;            // groups per tail workgroup
+  int ngrp;           // groups per item
+};
+__host__ __device__ inline AttnSplit attn_split(int64_t BH, int nblk, int nrep) {
+  AttnSplit p;
+  p.items = BH * ((nblk + 1) / 2);
+  p.ngrp = (nblk + kAttnGroup - 1) / kAttnGroup;
+  p.whole = p.items;
+  p.tail = p.tail_wg = p.per = 0;
+  const int R = static_cast<int>(p.items % kAttnSlots);
+  if (nrep > 0 || R == 0 || p.ngrp < 2) return p;
+  const int per = static_cast<int>((static_cast<int64_t>(R) * p.ngrp + kAttnSlots - 1) / kAttnSlots);
+  if (per >= p.ngrp) return p;           // no group saved per compute unit
+  p.whole = p.items - R;
+  p.tail = R;
+  p.per = per;
+  p.tail_wg = static_cast<int>((static_cast<int64_t>(R) * p.ngrp + per - 1) / per);
+  return p;
+}
+// A partial slot: O [256 queries][128 channels], then the row sums l [256]
+// and the reference exponents [256] (the integer running maximum M, or the
+// MXFP4 anchor A), all fp32; two slots per tail workgroup.
+constexpr int kPartFloats = 256 * kD + 2 * 256;
+constexpr size_t kPartBytes = sizeof(float) * kPartFloats;
+
+// k-means per-cluster sums of the sketch (|x| <= 255) reach 255 * S in
+// magnitude: 32-bit while S <= 2^23 (255 * 2^23 < 2^31), 64-bit beyond.  The
+// scratch holds the 64-bit width; the 32-bit sums use its first half.
+__host__ __device__ inline bool wide_sums(int S) { return S > (1 << 23); }
+
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));

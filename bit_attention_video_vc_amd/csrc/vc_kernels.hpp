@@ -47,15 +47,23 @@ struct AttnArgs {
   const uint8_t* rep_e8;
   uint16_t* out;
   int64_t osB, osS, osH;
-  int S, H, nblk, nrep_pad, total_wg;
+  int S, H, nblk, nrep_pad, whole;   // whole: work items run whole (the first launch's workgroups)
   float sm_scale;
   int v_format;       // vc_v_format of the residual tiles in v8
+};
+
+// The cut items (attn_split): tail_wg workgroups run the `tail` items after
+// the whole ones in runs of `per` 16-tile groups (ngrp per item), with
+// partial slots at `part`, then the merge launch.
+struct AttnTail {
+  int tail, tail_wg, per, ngrp;
+  float* part;
 };
 
 hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_opts& o, const WsPtrs& ws,
                             hipStream_t st);
 hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& k, int B, int S, int H, int v_format,
                              const WsPtrs& ws, hipStream_t st);
-hipError_t launch_attention(const AttnArgs& a, int BH, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, const AttnTail& tl, hipStream_t st);
 
 }  // namespace vc

@@ -133,6 +133,10 @@ typedef struct {
  *   rep_k8  u8  [BH][nrep_pad/128] tiles: K codes of the repaired positions
  *   rep_ks  f32 [BH][nrep_pad] K block scale of each repaired position
  *   rep_e8  u8  [BH][nrep_pad/128] tiles: E4M3 residual error, transposed
+ *   attn_part   vc_attention_fwd's partial results for work items it cuts
+ *               along the key axis (the partial last round of workgroups,
+ *               or every item of a launch with fewer items than compute
+ *               units); empty when nothing is cut (always with repair)
  *   scratch     internal (k-means state, sort counters, repair scores)
  * Tile formats (16384 B, 128 rows x 128 columns of codes):
  *   row tile (q8, k8, rep_k8): the byte for (row r, column d) is at
@@ -153,7 +157,7 @@ typedef struct {
 typedef struct {
   size_t total;
   size_t q8, q_scale, k8, k_scale, v8, v_mean, v_muop, hdr;
-  size_t assign, perm, rep_pos, rep_k8, rep_ks, rep_e8, scratch;
+  size_t assign, perm, rep_pos, rep_k8, rep_ks, rep_e8, attn_part, scratch;
   int32_t nblk, nrep, nrep_pad, reserved;
 } vc_ws_layout;
 
@@ -169,9 +173,12 @@ typedef struct {
   uint32_t e_amax_bits;    /* a_e (float bits)                                  */
 } vc_head_hdr;
 
-/* Host only: workspace size and offsets for a V descriptor and options.
- * Only B, S, H (and k, repair_budget) matter.  Returns VC_ERR_ARG or
- * VC_ERR_UNSUPPORTED on invalid shapes/options. */
+/* Infrastructure (no passage of the pages defines it): host-only workspace
+ * size and offsets for a V descriptor and options.  Only B, S, H, k and
+ * repair_budget matter.  Returns VC_ERR_ARG or VC_ERR_UNSUPPORTED on invalid
+ * shapes/options.  The layout depends on the options: every later call on
+ * the workspace must pass the same options (vc_prepare_qk and
+ * vc_attention_fwd read regions at these offsets). */
 vc_status vc_workspace_layout(const vc_desc* vd, const vc_v_opts* opts, vc_ws_layout* out);
 
 /* V-Smooth prepare ("VC-Attention: Value Smoothing and Softmax Casting for
@@ -207,7 +214,13 @@ vc_status vc_prepare_v_noalloc(const vc_desc* vd, const void* v, const vc_v_opts
  * Q is quantised in its original order; K is gathered through perm (written
  * by vc_prepare_v on the same workspace, earlier on the same stream) so that
  * keys and values stay paired.  Per 128-token block: scale = amax/448,
- * code = E4M3(x * (448/amax)).  qd and kd must agree on B, S, H, D. */
+ * code = E4M3(x * (448/amax)).  qd and kd must agree on B, S, H, D, and with
+ * the V that vc_prepare_v prepared; `opts` must be the options it was
+ * prepared with (the workspace offsets depend on them, and an MXFP4
+ * workspace stores K rows in its relabelled order).  A permutation entry
+ * outside [0, S) -- a workspace not prepared for this shape -- gives zero K
+ * rows, never a read outside the K tensor.
+ *   ws      : workspace (device), ws_bytes >= layout.scratch */
 vc_status vc_prepare_qk(const vc_desc* qd, const void* q, const vc_desc* kd, const void* k,
                         const vc_v_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
@@ -221,18 +234,30 @@ vc_status vc_prepare_qk(const vc_desc* qd, const void* q, const vc_desc* kd, con
  *   od      : output view (device memory `out`), dtype must be VC_BF16, same
  *             B, S, H as the prepared inputs; rows stay in the original
  *             query order
- *   opts    : the V options the workspace was prepared with
+ *   opts    : the V options the workspace was prepared with -- the same
+ *             struct values: the workspace offsets and the V tile format
+ *             depend on them, and nothing on the device records them, so
+ *             other options read other regions (within the workspace, never
+ *             outside it) and give a wrong result
  *   aopts   : may be NULL (defaults)
- *   ws      : a workspace prepared by vc_prepare_v and vc_prepare_qk */
+ *   ws      : a workspace prepared by vc_prepare_v and vc_prepare_qk,
+ *             ws_bytes >= layout.scratch
+ * Work items are (b,h) and a pair of 128-query blocks, one workgroup each;
+ * the items of a partial last round of workgroups (or all of them, when
+ * there are fewer items than compute units) are cut along the key axis and
+ * their pieces merged exactly (powers of two) by a second kernel, which uses
+ * the workspace's attn_part region.  Workspaces with a repair set are not
+ * cut. */
 vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts,
                            const vc_attn_opts* aopts, const void* ws, size_t ws_bytes,
                            void* stream);
 
-/* Static strings; never NULL. */
+/* Infrastructure (no passage of the pages defines them): status names and
+ * the calling thread's last error message.  Static strings; never NULL. */
 const char* vc_status_string(vc_status s);
 const char* vc_last_error(void);
 
-/* Library version, e.g. "0.1.0". */
+/* Infrastructure (no passage): library version, e.g. "0.1.0". */
 const char* vc_version(void);
 
 #ifdef __cplusplus

@@ -469,3 +469,28 @@ def test_mxfp4_rejects_repair():
     with pytest.raises(vc.VCError) as e:
         vc.alloc_workspace(v, opts)
     assert e.value.status == vc.VC_ERR_UNSUPPORTED
+
+
+# ---- work items cut along the key axis (the partial last round of
+# workgroups, and launches with fewer items than compute units): pieces of
+# 16-tile groups whose partial results a merge kernel combines -------------
+SPLIT_CASES = [
+    # (B, H, S, v_format, heads checked): what the cut does there
+    (1, 3, 4500, "e4m3", None),                     # 54 items cut into three 1-group pieces, the last ragged
+    (1, 6, 8492, "e4m3", None),                     # 204 items of 5 groups, runs of 4 crossing item boundaries
+    (1, 20, 4196, "e4m3", [(0, 0), (0, 15), (0, 19)]),  # 256 items whole, then 84 cut (heads 15-19)
+    (1, 6, 8492, "mxfp4", None),                    # the 4-bit residual's anchor exponent in the partials
+    (2, 4, 4096, "e4m3", None),                     # config 2's class: 128 items, two pieces each
+]
+
+
+@pytest.mark.parametrize("B,H,S,v_format,heads", SPLIT_CASES,
+                         ids=["S4500_three_pieces", "S8492_runs_cross_items", "H20_whole_then_cut",
+                              "S8492_mxfp4", "B2_S4096_halves"])
+def test_key_axis_split(B, H, S, v_format, heads):
+    from test_split_plan import plan
+    assert plan(B * H, -(-S // 128)) is not None, "the shape must be cut"
+    w, q, k, v = _cfg(2, B=B, H=H, S=S)
+    rows = np.unique(np.concatenate([np.arange(0, S, 3), np.arange(max(0, S - 130), S)]))
+    check_against_oracle(q, k, v, kc=8, iters=2, rows=rows, heads=heads, name=f"split B={B} H={H} S={S} {v_format}",
+                         v_format=v_format)
