@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256) k_kmeans_init(TensorArg v, int S, int H, 
     const int i = tid + 256 * j, c = i >> 7;
     if (c < k) {
       cent[static_cast<int64_t>(bh) * k * kD + i] = static_cast<int32_t>(sketch1(xs[j], shift));
-      csum[static_cast<int64_t>(bh) * k * kD + i] = 0;
+      csum[static_cast<int64_t>(bh) * k * kD + i] = 0;     // clears both widths (wide_sums)
     }
   }
   if (tid < k) ccount[bh * k + tid] = 0;
@@ -274,12 +274,21 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
   __syncthreads();
   if (ACCUM) {
     // a workgroup's sums fit int32 (asg <= 1024 tokens of |x| <= 255); the
-    // head's can reach 255 * S (> 2^31 for S > 2^23): 64-bit adds (two's
-    // complement, so an unsigned add accumulates signed values)
-    unsigned long long* gs = reinterpret_cast<unsigned long long*>(csum + static_cast<int64_t>(bh) * k * kD);
-    for (int i = tid; i < k * kD; i += 256) {
-      const int32_t val = sums[(i / kD) * kSumPitch + (i % kD)];
-      if (val != 0) atomicAdd(&gs[i], static_cast<unsigned long long>(static_cast<long long>(val)));
+    // head's reach 255 * S: 32-bit adds while that fits (S <= 2^23), 64-bit
+    // adds beyond (two's complement, so an unsigned add accumulates signed
+    // values)
+    if (wide_sums(S)) {
+      unsigned long long* gs = reinterpret_cast<unsigned long long*>(csum + static_cast<int64_t>(bh) * k * kD);
+      for (int i = tid; i < k * kD; i += 256) {
+        const int32_t val = sums[(i / kD) * kSumPitch + (i % kD)];
+        if (val != 0) atomicAdd(&gs[i], static_cast<unsigned long long>(static_cast<long long>(val)));
+      }
+    } else {
+      int32_t* gs = reinterpret_cast<int32_t*>(csum) + static_cast<int64_t>(bh) * k * kD;
+      for (int i = tid; i < k * kD; i += 256) {
+        const int32_t val = sums[(i / kD) * kSumPitch + (i % kD)];
+        if (val != 0) atomicAdd(&gs[i], val);
+      }
     }
     if (tid < k && cnt[tid] != 0) atomicAdd(&ccount[bh * k + tid], cnt[tid]);
   }
@@ -296,19 +305,22 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
 // (|q| <= 255 and a non-integer quotient is >= 1/(2n) >= 2^-25 from one).
 // grid (BH, ceil(k/8)), 256 threads; a workgroup owns 8 centroids.
 constexpr int kUpdCent = 8;
-__global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int64_t* csum, int32_t* ccount,
+__global__ void __launch_bounds__(256) k_kmeans_update(int S, int k, int32_t* cent, int64_t* csum, int32_t* ccount,
                                                       uint8_t* cent_op, int32_t* cnorm) {
   const int bh = blockIdx.x;
   const int c0 = blockIdx.y * kUpdCent, c1 = c0 + kUpdCent < k ? c0 + kUpdCent : k;
   int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
+  const bool wide = wide_sums(S);
   int64_t* sg = csum + static_cast<int64_t>(bh) * k * kD;
+  int32_t* sg32 = reinterpret_cast<int32_t*>(csum) + static_cast<int64_t>(bh) * k * kD;
   for (int i = c0 * kD + threadIdx.x; i < c1 * kD; i += blockDim.x) {
     const int32_t n = ccount[bh * k + i / kD];
     if (n > 0) {
-      const int64_t num = 2 * sg[i] + n;
+      const int64_t num = 2 * (wide ? sg[i] : static_cast<int64_t>(sg32[i])) + n;
       cg[i] = static_cast<int32_t>(floor(static_cast<double>(num) / static_cast<double>(2 * n)));
     }
-    sg[i] = 0;
+    if (wide) sg[i] = 0;
+    else sg32[i] = 0;
   }
   __syncthreads();
   if (threadIdx.x < c1 - c0) ccount[bh * k + c0 + threadIdx.x] = 0;
@@ -406,18 +418,22 @@ __global__ void k_identity_perm(int S, int32_t* assign, int32_t* perm) {
 }
 
 // Block means over permuted positions and the residual amax per head.
-// mu = fp32(fp64(sum) / n); R = fp32(v - mu).  The block's gathered rows are
-// read once, 16 bytes per load, into LDS.  Each channel's sum is split over
-// the two halves of the block and four accumulators per thread: the fp64 sum
-// of at most 128 fp16/bf16 values is exact while they span less than 2^38
-// (every fp16 tensor; bf16 values within 38 binades of each other), so any
-// order gives the same mu as the sequential sum.
-// grid (nblk, H, B), 256 threads: thread = (channel tid%128, half tid/128).
+// mu = fp32(fp64(sum) / n); R = fp32(v - mu).  One pass over the block's
+// gathered rows: thread (channel group cg of 8 channels, row group rg) reads
+// rows rg, rg+16, .. (16 bytes each; a wave's load covers 4 whole rows) and
+// keeps per channel the fp64 sum and the minimum and maximum; the 16 row
+// groups are then combined, by lane shuffles within a wave and in LDS across
+// the four waves.  The fp64 sum of at most 128 fp16/bf16
+// values is exact while they span less than 2^38 (every fp16 tensor; bf16
+// values within 38 binades of each other), so any order gives the mean of
+// the sequential sum.  fl(x - mu) is monotone in x, so the largest
+// |fl(x - mu)| is max(fl(xmax - mu), fl(mu - xmin)): the residual amax needs
+// no second pass.  grid (nblk, H, B), 256 threads.
 __global__ void __launch_bounds__(256) k_v_block_stats(TensorArg v, int S, int smooth, const int32_t* perm,
                                                        float* v_mean, vc_head_hdr* hdr) {
-  __shared__ uint4 rows[kBlock][kD / 8];      // raw 16-bit values of the block's rows
   __shared__ int32_t pp[kBlock];
-  __shared__ double part[2][kD];
+  __shared__ double psum[4][kD];              // per wave (its four row groups combined)
+  __shared__ float pmin[4][kD], pmax[4][kD];
   __shared__ float red[16];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x;
   const int tid = threadIdx.x;
@@ -425,40 +441,62 @@ __global__ void __launch_bounds__(256) k_v_block_stats(TensorArg v, int S, int s
   const int n = S - p0 < kBlock ? S - p0 : kBlock;
   if (tid < n) pp[tid] = perm[static_cast<int64_t>(bh) * S + p0 + tid];
   __syncthreads();
-  for (int t = tid; t < n * (kD / 8); t += blockDim.x) {
-    const int j = t >> 4, c8 = (t & 15) * 8;
-    rows[j][t & 15] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(v.p) + b * v.sB +
-                                                      static_cast<int64_t>(pp[j]) * v.sS + h * v.sH + c8);
-  }
-  __syncthreads();
-  const int d = tid & (kD - 1), half = tid >> 7;
-  const int j0 = half * (kBlock / 2), j1 = min(n, j0 + kBlock / 2);
-  const uint16_t* col = reinterpret_cast<const uint16_t*>(&rows[0][0]) + d;
-  const bool bf = v.dtype == VC_BF16;
-  if (smooth) {
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    int j = j0;
-    for (; j + 4 <= j1; j += 4) {
+  const int cg = tid & 15, rg = tid >> 4;
+  double sum[8];
+  float mn[8], mx[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t e = col[(j + u) * kD];
-        acc[u] += static_cast<double>(bf ? bf16_bits_to_f32(e) : f16_bits_to_f32(e));
+  for (int e = 0; e < 8; ++e) {
+    sum[e] = 0.0;
+    mn[e] = 3.0e38f;
+    mx[e] = -3.0e38f;
+  }
+#pragma unroll
+  for (int u = 0; u < kBlock / 16; ++u) {
+    const int j = rg + 16 * u;
+    if (j < n) {
+      float x[8];
+      load8(v.p, b * v.sB + static_cast<int64_t>(pp[j]) * v.sS + h * v.sH + 8 * cg, v.dtype, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sum[e] += static_cast<double>(x[e]);
+        mn[e] = fminf(mn[e], x[e]);
+        mx[e] = fmaxf(mx[e], x[e]);
       }
     }
-    for (; j < j1; ++j) {
-      const uint32_t e = col[j * kD];
-      acc[0] += static_cast<double>(bf ? bf16_bits_to_f32(e) : f16_bits_to_f32(e));
+  }
+  // the wave's four row groups (lanes l, l^16, l^32, l^48), then the 4 waves
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      sum[e] += __shfl_xor(sum[e], o, 64);
+      mn[e] = fminf(mn[e], __shfl_xor(mn[e], o, 64));
+      mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], o, 64));
     }
-    part[half][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+  if ((tid & 63) < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      psum[tid >> 6][8 * cg + e] = sum[e];
+      pmin[tid >> 6][8 * cg + e] = mn[e];
+      pmax[tid >> 6][8 * cg + e] = mx[e];
+    }
   }
   __syncthreads();
-  const float mu = smooth ? static_cast<float>((part[0][d] + part[1][d]) / static_cast<double>(n)) : 0.0f;
-  if (half == 0) v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + d] = mu;
   float m = 0.0f;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t e = col[j * kD];
-    const float x = bf ? bf16_bits_to_f32(e) : f16_bits_to_f32(e);
-    m = fmaxf(m, fabsf(x - mu));
+  if (tid < kD) {
+    const int d = tid;
+    double tot = 0.0;
+    float lo = 3.0e38f, hi = -3.0e38f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      tot += psum[r][d];
+      lo = fminf(lo, pmin[r][d]);
+      hi = fmaxf(hi, pmax[r][d]);
+    }
+    const float mu = smooth ? static_cast<float>(tot / static_cast<double>(n)) : 0.0f;
+    v_mean[(static_cast<int64_t>(bh) * gridDim.x + blk) * kD + d] = mu;
+    m = fmaxf(hi - mu, mu - lo);
   }
   m = block_max(m, red);
   if (tid == 0 && m > 0.0f) atomicMax(&hdr[bh].r_amax_bits, __float_as_uint(m));
@@ -983,7 +1021,7 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
     for (int it = 0; it < o.iters; ++it) {
       launch_assign<true, false>(dim3(nch, H, B), st, v, S, k, asg, ws);
       VC_LAUNCH_CHECK();
-      hipLaunchKernelGGL(k_kmeans_update, dim3(BH, (k + kUpdCent - 1) / kUpdCent), dim3(256), 0, st, k, ws.cent,
+      hipLaunchKernelGGL(k_kmeans_update, dim3(BH, (k + kUpdCent - 1) / kUpdCent), dim3(256), 0, st, S, k, ws.cent,
                          ws.csum, ws.ccount, ws.cent_op,
                          ws.cnorm);
       VC_LAUNCH_CHECK();
