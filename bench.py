@@ -76,8 +76,10 @@ def kernel_sources_sha256() -> str:
 
 
 def traffic_bytes(path: str, key: str):
-    """HBM bytes per attention launch from the rocprofv3 counter summary, or
-    None if there is none for this workload or the kernel sources changed since."""
+    """HBM bytes per attention call (the three kernels of vc_attention_fwd,
+    FETCH_SIZE and WRITE_SIZE scaled by a device copy's readings) from the
+    rocprofv3 counter summary, or None if there is none for this workload or
+    the kernel sources changed since."""
     try:
         with open(path) as fh:
             rec = json.load(fh).get(key)
@@ -261,7 +263,8 @@ def main() -> int:
                    "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
                    "compute_units": torch.cuda.get_device_properties(0).multi_processor_count},
         "roofline": {
-            "kernel": "k_vc_attn_fwd",
+            # the attention call: whole work items, the cut last round, the merge
+            "kernel": "vc_attention_fwd (k_vc_attn_fwd + k_vc_attn_tail + k_vc_attn_merge)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": PEAK_FP8_TFLOPS,

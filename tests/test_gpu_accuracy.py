@@ -13,7 +13,7 @@ oracle's own rel-L2 against exact attention on the same rows is reported
 beside the GPU's: the GPU may exceed it by at most 2% (plus 1e-3), so any
 error above the 4% accuracy target is shown to be the method's, not the
 kernel's.  The 4% target is gated where the method meets it; the workloads
-whose names say "north_star_4pct_not_met" are those where the oracle itself
+whose names say "accuracy_4pct_not_met" are those where the oracle itself
 is above it (zero-mean V), and there the test checks that it is.  Beside the
 errors the report gives the residual-energy ratio of the clustering, sum R^2
 over sum (V - mean of its unsorted 128-token block)^2, from the oracle's own
@@ -79,7 +79,7 @@ CASES = [
 
 
 def _case_id(c):
-    return f"config{c[0]}" + ("" if c[4] else "_north_star_4pct_not_met_method_on_zero_mean_v")
+    return f"config{c[0]}" + ("" if c[4] else "_accuracy_4pct_not_met_method_on_zero_mean_v")
 
 
 @pytest.mark.parametrize("cid,kw,heads,repair,meets", CASES, ids=[_case_id(c) for c in CASES])
@@ -105,7 +105,7 @@ def test_accuracy_report(cid, kw, heads, repair, meets):
         else:
             # the miss is the method's: the oracle itself is above the target
             assert e_s_or > TOL_EXACT, "labelled not met, but the oracle meets 4%: " + line
-            say(f"north_star 4%: not met ({w.name}, b={b}, h={h}): method {e_s_or:.3e}, GPU {e_s:.3e}")
+            say(f"4% accuracy target: not met ({w.name}, b={b}, h={h}): method {e_s_or:.3e}, GPU {e_s:.3e}")
         if norep is not None:
             # the repair adds back part of the residual's quantisation error;
             # it must not make the output measurably worse

@@ -34,39 +34,39 @@ def _whole_call_properties(run, name):
     say(f"{name}: all {BH} heads: perm/assign properties and finite output ok")
 
 
-def _run(cid, heads, north_star_met, v_format="e4m3", **kw):
+def _run(cid, heads, target_met, v_format="e4m3", **kw):
     w = synth.workload(cid, **kw)
     q, k, v = (t.cuda() for t in synth.generate(w, "cpu"))
     rows = synth.sample_rows(w.S, ROWS_PER_HEAD).numpy()
     run = check_against_oracle(q, k, v, kc=w.k, iters=w.iters, beta=w.repair_budget, rows=rows, heads=heads,
-                               name=f"{w.name} B={w.B} H={w.H} S={w.S} {v_format}", north_star_met=north_star_met,
+                               name=f"{w.name} B={w.B} H={w.H} S={w.S} {v_format}", target_met=target_met,
                                v_format=v_format)
     _whole_call_properties(run, w.name)
 
 
 def test_full_minimax_h56():
     # the benchmark's workload: B=1, S=73397, H=56
-    _run(4, heads=[(0, 0), (0, 29), (0, 55)], north_star_met=True)
+    _run(4, heads=[(0, 0), (0, 29), (0, 55)], target_met=True)
 
 
 @pytest.mark.parametrize("H", [7, 14])
 def test_full_minimax_other_heads(H):
-    _run(4, heads=[(0, 0), (0, H - 1)], north_star_met=True, H=H)
+    _run(4, heads=[(0, 0), (0, H - 1)], target_met=True, H=H)
 
 
-def test_full_wan_720p_north_star_4pct_not_met_method_on_zero_mean_v():
+def test_full_wan_720p_accuracy_4pct_not_met_method_on_zero_mean_v():
     # zero-mean V with 0.2% outlier tokens at 50x: the per-head V scale is set
     # by the outliers and the oracle itself sits 5-6% from exact attention;
     # the GPU is gated at 1.02x the oracle's error (plus 1e-3) instead
-    _run(3, heads=[(0, 0), (0, 39)], north_star_met=False)
+    _run(3, heads=[(0, 0), (0, 39)], target_met=False)
 
 
-def test_full_batched_repair_north_star_4pct_not_met_method_on_zero_mean_v():
+def test_full_batched_repair_accuracy_4pct_not_met_method_on_zero_mean_v():
     # Student-t V (zero mean): the oracle itself sits ~5.7% from exact
-    _run(5, heads=[(0, 0), (1, 23)], north_star_met=False)
+    _run(5, heads=[(0, 0), (1, 23)], target_met=False)
 
 
 def test_full_minimax_h14_mxfp4():
     # the 4-bit residual at the benchmark's sequence length (its own kernel
     # instance: FP4 P.V operands and the anchor maximum)
-    _run(4, heads=[(0, 0), (0, 13)], north_star_met=True, v_format="mxfp4", H=14)
+    _run(4, heads=[(0, 0), (0, 13)], target_met=True, v_format="mxfp4", H=14)

@@ -184,15 +184,15 @@ def _np(t):
 
 
 def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0.0, rows=None, heads=None,
-                         sm_scale=0.0, name="", north_star_met=None, v_format="e4m3"):
+                         sm_scale=0.0, name="", target_met=None, v_format="e4m3"):
     """Run the GPU path and compare every prepared product and the output with the oracle.
 
     Output gates per head: rel-L2 vs the oracle <= TOL_ORACLE, every row's
     rel-L2 vs the oracle's row <= TOL_ROW, and rel-L2 vs exact fp64 attention
     <= EXACT_RATIO x the oracle's own + EXACT_SLACK.  The 4% target vs exact
     is gated on every head where the oracle meets it; a head where the oracle
-    itself is above it is a miss of the method, listed in run.north_star_misses.
-    north_star_met=True asserts there is no such miss, False that the case
+    itself is above it is a miss of the method, listed in run.target_misses.
+    target_met=True asserts there is no such miss, False that the case
     does miss (so a case labelled "not met" is one where the method is above
     4%), None reports only."""
     say(f"{name}: shape={tuple(q.shape)} dtype={q.dtype} smooth={smooth} k={kc} T={iters} beta={beta} "
@@ -277,13 +277,13 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
         f"{max(errs_ex):.3e} (oracle's own {max(errs_or_ex):.3e})")
     for tag, e_ex, e_or_ex in misses:
         say(f"{tag}: 4% target vs exact not met by the method: GPU {e_ex:.3e}, oracle {e_or_ex:.3e}")
-    if north_star_met is True:
+    if target_met is True:
         assert not misses, f"{name}: the 4% target is missed: {misses}"
-    elif north_star_met is False:
+    elif target_met is False:
         assert misses, f"{name}: labelled 4% not met, but every head meets it"
     run.err_exact = errs_ex
     run.err_oracle_exact = errs_or_ex
-    run.north_star_misses = misses
+    run.target_misses = misses
     return run
 
 
