@@ -76,7 +76,7 @@ def kernel_sources_sha256() -> str:
 
 
 def traffic_bytes(path: str, key: str):
-    """HBM bytes per attention call (the three kernels of vc_attention_fwd,
+    """HBM bytes per attention call (the kernels of vc_attention_fwd,
     FETCH_SIZE and WRITE_SIZE scaled by a device copy's readings) from the
     rocprofv3 counter summary, or None if there is none for this workload or
     the kernel sources changed since."""
