@@ -120,6 +120,23 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, int dtype, 
   }
 }
 
+// load8 for an input type fixed at compile time (no branch on the type)
+template <int DT>
+__device__ __forceinline__ void load8_t(const void* base, int64_t off, float* out) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (DT == VC_BF16) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    } else {
+      out[2 * i] = f16_bits_to_f32(w[i] & 0xFFFFu);
+      out[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
+    }
+  }
+}
+
 __device__ __forceinline__ float load1(const void* base, int64_t off, int dtype) {
   const uint32_t b = reinterpret_cast<const uint16_t*>(base)[off];
   return dtype == VC_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);

@@ -171,14 +171,25 @@ __device__ __forceinline__ TokRaw load_tok(const TensorArg& v, int b, int h, int
                     : make_uint4(0, 0, 0, 0);
   return t;
 }
-// fp16/bf16 element -> sketch value (an integer in [-255, 255]) as bf16 bits
-__device__ __forceinline__ uint32_t sketch_bits(uint32_t e16, int dtype, int shift) {
-  const float x = dtype == VC_BF16 ? __uint_as_float(e16 << 16) : f16_bits_to_f32(e16);
-  const float s = __builtin_amdgcn_fmed3f(rintf(ldexpf(x, shift)), -255.0f, 255.0f);
-  return __float_as_uint(s) >> 16;           // exact: at most 8 significant bits
+// The sketch value (an integer in [-255, 255], so exact in bf16) of the two
+// fp16/bf16 elements of a dword, as a packed pair of bf16 (element order
+// kept).  DT is the input type, fixed per instantiation so the conversion
+// has no branch.
+template <int DT>
+__device__ __forceinline__ float sketch_f32(uint32_t half_bits, int shift) {
+  const float x = DT == VC_BF16 ? __uint_as_float(half_bits) : f16_bits_to_f32(half_bits);
+  return __builtin_amdgcn_fmed3f(rintf(ldexpf(x, shift)), -255.0f, 255.0f);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t sketch_pair(uint32_t w, int shift) {
+  // bf16: the low element's bits moved up, the high element's masked in place
+  const float lo = sketch_f32<DT>(DT == VC_BF16 ? w << 16 : (w & 0xFFFFu), shift);
+  const float hi = sketch_f32<DT>(DT == VC_BF16 ? (w & 0xFFFF0000u) : (w >> 16), shift);
+  // the upper halves of the two fp32 values (exact: at most 8 significant bits)
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-template <bool ACCUM, bool FINAL, int NCT>
+template <int DT, bool ACCUM, bool FINAL, int NCT>
 __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k, int asg, const vc_head_hdr* hdr,
                                                        const uint8_t* cent_op, const int32_t* cnorm,
                                                        int64_t* csum, int32_t* ccount, int32_t* assign,
@@ -208,24 +219,16 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
 
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const int s0 = blockIdx.x * asg;
-  const int kIters = asg / 64;
-  int tok = s0 + w * 16 + l16;
-  TokRaw nxt = load_tok(v, b, h, tok, tok < S, g);
-  for (int tt = 0; tt < kIters; ++tt) {
-    const TokRaw cur = nxt;
+  static_assert(kAsgTokMin % 128 == 0, "the loop below takes token rows in pairs");
+  const int kIters = asg / 64;        // asg is a power of two >= kAsgTokMin: even
+  // one iteration: 16 tokens per wave (token `tok` in lane group g's dims)
+  auto assign_tokens = [&](const TokRaw& cur, int tok) {
     const bool valid = tok < S;
-    const int tok_next = tok + 64;
-    if (tt + 1 < kIters) nxt = load_tok(v, b, h, tok_next, tok_next < S, g);   // one iteration ahead
     v8bf xb[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t wv[4] = {cur.r[kk].x, cur.r[kk].y, cur.r[kk].z, cur.r[kk].w};
-      uint32_t pk[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pk[i] = sketch_bits(wv[i] & 0xFFFFu, v.dtype, shift) | (sketch_bits(wv[i] >> 16, v.dtype, shift) << 16);
-      xb[kk] = __builtin_bit_cast(v8bf, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    }
+    for (int kk = 0; kk < 4; ++kk)
+      xb[kk] = __builtin_bit_cast(v8bf, make_uint4(sketch_pair<DT>(cur.r[kk].x, shift), sketch_pair<DT>(cur.r[kk].y, shift),
+                                                   sketch_pair<DT>(cur.r[kk].z, shift), sketch_pair<DT>(cur.r[kk].w, shift)));
     v4f acc[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] = zero;
@@ -239,22 +242,19 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (cn[ct][i] != 0x7FFFFFFF) {
-          const int32_t sc = cn[ct][i] - 2 * static_cast<int32_t>(acc[ct][i]);
-          if (sc < best) {
-            best = sc;
-            bc = 16 * ct + 4 * g + i;
-          }
-        }
+        // absent centroids carry norm 0x7FFFFFFF and never win
+        const int32_t sc = cn[ct][i] == 0x7FFFFFFF ? 0x7FFFFFFF : cn[ct][i] - 2 * static_cast<int32_t>(acc[ct][i]);
+        const bool lt = sc < best;
+        best = lt ? sc : best;
+        bc = lt ? 16 * ct + 4 * g + i : bc;
       }
 #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
       const int32_t ob = __shfl_xor(best, off, 64);
       const int oc = __shfl_xor(bc, off, 64);
-      if (ob < best || (ob == best && oc < bc)) {
-        best = ob;
-        bc = oc;
-      }
+      const bool take = ob < best || (ob == best && oc < bc);
+      best = take ? ob : best;
+      bc = take ? oc : bc;
     }
     if (valid) {
       if (g == 0) {
@@ -269,7 +269,17 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
             atomicAdd(&sums[bc * kSumPitch + 32 * kk + 8 * g + i], static_cast<int32_t>(static_cast<float>(xb[kk][i])));
       }
     }
-    tok = tok_next;
+  };
+  // two token buffers in turn: the next iteration's loads are in flight
+  // while one is processed
+  int tok = s0 + w * 16 + l16;
+  TokRaw b0 = load_tok(v, b, h, tok, tok < S, g), b1;
+  for (int tt = 0; tt < kIters; tt += 2) {
+    b1 = load_tok(v, b, h, tok + 64, tok + 64 < S, g);
+    assign_tokens(b0, tok);
+    if (tt + 2 < kIters) b0 = load_tok(v, b, h, tok + 128, tok + 128 < S, g);
+    assign_tokens(b1, tok + 64);
+    tok += 128;
   }
   __syncthreads();
   if (ACCUM) {
@@ -429,6 +439,7 @@ __global__ void k_identity_perm(int S, int32_t* assign, int32_t* perm) {
 // the sequential sum.  fl(x - mu) is monotone in x, so the largest
 // |fl(x - mu)| is max(fl(xmax - mu), fl(mu - xmin)): the residual amax needs
 // no second pass.  grid (nblk, H, B), 256 threads.
+template <int DT>
 __global__ void __launch_bounds__(256) k_v_block_stats(TensorArg v, int S, int smooth, const int32_t* perm,
                                                        float* v_mean, vc_head_hdr* hdr) {
   __shared__ int32_t pp[kBlock];
@@ -455,7 +466,7 @@ __global__ void __launch_bounds__(256) k_v_block_stats(TensorArg v, int S, int s
     const int j = rg + 16 * u;
     if (j < n) {
       float x[8];
-      load8(v.p, b * v.sB + static_cast<int64_t>(pp[j]) * v.sS + h * v.sH + 8 * cg, v.dtype, x);
+      load8_t<DT>(v.p, b * v.sB + static_cast<int64_t>(pp[j]) * v.sS + h * v.sH + 8 * cg, x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         sum[e] += static_cast<double>(x[e]);
@@ -990,17 +1001,22 @@ __global__ void __launch_bounds__(256) k_repair_kpack(int S, int nrep_pad, const
     if (_e != hipSuccess) return _e;                        \
   } while (0)
 
-template <bool ACCUM, bool FINAL>
-void launch_assign(dim3 grid, hipStream_t st, const TensorArg& v, int S, int k, int asg, const WsPtrs& ws) {
+template <int DT, bool ACCUM, bool FINAL>
+void launch_assign_dt(dim3 grid, hipStream_t st, const TensorArg& v, int S, int k, int asg, const WsPtrs& ws) {
   const int nct = (k + 15) / 16;     // 1..4 (k <= 64)
 #define VC_ASSIGN(N)                                                                                    \
-  hipLaunchKernelGGL((k_kmeans_assign<ACCUM, FINAL, N>), grid, dim3(256), 0, st, v, S, k, asg, ws.hdr, ws.cent_op, \
+  hipLaunchKernelGGL((k_kmeans_assign<DT, ACCUM, FINAL, N>), grid, dim3(256), 0, st, v, S, k, asg, ws.hdr, ws.cent_op, \
                      ws.cnorm, ws.csum, ws.ccount, ws.assign, ws.chunk_hist)
   if (nct == 1) VC_ASSIGN(1);
   else if (nct == 2) VC_ASSIGN(2);
   else if (nct == 3) VC_ASSIGN(3);
   else VC_ASSIGN(4);
 #undef VC_ASSIGN
+}
+template <bool ACCUM, bool FINAL>
+void launch_assign(dim3 grid, hipStream_t st, const TensorArg& v, int S, int k, int asg, const WsPtrs& ws) {
+  if (v.dtype == VC_BF16) launch_assign_dt<VC_BF16, ACCUM, FINAL>(grid, st, v, S, k, asg, ws);
+  else launch_assign_dt<VC_F16, ACCUM, FINAL>(grid, st, v, S, k, asg, ws);
 }
 
 hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_opts& o, const WsPtrs& ws,
@@ -1038,7 +1054,10 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
     hipLaunchKernelGGL(k_identity_perm, dim3((S + 255) / 256, H, B), dim3(256), 0, st, S, ws.assign, ws.perm);
     VC_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(k_v_block_stats, gblk, dim3(256), 0, st, v, S, o.smooth, ws.perm, ws.v_mean, ws.hdr);
+  if (v.dtype == VC_BF16)
+    hipLaunchKernelGGL(k_v_block_stats<VC_BF16>, gblk, dim3(256), 0, st, v, S, o.smooth, ws.perm, ws.v_mean, ws.hdr);
+  else
+    hipLaunchKernelGGL(k_v_block_stats<VC_F16>, gblk, dim3(256), 0, st, v, S, o.smooth, ws.perm, ws.v_mean, ws.hdr);
   VC_LAUNCH_CHECK();
   // restore operands: zero first (blocks past the last stay zero)
   hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws.v_muop), 0u,
