@@ -115,6 +115,15 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0,
                                            0, 0);
 }
+// The same with the wave-uniform part of the offset in the scalar offset
+// field, so the lane's part (16 * lane, one kept register) needs no vector
+// arithmetic.  Callers keep soff + voff inside the tile range by
+// construction (clamped tile indices).
+__device__ __forceinline__ void copy16_to_lds_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                uint8_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff,
+                                           static_cast<int>(soff), 0, 0);
+}
 constexpr int kDmaPerTile = kTileBytes / (16 * kAttnThreads);   // copy instructions per 16 KB tile
 // LDS ring depth for K and for V tiles; copies run kStages-1 tiles ahead.
 constexpr int kStages = 4;
@@ -269,20 +278,22 @@ __device__ __forceinline__ v4f pv_mfma(const v8i& vop, const v8i& p, const v4f& 
 }
 
 // The new maximum of query sub-tile qi from the held tile's partial row
-// maxima: the cross-row combine, the integer ceiling and the cast constant;
-// d = how far it rose (>= 0, an integer).  Did any row's maximum rise?
-// ceil(fl(m*sigma)) > M for an integer M exactly when fl(m*sigma) > M, and
-// fl(m*sigma) is monotone in m, so each lane's partial maximum decides
-// without the cross-row combine, which then runs only when one did (a
-// wave-uniform branch).
-__device__ __forceinline__ void new_max(SoftState& st, int qi, float mh, float sig, float& d) {
-  d = 0.0f;
+// maxima: the cross-row combine, the integer ceiling and the cast constant.
+// Did any row's maximum rise?  ceil(fl(m*sigma)) > M for an integer M
+// exactly when fl(m*sigma) > M, and fl(m*sigma) is monotone in m, so each
+// lane's partial maximum decides without the cross-row combine, which then
+// runs only when one did (a wave-uniform branch).  Returns that decision
+// (wave-uniform); only then is d = how far each row rose (>= 0, an integer)
+// set, and some row's d is > 0.
+__device__ __forceinline__ bool new_max(SoftState& st, int qi, float mh, float sig, float& d) {
   if (__builtin_expect(__any(mh * sig > st.M[qi]), 0)) {
     const float mn = fmaxf(st.M[qi], ceilf(max_over_rows(mh) * sig));
     d = mn - st.M[qi];
     st.M[qi] = mn;
     st.cq[qi] = cast_const(mn);
+    return true;
   }
+  return false;
 }
 
 // The matrix-core work of one step kb, in two halves.  First the P.V MFMAs
@@ -304,7 +315,7 @@ __device__ __forceinline__ void new_max(SoftState& st, int qi, float mh, float s
 // step.
 template <int VF, typename Copies>
 __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* vt, int lane, const v8i (&qop)[2],
-                                           const v8i (&P)[2], float sig, SoftState& st, float (&d)[2],
+                                           const v8i (&P)[2], float sig, SoftState& st, float (&d)[2], bool (&rose)[2],
                                            const v4f (&sh)[8][2], const float (&mh)[2], v4f (&sn)[8][2],
                                            v8i (&Pn)[2], float (&mn)[2], v4f (&O)[8][2], float (&rr)[2],
                                            bool rsel, const Copies& cp) {
@@ -349,7 +360,7 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
     if (dt == 0) {
       // the held tile's last sub-tile, then the maximum after it
       max_acc(sh[7][0], mx[0]);
-      new_max(st, 0, mx[0], sig, d[0]);
+      rose[0] = new_max(st, 0, mx[0], sig, d[0]);
       asm volatile("" : "+v"(st.cq[0]), "+v"(d[0]));
     } else {
       half(2 * dt - 1);                    // slots 2, 4, .. 14: halves 1, 3, .. 13
@@ -360,7 +371,7 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* ktile, const uint8_t* 
     __builtin_amdgcn_sched_barrier(0);
     if (dt == 0) {
       max_acc(sh[7][1], mx[1]);
-      new_max(st, 1, mx[1], sig, d[1]);
+      rose[1] = new_max(st, 1, mx[1], sig, d[1]);
       asm volatile("" : "+v"(st.cq[1]), "+v"(d[1]));
       half(0);
     } else {
@@ -498,16 +509,17 @@ struct TileAcc {
 template <int VF>
 struct StepCopies {
   const TileCtx& c;
-  uint32_t koff, voff, soff, roff;
+  uint32_t koff, voff, soff, roff;   // koff, voff: wave-uniform (tile and wave), the lane's part is c.lane16
   uint8_t* kdst;
   uint8_t* vdst;
   uint8_t* rdst;
   __device__ __forceinline__ StepCopies(const TileCtx& ctx, int tk, int tv, int row, uint8_t* kfree, uint8_t* vfree)
       : c(ctx) {
-    // per-lane parts from the one lane-offset register (16 * tid = 1024 * w + 16 * lane)
-    const uint32_t tid16 = static_cast<uint32_t>(c.w) * 1024 + static_cast<uint32_t>(c.lane16);
-    koff = static_cast<uint32_t>(tk) * kTileBytes + tid16;
-    voff = static_cast<uint32_t>(tv) * kTileBytes + tid16;
+    // 16 * tid = 1024 * w + 16 * lane: the wave's part goes with the tile
+    // offset into the scalar offset, the lane's part is c.lane16 (tk, tv
+    // <= the last tile, so every copy stays inside the resource)
+    koff = static_cast<uint32_t>(tk) * kTileBytes + static_cast<uint32_t>(c.w) * 1024;
+    voff = static_cast<uint32_t>(tv) * kTileBytes + static_cast<uint32_t>(c.w) * 1024;
     soff = static_cast<uint32_t>(tk) * 4;
     roff = static_cast<uint32_t>(row) * kMuOpRowBytes + static_cast<uint32_t>(c.lane16);
     kdst = kfree;
@@ -522,14 +534,17 @@ struct StepCopies {
                                                  4, soff, 0, 0, 0);
     } else if (part <= kDmaPerTile) {
       const int j = part - 1;
-      copy16_to_lds(c.kr, koff + j * (16 * kAttnThreads), kdst + j * (16 * kAttnThreads) + w * 1024);
+      copy16_to_lds_s(c.kr, static_cast<uint32_t>(c.lane16), koff + j * (16 * kAttnThreads),
+                      kdst + j * (16 * kAttnThreads) + w * 1024);
     } else if (part <= 2 * kDmaPerTile) {
       const int j = part - 1 - kDmaPerTile;
       if (j < VTile<VF>::kDma) {
-        copy16_to_lds(c.vr, voff + j * (16 * kAttnThreads), vdst + j * (16 * kAttnThreads) + w * 1024);
+        copy16_to_lds_s(c.vr, static_cast<uint32_t>(c.lane16), voff + j * (16 * kAttnThreads),
+                        vdst + j * (16 * kAttnThreads) + w * 1024);
       } else if (VF && w == 1) {
         // MXFP4: the tile's 512 scale bytes (and 512 unused bytes of the slot)
-        copy16_to_lds(c.vr, voff - static_cast<uint32_t>(w) * 1024 + kFp4CodeBytes, vdst + kFp4CodeBytes);
+        copy16_to_lds_s(c.vr, static_cast<uint32_t>(c.lane16), voff - static_cast<uint32_t>(w) * 1024 + kFp4CodeBytes,
+                        vdst + kFp4CodeBytes);
       }
     } else {
       if (w == 0) copy16_to_lds(c.mr, roff, rdst);
@@ -638,12 +653,13 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
   static_assert(2 * kDmaPerTile + 2 == 6, "six copy parts, one per sub-tile");
   v8i Pn[2];
   float d[2], ks_new;
+  bool rose[2];
   {
     v4f sn[8][2];
     float mn[2];
     // tile kb's row sum goes to l and to the restore weight of tile kb%16
     // of its group, held by lane group (kb/4)%4 in slot J
-    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, acc.sig, acc.st, d, acc.sh, acc.mh, sn, Pn, mn, acc.O,
+    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, acc.sig, acc.st, d, rose, acc.sh, acc.mh, sn, Pn, mn, acc.O,
                    acc.rr[J], (c.lane16 >> 8) == ((kb >> 2) & 3), cp);
     // K(kb+2)'s scale (replicated per lane after the tile), read before the
     // barrier: the next step refills this buffer.  Wave-uniform, so it is
@@ -670,7 +686,7 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
   // the maximum rose by d from tile kb to tile kb+1
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
-    if (__builtin_expect(__any(d[qi] != 0.0f), 0)) {
+    if (__builtin_expect(rose[qi], 0)) {
       float alpha;
       bool resc = true;
       if (VF == 0) {
