@@ -216,3 +216,25 @@ def test_repair_zero_budget_is_identical_and_repair_helps():
     ex = O.attention_exact(q, k, v)
     e = {b: O.rel_l2(o, ex) for b, o in outs.items()}
     assert e[0.05] < e[0.005] < e[0.0]
+
+
+def test_softmax_temperature_two_keys():
+    # Two keys whose exact softmax weights are 9:1 (score gap ln 9 after the
+    # 1/sqrt(128) scale), values +e0 and -e0: exact output 0.8 e0.  The
+    # quantised path sees the gap as log2(9) = 3.17 octaves, 25 ExpCast steps
+    # of 1/8 (ratio 2^(25/8) = 8.72, output 0.794).  A temperature slip (the
+    # log2 e factor lost, or natural-log codes) moves the output by ~18%.
+    a = float(np.sqrt(np.log(9.0) * np.sqrt(128.0) / 2.0))
+    q = np.zeros((2, 128)); q[:, 0] = a          # Q and K have one length; both rows alike
+    k = np.zeros((2, 128)); k[0, 0] = a; k[1, 0] = -a
+    v = np.zeros((2, 128)); v[0, 0] = 1.0; v[1, 0] = -1.0
+    f = lambda x: x.astype(np.float32).astype(np.float64)
+    q, k, v = f(q), f(k), f(v)
+    ex = O.attention_exact(q, k, v)
+    assert abs(ex[0, 0] - 0.8) < 1e-6
+    hv = O.prepare_v_head(v, smooth=False)
+    hq = O.prepare_qk_head(q, k, hv.perm)
+    out = O.attend_head(hq, hv)
+    assert abs(out[0, 0] - 0.8) < 0.02, out[0, 0]
+    assert np.array_equal(out[0], out[1])
+    assert np.all(np.abs(out[0, 1:]) < 1e-12)

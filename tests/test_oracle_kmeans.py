@@ -27,11 +27,27 @@ def test_sketch_scaling_and_range():
         x = O.sketch(v)
         a = np.abs(v).max()
         e = int(np.floor(np.log2(a)))
-        shift = 7 - e
+        shift = 7 - e                       # max|v| * 2^shift in [128, 256)
         assert 128 <= np.abs(x).max() <= 255
-        # x is v * 2^shift rounded to the nearest integer, within half a unit
-        assert np.all(np.abs(x - v * 2.0 ** shift) <= 0.5 + 1e-12)
+        # x is v * 2^shift rounded to the nearest integer, within half a unit,
+        # except where the clamp to +-255 applies
+        y = v * 2.0 ** shift
+        free = np.abs(y) < 255.5
+        assert np.all(np.abs(x - y)[free] <= 0.5 + 1e-12)
     assert not np.any(O.sketch(np.zeros((5, 128))))
+
+
+def test_sketch_exact_values():
+    # max|v| = 1.99609375 (bf16 0x3FFF) -> floor(log2) = 0, shift 7: values
+    # times 128, rounded half to even, clamped to [-255, 255]
+    v = np.zeros((2, 128))
+    v[0, :8] = [1.99609375, -1.99609375, 1.0, -0.5, 0.00390625, 0.01171875, 1.9921875, -1.9921875]
+    v[1, :4] = [0.00390625, -0.01171875, 1.5, 0.25]
+    x = O.sketch(v)
+    # 255.5 -> 256 -> 255 and -255.5 -> -256 -> -255 (clamped); 0.5 -> 0 and
+    # 1.5 -> 2 (ties to even); 255 and -255 exact
+    assert x[0, :8].tolist() == [255, -255, 128, -64, 0, 2, 255, -255]
+    assert x[1, :4].tolist() == [0, -2, 192, 32]
 
 
 def test_init_positions_distinct_in_range():

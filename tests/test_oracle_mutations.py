@@ -105,7 +105,7 @@ def test_block_mean_off_by_one_count(monkeypatch):
 def test_missing_log2e_in_sigma(monkeypatch):
     monkeypatch.setattr(O, "sigma_of", lambda sq, sk, sm: (np.asarray(sq, np.float32) * np.asarray(sk, np.float32)
                                                            * np.float32(sm)).astype(np.float32))
-    _fails(TA.test_pipeline_config2_heads_accuracy_and_vsmooth_benefit)
+    _fails(TA.test_softmax_temperature_two_keys)
 
 
 def test_mx_groups_strided_keys(monkeypatch):
@@ -118,3 +118,28 @@ def test_mx_groups_strided_keys(monkeypatch):
 def test_mx_groups_of_16(monkeypatch):
     monkeypatch.setattr(O, "mx_group_of_key", lambda j: ((np.asarray(j, np.int64) % 128) // 16) % 4)
     _fails(TM.test_groups_are_runs_of_32_positions_of_one_tile_and_channel)
+
+
+def _sketch_with(shift_base, lo, hi):
+    import math
+
+    def bad(v):
+        v = np.asarray(v, dtype=np.float64)
+        a = float(np.max(np.abs(v))) if v.size else 0.0
+        if a == 0.0:
+            return np.zeros(v.shape, dtype=np.int64)
+        _, e = math.frexp(a)
+        return np.clip(np.rint(np.ldexp(v, shift_base + 1 - e)), lo, hi).astype(np.int64)
+    return bad
+
+
+def test_sketch_eight_bits(monkeypatch):
+    # the narrower sketch (max|v| scaled into [64, 128), int8 clamp)
+    monkeypatch.setattr(O, "sketch", _sketch_with(6, -128, 127))
+    _fails(TK.test_sketch_exact_values)
+    _fails(TK.test_sketch_scaling_and_range)
+
+
+def test_sketch_clamp_asymmetric(monkeypatch):
+    monkeypatch.setattr(O, "sketch", _sketch_with(7, -256, 255))
+    _fails(TK.test_sketch_exact_values)
