@@ -104,12 +104,19 @@ def test_layout_regions_are_disjoint_and_sized():
     (dict(dtype=7), vc.VC_ERR_UNSUPPORTED),
     (dict(sS=129), vc.VC_ERR_ARG),
     (dict(H=70000), vc.VC_ERR_UNSUPPORTED),          # past the launch grid's second dimension
+    (dict(S=(1 << 24) + 1, H=1), vc.VC_ERR_UNSUPPORTED),   # past the largest supported S
 ])
 def test_layout_rejects_bad_descriptors(mut, code):
     d = _desc(**mut)
     st, _ = _layout(d, vc.v_opts(True, 2, 1))
     assert st == code
     assert vc.lib().vc_last_error().decode()
+
+
+def test_layout_accepts_the_largest_s():
+    st, L = _layout(_desc(S=1 << 24, H=1), vc.v_opts(True, 32, 5))
+    assert st == vc.VC_OK
+    assert L.nblk == (1 << 24) // 128 and L.total > 3 * (1 << 24) * 128
 
 
 @pytest.mark.parametrize("opts,code", [

@@ -325,6 +325,42 @@ def test_kmeans_options(kc, iters, seed):
     check_against_oracle(q, k, v, kc=kc, iters=iters, seed=seed, name=f"k={kc} T={iters} seed={seed}")
 
 
+def test_kmeans_sums_past_int32():
+    """k-means at a length where a cluster's sketch sum passes 2^31.
+
+    S = 8422400 tokens with channel 0 = 1.9921875 (sketch +255) except a run
+    of 200 tokens at -1.9921875 (sketch -255) around cluster 1's initial
+    position; every other channel is 0.  With k=2 and one iteration the
+    centroids must come out (255, 0, ...) and (-255, 0, ...): cluster 0's
+    sum is 255 * 8422200 > 2^31 - 1, so a 32-bit accumulation would wrap
+    and pull both centroids to -255.  The answer is known by construction:
+    A tokens in cluster 0, the run in cluster 1, the permutation A then the
+    run, each ascending."""
+    S, seed = 8422400, 5
+    init = O.init_positions(S, 2, seed, 0)
+    lo, hi = max(S // 2, int(init[1]) - 100), min(S, max(S // 2, int(init[1]) - 100) + 200)
+    assert int(init[0]) < S // 2 and lo <= int(init[1]) < hi and hi - lo == 200
+    assert 255 * (S - 200) > 2 ** 31 - 1
+    say(f"k-means sums past int32: S={S} run [{lo}, {hi})")
+    v = torch.zeros((1, S, 1, 128), dtype=torch.bfloat16, device="cuda")
+    v[0, :, 0, 0] = 1.9921875
+    v[0, lo:hi, 0, 0] = -1.9921875
+    opts = vc.v_opts(True, 2, 1, seed, 0.0)
+    lay = vc.vc_workspace_layout(v, opts)
+    ws = torch.zeros((lay.total,), dtype=torch.uint8, device="cuda")
+    vc.vc_prepare_v(v, opts, ws)
+    torch.cuda.synchronize()
+    assign = ws[lay.assign:lay.assign + 4 * S].view(torch.int32).cpu().numpy()
+    perm = ws[lay.perm:lay.perm + 4 * S].view(torch.int32).cpu().numpy()
+    want = np.zeros(S, np.int32)
+    want[lo:hi] = 1
+    assert np.array_equal(assign, want), f"{int((assign != want).sum())} tokens in the wrong cluster"
+    want_perm = np.concatenate([np.arange(0, lo), np.arange(hi, S), np.arange(lo, hi)]).astype(np.int32)
+    assert np.array_equal(perm, want_perm)
+    del v, ws
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("smooth", [0, 1])
 def test_plain_and_smooth_on_outliers(smooth):
     w, q, k, v = _cfg(2, H=2, S=2048)
