@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -67,11 +68,21 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (the attention sources
+    hold no string literal with comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_sources_sha256() -> str:
+    """Hash of the attention kernels' code (comments and blank lines left
+    out, so a comment edit keeps a traffic record taken on the same code)."""
     h = hashlib.sha256()
     for f in ("vc_attn.hip", "vc_common.hpp", "vc_kernels.hpp"):
-        with open(os.path.join(ROOT, "bit_attention_video_vc_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bit_attention_video_vc_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -46,7 +46,14 @@
 //     prepared mu/s_v operands in 16x16x16 bf16 MFMAs (high/low bf16 parts,
 //     three products), instead of 64 fp32 FMAs per tile on the VALU;
 //   * workgroup ids are remapped so each XCD runs consecutive query blocks of
-//     the same head: its 4 MB L2 then serves the K/V stream to all of them.
+//     the same head: its 4 MB L2 then serves the K/V stream to all of them;
+//   * one workgroup fills a compute unit (its LDS), so work items run in
+//     rounds of 256.  The items of a partial last round (all of them, when a
+//     launch has fewer) are cut along the key axis into pieces of whole
+//     16-tile groups (k_vc_attn_tail); each piece leaves unnormalised O, row
+//     sums and its reference exponent in a partial slot, and k_vc_attn_merge
+//     adds an item's pieces with power-of-two weights, the online softmax's
+//     own rescale.
 #include "vc_common.hpp"
 #include "vc_kernels.hpp"
 
