@@ -36,8 +36,8 @@ def log(msg: str) -> None:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, help="synthetic workload id (3, 4 or 5)")
     ap.add_argument("--heads", type=int, default=None, help="override H (config 4: 7, 14 or 56)")
     ap.add_argument("--seq", type=int, default=None, help="override S")
