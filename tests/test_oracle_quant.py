@@ -78,6 +78,10 @@ def test_repair_set_is_worst_rounded_tokens():
 
 
 def test_repair_count():
-    assert O.repair_count(0.005, 32768) == 164
+    # ceil(beta * S) with beta as the fp32 the call carries
+    assert O.repair_count(0.005, 32768) == 164          # 163.84 -> 164
     assert O.repair_count(0.0, 32768) == 0
-    assert O.repair_count(0.5, 3) == 2
+    assert O.repair_count(0.5, 3) == 2                  # 1.5 -> 2
+    assert O.repair_count(0.0011, 1000) == 2            # fp32 0.0011 * 1000 = 1.09999... -> 2, not 1
+    assert O.repair_count(0.25, 8) == 2                 # exact: no rounding up
+    assert O.repair_count(0.999, 10) == 10              # capped at S
