@@ -915,9 +915,20 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int bh, int qp, in
     const float* rks = a.rep_ks + static_cast<int64_t>(bh) * a.nrep_pad;
     for (int rt = 0; rt < a.nrep_pad / kBlock; ++rt) {
       v8i Pr[2];
+      // the tile's K operands and key scales are loaded together (one round
+      // trip from global memory rather than one per sub-tile)
+      v8i kops[8];
+      float4 ksc[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const v8i kop = ld_op_global(rk + static_cast<int64_t>(rt) * kTileBytes, t, lane_p);
+        kops[t] = ld_op_global(rk + static_cast<int64_t>(rt) * kTileBytes, t, lane_p);
+        ksc[t] = *reinterpret_cast<const float4*>(rks + rt * kBlock + 16 * t + 4 * g_p);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const v8i kop = kops[t];
+        const float kst[4] = {ksc[t].x, ksc[t].y, ksc[t].z, ksc[t].w};
         const v4f s0 = mfma_fp8(kop, qop[0], zero);
         const v4f s1 = mfma_fp8(kop, qop[1], zero);
         uint32_t w0 = 0, w1 = 0;
@@ -926,7 +937,7 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int bh, int qp, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = rt * kBlock + 16 * t + 4 * g_p + i;
-          const float sig = ((sqs * rks[j]) * a.sm_scale) * kLog2e;
+          const float sig = ((sqs * kst[i]) * a.sm_scale) * kLog2e;
           // (the ExpCast constants written out: as calls of cast_scale and
           // cast_const the register allocation of the whole kernel spills)
           const float s8j = j < nrep ? 8.0f * sig : 0.0f;
@@ -943,7 +954,7 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int bh, int qp, in
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const int j = rt * kBlock + 16 * t + 4 * g_p + i + k;
-            const float sig = ((sqs * rks[j]) * a.sm_scale) * kLog2e;
+            const float sig = ((sqs * kst[i + k]) * a.sm_scale) * kLog2e;
             sa[k] = j < nrep ? cast_scale(sig) : 0.0f;
             b0[k] = j < nrep ? cast_const(st.M[0]) : kCastOff;
             b1[k] = j < nrep ? cast_const(st.M[1]) : kCastOff;
@@ -955,9 +966,14 @@ __device__ __forceinline__ void attn_piece(const AttnArgs& a, int bh, int qp, in
         Pr[0][t] = static_cast<int>(w0);
         Pr[1][t] = static_cast<int>(w1);
       }
+      // likewise the tile's eight error operands
+      v8i eops[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) eops[dt] = ld_op_global(re + static_cast<int64_t>(rt) * kTileBytes, dt, lane_p);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const v8i eop = ld_op_global(re + static_cast<int64_t>(rt) * kTileBytes, dt, lane_p);
+        const v8i eop = eops[dt];
         // codes against M, accumulators against the anchor
         const v4f o0 = mfma_fp8_sb<0>(eop, Pr[0], zero, st.se);
         const v4f o1 = mfma_fp8_sb<1>(eop, Pr[1], zero, st.se);
@@ -1026,13 +1042,15 @@ __device__ __forceinline__ int xcd_order(int total, int wg) {
   __shared__ __align__(16) uint8_t grp1[kGrpBytes]; /* and odd groups */            \
   const AttnLds L = {kbuf0, kbuf1, kbuf2, kbuf3, vbuf0, vbuf1, vbuf2, vbuf3, grp0, grp1}
 
-// Whole work items: (b,h) and query-block pair, in XCD-aware order.
-template <int VF>
+// Whole work items: (b,h) and query-block pair, in XCD-aware order.  REPAIR:
+// the workspace has a repair set (the repair tiles follow the main loop);
+// without one the kernel is built without that code.
+template <int VF, bool REPAIR>
 __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_fwd(AttnArgs a) {
   VC_ATTN_LDS_DECL(VF);
   const int npair = (a.nblk + 1) >> 1;
   const int item = xcd_order(a.whole, blockIdx.x);
-  attn_piece<VF, true>(a, item / npair, item - (item / npair) * npair, 0, a.nblk, nullptr, L);
+  attn_piece<VF, REPAIR>(a, item / npair, item - (item / npair) * npair, 0, a.nblk, nullptr, L);
 }
 
 // The cut items, launched after the whole ones: workgroup t runs groups
@@ -1129,10 +1147,13 @@ __global__ void __launch_bounds__(256) k_vc_attn_merge(AttnArgs a, AttnTail tl) 
 hipError_t launch_attention(const AttnArgs& a, const AttnTail& tl, hipStream_t st) {
   const bool fp4 = a.v_format == VC_V_MXFP4;
   if (a.whole > 0) {
+    // (MXFP4 workspaces have no repair set)
     if (fp4)
-      hipLaunchKernelGGL(k_vc_attn_fwd<VC_V_MXFP4>, dim3(a.whole), dim3(kAttnThreads), 0, st, a);
+      hipLaunchKernelGGL((k_vc_attn_fwd<VC_V_MXFP4, false>), dim3(a.whole), dim3(kAttnThreads), 0, st, a);
+    else if (a.nrep_pad > 0)
+      hipLaunchKernelGGL((k_vc_attn_fwd<VC_V_E4M3, true>), dim3(a.whole), dim3(kAttnThreads), 0, st, a);
     else
-      hipLaunchKernelGGL(k_vc_attn_fwd<VC_V_E4M3>, dim3(a.whole), dim3(kAttnThreads), 0, st, a);
+      hipLaunchKernelGGL((k_vc_attn_fwd<VC_V_E4M3, false>), dim3(a.whole), dim3(kAttnThreads), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
