@@ -461,17 +461,22 @@ __global__ void __launch_bounds__(256) k_v_block_stats(TensorArg v, int S, int s
     mn[e] = 3.0e38f;
     mx[e] = -3.0e38f;
   }
+  // All eight row loads go out before any is used (rows past the block's end re-read its last row and
+  // are not counted), so a thread keeps eight gathers in flight.
+  float x[kBlock / 16][8];
 #pragma unroll
   for (int u = 0; u < kBlock / 16; ++u) {
     const int j = rg + 16 * u;
-    if (j < n) {
-      float x[8];
-      load8_t<DT>(v.p, b * v.sB + static_cast<int64_t>(pp[j]) * v.sS + h * v.sH + 8 * cg, x);
+    load8_t<DT>(v.p, b * v.sB + static_cast<int64_t>(pp[j < n ? j : n - 1]) * v.sS + h * v.sH + 8 * cg, x[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kBlock / 16; ++u) {
+    if (rg + 16 * u < n) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        sum[e] += static_cast<double>(x[e]);
-        mn[e] = fminf(mn[e], x[e]);
-        mx[e] = fmaxf(mx[e], x[e]);
+        sum[e] += static_cast<double>(x[u][e]);
+        mn[e] = fminf(mn[e], x[u][e]);
+        mx[e] = fmaxf(mx[e], x[u][e]);
       }
     }
   }
@@ -540,8 +545,29 @@ __device__ __forceinline__ void store_tr_tile(const uint8_t* codes /*[128][128] 
   }
 }
 
+// The tile's gathered rows for one thread: rows t>>4 for t = tid, tid + 256, ... (16 threads of 8
+// channels per row).  All permutation reads, then all row loads, go out before any is used; a row past
+// the end of the sequence re-reads the tile's first row and is flagged dead.
+constexpr int kPackIt = kBlock * 16 / 256;
+template <int DT>
+__device__ __forceinline__ void gather_tile_rows(const TensorArg& v, int S, const int32_t* perm, int b, int h,
+                                                 int bh, int blk, float (&x)[kPackIt][8], bool (&live)[kPackIt]) {
+  const int c8 = (threadIdx.x & 15) * 8;
+  int s[kPackIt];
+#pragma unroll
+  for (int it = 0; it < kPackIt; ++it) {
+    const int p = blk * kBlock + ((threadIdx.x + 256 * it) >> 4);
+    live[it] = p < S;
+    s[it] = perm[static_cast<int64_t>(bh) * S + (live[it] ? p : blk * kBlock)];
+  }
+#pragma unroll
+  for (int it = 0; it < kPackIt; ++it)
+    load8_t<DT>(v.p, b * v.sB + static_cast<int64_t>(s[it]) * v.sS + h * v.sH + c8, x[it]);
+}
+
 // E4M3 residual codes, written as transposed tiles; mu' = mu / s_v.
 // grid (nblk, H, B), 256 threads.
+template <int DT>
 __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const int32_t* perm, const float* v_mean,
                                                       vc_head_hdr* hdr, uint8_t* v8, uint8_t* v_muop) {
   __shared__ __align__(16) uint8_t codes[kTileBytes];
@@ -567,17 +593,19 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
     hdr[bh].v_scale = s_v;
     hdr[bh].v_inv = inv;
   }
+  float x[kPackIt][8];
+  bool live[kPackIt];
+  gather_tile_rows<DT>(v, S, perm, b, h, bh, blk, x, live);
   __syncthreads();
-  for (int t = threadIdx.x; t < kBlock * 16; t += blockDim.x) {
-    const int j = t >> 4, c8 = (t & 15) * 8;
-    const int p = blk * kBlock + j;
-    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (p < S) {
-      const int s = perm[static_cast<int64_t>(bh) * S + p];
-      float x[8], r[8];
-      load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
+  const int c8 = (threadIdx.x & 15) * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = (x[e] - mu[c8 + e]) * inv;
+  for (int it = 0; it < kPackIt; ++it) {
+    const int j = (threadIdx.x + 256 * it) >> 4;
+    uint32_t c[2] = {0u, 0u};
+    if (live[it]) {
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = (x[it][e] - mu[c8 + e]) * inv;
       c[0] = e4m3_pack4(r[0], r[1], r[2], r[3]);
       c[1] = e4m3_pack4(r[4], r[5], r[6], r[7]);
     }
@@ -614,6 +642,7 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   const int e = k - (m <= 0.75f ? 3 : 2);
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
+template <int DT>
 __global__ void __launch_bounds__(256) k_v_quant_pack_fp4(TensorArg v, int S, const int32_t* perm,
                                                           const float* v_mean, vc_head_hdr* hdr, uint8_t* v8,
                                                           uint8_t* v_muop) {
@@ -637,20 +666,16 @@ __global__ void __launch_bounds__(256) k_v_quant_pack_fp4(TensorArg v, int S, co
     hdr[bh].v_scale = 1.0f;
     hdr[bh].v_inv = 1.0f;
   }
+  float x[kPackIt][8];
+  bool live[kPackIt];
+  gather_tile_rows<DT>(v, S, perm, b, h, bh, blk, x, live);
   __syncthreads();
-  for (int t = threadIdx.x; t < kBlock * 16; t += blockDim.x) {
-    const int j = t >> 4, c8 = (t & 15) * 8;
-    const int p = blk * kBlock + j;
-    float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (p < S) {
-      const int s = perm[static_cast<int64_t>(bh) * S + p];
-      float x[8];
-      load8(v.p, b * v.sB + s * v.sS + h * v.sH + c8, v.dtype, x);
+  const int c8 = (threadIdx.x & 15) * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = x[e] - mu[c8 + e];
-    }
+  for (int it = 0; it < kPackIt; ++it) {
+    const int j = (threadIdx.x + 256 * it) >> 4;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) res[j][c8 + e] = r[e];
+    for (int e = 0; e < 8; ++e) res[j][c8 + e] = live[it] ? x[it][e] - mu[c8 + e] : 0.0f;
   }
   __syncthreads();
   uint8_t* tile = v8 + (static_cast<int64_t>(bh) * nblk + blk) * kTileBytes;
@@ -680,34 +705,40 @@ __global__ void __launch_bounds__(256) k_v_quant_pack_fp4(TensorArg v, int S, co
 // [0, S) -- a workspace that vc_prepare_v did not write for this shape --
 // reads as a zero row instead of an address outside the tensor.
 // grid (nblk, H, B), 256 threads; 4 (row, 16-channel) tasks per thread.
-template <bool GATHER>
+// All four row loads of a thread go out before any is used: a dead row (past the end, or a bad
+// permutation entry) reads token 0 and is zeroed afterwards.
+template <bool GATHER, int DT>
 __global__ void __launch_bounds__(256) k_quant_rows(TensorArg x, int S, const int32_t* perm, int relabel,
                                                     uint8_t* out8, float* scale) {
   __shared__ float red[16];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
   float val[4][16];
+  bool live[4];
+  int s[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = (threadIdx.x + 256 * it) >> 3;
+    const int p = blk * kBlock + (GATHER && relabel ? mx_pos_of_slot(r) : r);
+    live[it] = p < S;
+    s[it] = p;
+    if (GATHER) s[it] = perm[static_cast<int64_t>(bh) * S + (live[it] ? p : blk * kBlock)];
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    if (GATHER) live[it] = live[it] && static_cast<unsigned>(s[it]) < static_cast<unsigned>(S);
+    const int c16 = (threadIdx.x & 7) * 16;
+    const int64_t off = b * x.sB + static_cast<int64_t>(live[it] ? s[it] : 0) * x.sS + h * x.sH + c16;
+    load8_t<DT>(x.p, off, &val[it][0]);
+    load8_t<DT>(x.p, off + 8, &val[it][8]);
+  }
   float m = 0.0f;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int task = threadIdx.x + 256 * it;
-    const int r = task >> 3, c16 = (task & 7) * 16;
-    const int p = blk * kBlock + (GATHER && relabel ? mx_pos_of_slot(r) : r);
-    int s = p;
-    bool live = p < S;
-    if (GATHER && live) {
-      s = perm[static_cast<int64_t>(bh) * S + p];
-      live = static_cast<unsigned>(s) < static_cast<unsigned>(S);
-    }
-    if (live) {
-      const int64_t off = b * x.sB + s * x.sS + h * x.sH + c16;
-      load8(x.p, off, x.dtype, &val[it][0]);
-      load8(x.p, off + 8, x.dtype, &val[it][8]);
-    } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) val[it][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) {
+      val[it][e] = live[it] ? val[it][e] : 0.0f;
+      m = fmaxf(m, fabsf(val[it][e]));
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(val[it][e]));
   }
   m = block_max(m, red);
   const float inv = m > 0.0f ? 448.0f / m : 1.0f;
@@ -1063,11 +1094,13 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
   hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws.v_muop), 0u,
                      static_cast<int64_t>(BH) * muop_rows(nblk) * (kMuOpRowBytes / 4));
   VC_LAUNCH_CHECK();
+  const bool bf16 = v.dtype == VC_BF16;
   if (o.v_format == VC_V_MXFP4)
-    hipLaunchKernelGGL(k_v_quant_pack_fp4, gblk, dim3(256), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.v8,
-                       ws.v_muop);
+    hipLaunchKernelGGL(bf16 ? k_v_quant_pack_fp4<VC_BF16> : k_v_quant_pack_fp4<VC_F16>, gblk, dim3(256), 0, st, v, S,
+                       ws.perm, ws.v_mean, ws.hdr, ws.v8, ws.v_muop);
   else
-    hipLaunchKernelGGL(k_v_quant_pack, gblk, dim3(256), 0, st, v, S, ws.perm, ws.v_mean, ws.hdr, ws.v8, ws.v_muop);
+    hipLaunchKernelGGL(bf16 ? k_v_quant_pack<VC_BF16> : k_v_quant_pack<VC_F16>, gblk, dim3(256), 0, st, v, S, ws.perm,
+                       ws.v_mean, ws.hdr, ws.v8, ws.v_muop);
   VC_LAUNCH_CHECK();
   if (ws.nrep > 0) {
     const dim3 grep(ws.nrep_pad / kBlock, H, B);
@@ -1090,10 +1123,11 @@ hipError_t launch_prepare_qk(const TensorArg& q, const TensorArg& kt, int B, int
                              const WsPtrs& ws, hipStream_t st) {
   const int nblk = (S + kBlock - 1) / kBlock;
   const dim3 gblk(nblk, H, B);
-  hipLaunchKernelGGL((k_quant_rows<false>), gblk, dim3(256), 0, st, q, S, ws.perm, 0, ws.q8, ws.q_scale);
+  hipLaunchKernelGGL((q.dtype == VC_BF16 ? k_quant_rows<false, VC_BF16> : k_quant_rows<false, VC_F16>), gblk,
+                     dim3(256), 0, st, q, S, ws.perm, 0, ws.q8, ws.q_scale);
   VC_LAUNCH_CHECK();
-  hipLaunchKernelGGL((k_quant_rows<true>), gblk, dim3(256), 0, st, kt, S, ws.perm, v_format == VC_V_MXFP4 ? 1 : 0,
-                     ws.k8, ws.k_scale);
+  hipLaunchKernelGGL((kt.dtype == VC_BF16 ? k_quant_rows<true, VC_BF16> : k_quant_rows<true, VC_F16>), gblk,
+                     dim3(256), 0, st, kt, S, ws.perm, v_format == VC_V_MXFP4 ? 1 : 0, ws.k8, ws.k_scale);
   VC_LAUNCH_CHECK();
   if (ws.nrep > 0) {
     hipLaunchKernelGGL(k_repair_kpack, dim3(ws.nrep_pad / kBlock, H, B), dim3(256), 0, st, S, ws.nrep_pad,
