@@ -66,34 +66,38 @@ __device__ __forceinline__ float sketch1(float x, int shift) {
   return fminf(fmaxf(rintf(ldexpf(x, shift)), -255.0f), 255.0f);
 }
 
-// Centroid operands and squared norms for the assignment pass, from the
-// integer centroids of one (b,h) (exact: |c| <= 255 fits bf16, norms < 2^24).
-// Called by a whole block after the centroids are final; `nthr` threads.
-__device__ void write_cent_ops(int bh, int k, const int32_t* cg, uint8_t* cent_op, int32_t* cnorm, int nthr,
-                               int c0 = 0, int c1 = kMaxK) {
-  // operands and norms of centroids c0 .. c1-1 (c >= k: absent, zero operand)
+// Centroid operands and squared norms for the assignment pass, for
+// centroids c0 .. c1-1 of one (b,h) (c >= k: absent, zero operand, norm
+// 0x7FFFFFFF), from their integer values in LDS, cl[(c - c0) * kD + d]
+// (exact: |c| <= 255 fits bf16, norms < 2^24).  Called by a whole block of
+// 256 threads after cl is written and a barrier.
+__device__ void write_cent_ops(int bh, int k, const int32_t* cl, int c0, int c1, uint8_t* cent_op, int32_t* cnorm) {
   uint8_t* op = cent_op + static_cast<int64_t>(bh) * kCentOpBytes;
-  for (int u = threadIdx.x; u < 4 * 4 * 64; u += nthr) {
-    const int ct = u >> 8, kk = (u >> 6) & 3, lane = u & 63;
-    const int c = 16 * ct + (lane & 15), d0 = 32 * kk + 8 * (lane >> 4);
-    if (c < c0 || c >= c1) continue;
-    uint32_t w[4];
+  // task t: centroid c0 + t/16, 8 channels d0 = 32kk + 8g; operand slot
+  // u = 256(c/16) + 64kk + 16g + c%16
+  for (int t = threadIdx.x; t < (c1 - c0) * 16; t += 256) {
+    const int c = c0 + (t >> 4), kk = (t >> 2) & 3, g = t & 3, d0 = 32 * kk + 8 * g;
+    const int u = 256 * (c >> 4) + 64 * kk + 16 * g + (c & 15);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (c < k) {
+      const int4 lo = *reinterpret_cast<const int4*>(cl + (c - c0) * kD + d0);
+      const int4 hi = *reinterpret_cast<const int4*>(cl + (c - c0) * kD + d0 + 4);
+      const int x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = c < k ? static_cast<float>(cg[c * kD + d0 + 2 * i]) : 0.0f;
-      const float hi = c < k ? static_cast<float>(cg[c * kD + d0 + 2 * i + 1]) : 0.0f;
-      w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);   // exact: small integers
+      for (int i = 0; i < 4; ++i)   // exact: small integers
+        w[i] = (__float_as_uint(static_cast<float>(x[2 * i])) >> 16) |
+               (__float_as_uint(static_cast<float>(x[2 * i + 1])) & 0xFFFF0000u);
     }
     *reinterpret_cast<uint4*>(op + static_cast<int64_t>(u) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   // squared norms, one wave per centroid at a time: lane l adds dims 2l, 2l+1
   // (exact integers, so the order of the sum does not matter)
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nwv = nthr >> 6;
-  for (int c = c0 + wv; c < c1; c += nwv) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int c = c0 + wv; c < c1; c += 4) {
     int32_t n2 = 0x7FFFFFFF;                    // absent centroid: never the minimum
     if (c < k) {
-      const int32_t a = cg[c * kD + 2 * lane], b = cg[c * kD + 2 * lane + 1];
-      n2 = a * a + b * b;
+      const int2 ab = *reinterpret_cast<const int2*>(cl + (c - c0) * kD + 2 * lane);
+      n2 = ab.x * ab.x + ab.y * ab.y;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) n2 += __shfl_xor(n2, o, 64);
     }
@@ -101,7 +105,10 @@ __device__ void write_cent_ops(int bh, int k, const int32_t* cg, uint8_t* cent_o
   }
 }
 
-// Sketch shift and seeded strided initial centroids.  grid (BH), 256 threads.
+// Sketch shift and seeded strided initial centroids.  grid (BH), 256 threads;
+// a thread takes 8 consecutive channels of 4 centroids (16-byte loads, all
+// issued before the first store; an absent centroid re-reads the last one).
+template <int DT>
 __global__ void __launch_bounds__(256) k_kmeans_init(TensorArg v, int S, int H, int k, uint64_t seed,
                                                      vc_head_hdr* hdr, int32_t* cent, int64_t* csum,
                                                      int32_t* ccount, uint8_t* cent_op, int32_t* cnorm) {
@@ -116,27 +123,38 @@ __global__ void __launch_bounds__(256) k_kmeans_init(TensorArg v, int S, int H, 
   if (tid == 0) hdr[bh].shift = shift;
   const int stride = S / k > 1 ? S / k : 1;
   const int phi = static_cast<int>(splitmix64(seed ^ static_cast<uint64_t>(bh)) % static_cast<uint64_t>(stride));
-  // (centroid c, dim d) pairs i = 128c + d, 32 per thread; every load is
-  // issued before the first store (c*S < 2^31 for S <= 2^24, k <= 64)
-  constexpr int kPer = kMaxK * kD / 256;
-  float xs[kPer];
+  // task u = 16c + (d/8): centroid c, channels d .. d+7 (c*S < 2^31 for
+  // S <= 2^24, k <= 64)
+  __shared__ __align__(16) int32_t cl[kMaxK * kD];
+  constexpr int kPer = kMaxK * (kD / 8) / 256;
+  float xs[kPer][8];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int i = tid + 256 * j, c = i >> 7, d = i & (kD - 1);
-    const int t = (c * S) / k + phi;
-    xs[j] = c < k ? load1(v.p, b * v.sB + static_cast<int64_t>(t) * v.sS + h * v.sH + d, v.dtype) : 0.0f;
+    const int u = tid + 256 * j, c = u >> 4, d8 = (u & 15) * 8;
+    const int t = ((c < k ? c : k - 1) * S) / k + phi;
+    load8_t<DT>(v.p, b * v.sB + static_cast<int64_t>(t) * v.sS + h * v.sH + d8, xs[j]);
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int i = tid + 256 * j, c = i >> 7;
+    const int u = tid + 256 * j, c = u >> 4, d8 = (u & 15) * 8;
     if (c < k) {
-      cent[static_cast<int64_t>(bh) * k * kD + i] = static_cast<int32_t>(sketch1(xs[j], shift));
-      csum[static_cast<int64_t>(bh) * k * kD + i] = 0;     // clears both widths (wide_sums)
+      int32_t q[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = static_cast<int32_t>(sketch1(xs[j][e], shift));
+      int32_t* cp = cent + static_cast<int64_t>(bh) * k * kD + c * kD + d8;
+      *reinterpret_cast<int4*>(cp) = make_int4(q[0], q[1], q[2], q[3]);
+      *reinterpret_cast<int4*>(cp + 4) = make_int4(q[4], q[5], q[6], q[7]);
+      *reinterpret_cast<int4*>(cl + c * kD + d8) = make_int4(q[0], q[1], q[2], q[3]);
+      *reinterpret_cast<int4*>(cl + c * kD + d8 + 4) = make_int4(q[4], q[5], q[6], q[7]);
+      // clears both widths (wide_sums)
+      int4* sp = reinterpret_cast<int4*>(csum + static_cast<int64_t>(bh) * k * kD + c * kD + d8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[e] = make_int4(0, 0, 0, 0);
     }
   }
   if (tid < k) ccount[bh * k + tid] = 0;
   __syncthreads();
-  write_cent_ops(bh, k, cent + static_cast<int64_t>(bh) * k * kD, cent_op, cnorm, 256);
+  write_cent_ops(bh, k, cl, 0, kMaxK, cent_op, cnorm);
 }
 
 // One Lloyd assignment pass over asg (asg_tokens: 256..1024) tokens per workgroup.
@@ -314,27 +332,49 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
 // fp64 quotient lies on the same side of every integer as the exact one
 // (|q| <= 255 and a non-integer quotient is >= 1/(2n) >= 2^-25 from one).
 // grid (BH, ceil(k/8)), 256 threads; a workgroup owns 8 centroids.
+// WIDE = wide_sums(S): the sums' width, fixed per instantiation.
 constexpr int kUpdCent = 8;
-__global__ void __launch_bounds__(256) k_kmeans_update(int S, int k, int32_t* cent, int64_t* csum, int32_t* ccount,
+template <bool WIDE>
+__global__ void __launch_bounds__(256) k_kmeans_update(int k, int32_t* cent, int64_t* csum, int32_t* ccount,
                                                       uint8_t* cent_op, int32_t* cnorm) {
+  __shared__ __align__(16) int32_t cl[kUpdCent * kD];
   const int bh = blockIdx.x;
   const int c0 = blockIdx.y * kUpdCent, c1 = c0 + kUpdCent < k ? c0 + kUpdCent : k;
   int32_t* cg = cent + static_cast<int64_t>(bh) * k * kD;
-  const bool wide = wide_sums(S);
   int64_t* sg = csum + static_cast<int64_t>(bh) * k * kD;
   int32_t* sg32 = reinterpret_cast<int32_t*>(csum) + static_cast<int64_t>(bh) * k * kD;
-  for (int i = c0 * kD + threadIdx.x; i < c1 * kD; i += blockDim.x) {
-    const int32_t n = ccount[bh * k + i / kD];
-    if (n > 0) {
-      const int64_t num = 2 * (wide ? sg[i] : static_cast<int64_t>(sg32[i])) + n;
-      cg[i] = static_cast<int32_t>(floor(static_cast<double>(num) / static_cast<double>(2 * n)));
+  // value i = c0*kD + tid + 256j of the block's centroids; every load is
+  // issued before the first use (a value past c1 re-reads the block's first)
+  constexpr int kPer = kUpdCent * kD / 256;
+  int32_t n[kPer], old[kPer];
+  int64_t sm[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int r = threadIdx.x + 256 * j;
+    const int i = c0 * kD + (r < (c1 - c0) * kD ? r : 0);
+    n[j] = ccount[bh * k + i / kD];
+    old[j] = cg[i];
+    sm[j] = WIDE ? sg[i] : static_cast<int64_t>(sg32[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int r = threadIdx.x + 256 * j;
+    if (r < (c1 - c0) * kD) {
+      const int i = c0 * kD + r;
+      int32_t c = old[j];
+      if (n[j] > 0) {
+        const int64_t num = 2 * sm[j] + n[j];
+        c = static_cast<int32_t>(floor(static_cast<double>(num) / static_cast<double>(2 * n[j])));
+        cg[i] = c;
+      }
+      cl[r] = c;
+      if (WIDE) sg[i] = 0;
+      else sg32[i] = 0;
     }
-    if (wide) sg[i] = 0;
-    else sg32[i] = 0;
   }
   __syncthreads();
   if (threadIdx.x < c1 - c0) ccount[bh * k + c0 + threadIdx.x] = 0;
-  write_cent_ops(bh, k, cg, cent_op, cnorm, 256, c0, c1);
+  write_cent_ops(bh, k, cl, c0, c1, cent_op, cnorm);
 }
 
 // Per-cluster start offsets and per-chunk offsets for the stable scatter.
@@ -1062,15 +1102,15 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
     const int nch = (S + asg - 1) / asg;
     hipLaunchKernelGGL(k_v_absmax, dim3((S + kAbsTok - 1) / kAbsTok, H, B), dim3(256), 0, st, v, S, ws.hdr);
     VC_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_kmeans_init, dim3(BH), dim3(256), 0, st, v, S, H, k, o.seed, ws.hdr, ws.cent, ws.csum,
-                       ws.ccount, ws.cent_op, ws.cnorm);
+    hipLaunchKernelGGL((v.dtype == VC_BF16 ? k_kmeans_init<VC_BF16> : k_kmeans_init<VC_F16>), dim3(BH), dim3(256), 0,
+                       st, v, S, H, k, o.seed, ws.hdr, ws.cent, ws.csum, ws.ccount, ws.cent_op, ws.cnorm);
     VC_LAUNCH_CHECK();
     for (int it = 0; it < o.iters; ++it) {
       launch_assign<true, false>(dim3(nch, H, B), st, v, S, k, asg, ws);
       VC_LAUNCH_CHECK();
-      hipLaunchKernelGGL(k_kmeans_update, dim3(BH, (k + kUpdCent - 1) / kUpdCent), dim3(256), 0, st, S, k, ws.cent,
-                         ws.csum, ws.ccount, ws.cent_op,
-                         ws.cnorm);
+      hipLaunchKernelGGL((wide_sums(S) ? k_kmeans_update<true> : k_kmeans_update<false>),
+                         dim3(BH, (k + kUpdCent - 1) / kUpdCent), dim3(256), 0, st, k, ws.cent, ws.csum, ws.ccount,
+                         ws.cent_op, ws.cnorm);
       VC_LAUNCH_CHECK();
     }
     launch_assign<false, true>(dim3(nch, H, B), st, v, S, k, asg, ws);
