@@ -169,7 +169,13 @@ __global__ void __launch_bounds__(256) k_kmeans_init(TensorArg v, int S, int H, 
 // l%16: an in-lane argmin over its centroids and a 4-lane combine give the
 // cluster, ties to the lowest index.  grid (ceil(S/asg), H, B), 256 threads.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-constexpr int kSumPitch = kD + 1;   // padded LDS pitch of the per-cluster sums
+// Per-cluster sums in LDS, two channels per 64-bit word: each 32-bit half
+// sums t + 256 over the block's tokens of the cluster (t the sketch value,
+// so t + 256 is in [1, 511]; at most 1024 tokens per block keep a half below
+// 2^19, so no carry crosses into the other half).  One 64-bit LDS add then
+// takes two channels; the bias, 256 per token, comes off when the block's
+// sums go out.
+constexpr int kPairPitch = kD / 2 + 1;   // padded LDS pitch of a cluster's sums, in 64-bit words
 
 __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -189,22 +195,50 @@ __device__ __forceinline__ TokRaw load_tok(const TensorArg& v, int b, int h, int
                     : make_uint4(0, 0, 0, 0);
   return t;
 }
-// The sketch value (an integer in [-255, 255], so exact in bf16) of the two
-// fp16/bf16 elements of a dword, as a packed pair of bf16 (element order
-// kept).  DT is the input type, fixed per instantiation so the conversion
-// has no branch.
-template <int DT>
-__device__ __forceinline__ float sketch_f32(uint32_t half_bits, int shift) {
-  const float x = DT == VC_BF16 ? __uint_as_float(half_bits) : f16_bits_to_f32(half_bits);
-  return __builtin_amdgcn_fmed3f(rintf(ldexpf(x, shift)), -255.0f, 255.0f);
-}
-template <int DT>
-__device__ __forceinline__ uint32_t sketch_pair(uint32_t w, int shift) {
+
+// The sketch t = clamp(rne(x * 2^shift), -255, 255) by one FMA:
+// y = fma(x, 2^shift, kSkMagic), kSkMagic = 1.5*2^23 + 256.  The FMA rounds
+// once, to nearest even, and kSkMagic is an even integer, so y = kSkMagic +
+// rne(x * 2^shift); |x * 2^shift| < 256 (shift = 7 - floor(log2 max|x|))
+// keeps y in [2^23, 2^24), where floats are spaced by 1, so y - kSkMagic = t
+// and bits(y) - bits(1.5*2^23) = t + 256, both exact.  For bf16 the clamp
+// never acts: a bf16 value in [128, 256) is an integer, so rne stays <= 255;
+// fp16 values in [255.5, 256) do round to 256 and are clamped.  2^shift is a
+// float for shift <= 127; a bf16 head with max|x| < 2^-120 (shift > 127)
+// first scales x by 2^(shift - 127) (exact: x only grows), the BIG form.
+constexpr float kSkMagic = 12583168.0f;     // 1.5 * 2^23 + 256
+constexpr int32_t kSkBase = 0x4B400000;     // bits of 1.5 * 2^23
+template <bool B> struct BigTag {
+  static constexpr bool value = B;
+};
+struct SketchScale {
+  float sc;    // 2^min(shift, 127)
+  float pre;   // 2^(shift - 127) when shift > 127
+};
+// Two elements of a dword (element order kept): the bf16 pair of t (the
+// assignment operand) and, for the sums, t + 256 of each.
+template <int DT, bool BIG>
+__device__ __forceinline__ uint32_t sketch_word(uint32_t w, const SketchScale& k, uint32_t& ulo, uint32_t& uhi) {
   // bf16: the low element's bits moved up, the high element's masked in place
-  const float lo = sketch_f32<DT>(DT == VC_BF16 ? w << 16 : (w & 0xFFFFu), shift);
-  const float hi = sketch_f32<DT>(DT == VC_BF16 ? (w & 0xFFFF0000u) : (w >> 16), shift);
+  float xlo = DT == VC_BF16 ? __uint_as_float(w << 16) : f16_bits_to_f32(w & 0xFFFFu);
+  float xhi = DT == VC_BF16 ? __uint_as_float(w & 0xFFFF0000u) : f16_bits_to_f32(w >> 16);
+  if (BIG) {
+    xlo *= k.pre;
+    xhi *= k.pre;
+  }
+  const float ylo = fmaf(xlo, k.sc, kSkMagic), yhi = fmaf(xhi, k.sc, kSkMagic);
+  float tlo = ylo - kSkMagic, thi = yhi - kSkMagic;
+  int32_t blo = __float_as_int(ylo) - kSkBase, bhi = __float_as_int(yhi) - kSkBase;
+  if (DT != VC_BF16) {
+    tlo = __builtin_amdgcn_fmed3f(tlo, -255.0f, 255.0f);
+    thi = __builtin_amdgcn_fmed3f(thi, -255.0f, 255.0f);
+    blo = min(max(blo, 1), 511);
+    bhi = min(max(bhi, 1), 511);
+  }
+  ulo = static_cast<uint32_t>(blo);
+  uhi = static_cast<uint32_t>(bhi);
   // the upper halves of the two fp32 values (exact: at most 8 significant bits)
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  return __builtin_amdgcn_perm(__float_as_uint(thi), __float_as_uint(tlo), 0x07060302u);
 }
 
 template <int DT, bool ACCUM, bool FINAL, int NCT>
@@ -212,13 +246,15 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
                                                        const uint8_t* cent_op, const int32_t* cnorm,
                                                        int64_t* csum, int32_t* ccount, int32_t* assign,
                                                        int32_t* chunk_hist) {
-  __shared__ int32_t sums[ACCUM ? kMaxK * kSumPitch : 1];
+  __shared__ uint64_t sums[ACCUM ? kMaxK * kPairPitch : 1];
   __shared__ int32_t cnt[kMaxK];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int shift = hdr[bh].shift;
+  const bool big = DT == VC_BF16 && shift > 127;
+  const SketchScale skc = {ldexpf(1.0f, min(shift, 127)), ldexpf(1.0f, shift - 127)};
   if (ACCUM)
-    for (int i = tid; i < k * kSumPitch; i += 256) sums[i] = 0;
+    for (int i = tid; i < k * kPairPitch; i += 256) sums[i] = 0;
   if (tid < kMaxK) cnt[tid] = 0;
   // centroid operands (prepared with the centroids) and norms
   v8bf ca[NCT][4];
@@ -240,13 +276,19 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
   static_assert(kAsgTokMin % 128 == 0, "the loop below takes token rows in pairs");
   const int kIters = asg / 64;        // asg is a power of two >= kAsgTokMin: even
   // one iteration: 16 tokens per wave (token `tok` in lane group g's dims)
-  auto assign_tokens = [&](const TokRaw& cur, int tok) {
+  auto assign_tokens = [&](auto bigtag, const TokRaw& cur, int tok) {
+    constexpr bool BIG = decltype(bigtag)::value;
     const bool valid = tok < S;
     v8bf xb[4];
+    uint32_t u[4][4][2];   // t + 256 of dword q's two elements (ACCUM)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      xb[kk] = __builtin_bit_cast(v8bf, make_uint4(sketch_pair<DT>(cur.r[kk].x, shift), sketch_pair<DT>(cur.r[kk].y, shift),
-                                                   sketch_pair<DT>(cur.r[kk].z, shift), sketch_pair<DT>(cur.r[kk].w, shift)));
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t wd[4] = {cur.r[kk].x, cur.r[kk].y, cur.r[kk].z, cur.r[kk].w};
+      uint32_t pk[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pk[q] = sketch_word<DT, BIG>(wd[q], skc, u[kk][q][0], u[kk][q][1]);
+      xb[kk] = __builtin_bit_cast(v8bf, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
     v4f acc[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] = zero;
@@ -280,41 +322,52 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
         if (FINAL) assign[static_cast<int64_t>(bh) * S + tok] = bc;
       }
       if (ACCUM) {
+        // channel pair 16kk + 4g + q holds channels 32kk + 8g + 2q, +1
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            atomicAdd(&sums[bc * kSumPitch + 32 * kk + 8 * g + i], static_cast<int32_t>(static_cast<float>(xb[kk][i])));
+          for (int q = 0; q < 4; ++q)
+            atomicAdd(&sums[bc * kPairPitch + 16 * kk + 4 * g + q],
+                      (static_cast<uint64_t>(u[kk][q][1]) << 32) | u[kk][q][0]);
       }
     }
   };
   // two token buffers in turn: the next iteration's loads are in flight
   // while one is processed
-  int tok = s0 + w * 16 + l16;
-  TokRaw b0 = load_tok(v, b, h, tok, tok < S, g), b1;
-  for (int tt = 0; tt < kIters; tt += 2) {
-    b1 = load_tok(v, b, h, tok + 64, tok + 64 < S, g);
-    assign_tokens(b0, tok);
-    if (tt + 2 < kIters) b0 = load_tok(v, b, h, tok + 128, tok + 128 < S, g);
-    assign_tokens(b1, tok + 64);
-    tok += 128;
-  }
+  auto run = [&](auto bigtag) {
+    int tok = s0 + w * 16 + l16;
+    TokRaw b0 = load_tok(v, b, h, tok, tok < S, g), b1;
+    for (int tt = 0; tt < kIters; tt += 2) {
+      b1 = load_tok(v, b, h, tok + 64, tok + 64 < S, g);
+      assign_tokens(bigtag, b0, tok);
+      if (tt + 2 < kIters) b0 = load_tok(v, b, h, tok + 128, tok + 128 < S, g);
+      assign_tokens(bigtag, b1, tok + 64);
+      tok += 128;
+    }
+  };
+  if (big) run(BigTag<true>{});
+  else run(BigTag<false>{});
   __syncthreads();
   if (ACCUM) {
     // a workgroup's sums fit int32 (asg <= 1024 tokens of |x| <= 255); the
     // head's reach 255 * S: 32-bit adds while that fits (S <= 2^23), 64-bit
     // adds beyond (two's complement, so an unsigned add accumulates signed
     // values)
+    auto block_sum = [&](int i) {
+      const int c = i / kD, d = i % kD;
+      const uint64_t wd = sums[c * kPairPitch + (d >> 1)];
+      return static_cast<int32_t>(d & 1 ? wd >> 32 : wd & 0xFFFFFFFFu) - 256 * cnt[c];
+    };
     if (wide_sums(S)) {
       unsigned long long* gs = reinterpret_cast<unsigned long long*>(csum + static_cast<int64_t>(bh) * k * kD);
       for (int i = tid; i < k * kD; i += 256) {
-        const int32_t val = sums[(i / kD) * kSumPitch + (i % kD)];
+        const int32_t val = block_sum(i);
         if (val != 0) atomicAdd(&gs[i], static_cast<unsigned long long>(static_cast<long long>(val)));
       }
     } else {
       int32_t* gs = reinterpret_cast<int32_t*>(csum) + static_cast<int64_t>(bh) * k * kD;
       for (int i = tid; i < k * kD; i += 256) {
-        const int32_t val = sums[(i / kD) * kSumPitch + (i % kD)];
+        const int32_t val = block_sum(i);
         if (val != 0) atomicAdd(&gs[i], val);
       }
     }

@@ -361,6 +361,49 @@ def test_kmeans_sums_past_int32():
     torch.cuda.empty_cache()
 
 
+def test_sketch_rounding_extremes():
+    """The two edges of the k-means sketch x = clamp(rne(v * 2^shift), +-255).
+
+    fp16 V clipped at +-(1 - 2^-11): shift = 8, and the top fp16 values
+    1 - j * 2^-11 (j = 1..4) scale to 255.5 .. 255.875, which round to 256
+    and must clamp to 255 (j = 4 is a tie, to even).  Compared in full."""
+    g = torch.Generator().manual_seed(41)
+    S, H = 700, 2
+    q = torch.randn(1, S, H, 128, generator=g).to(torch.float16)
+    k = torch.randn(1, S, H, 128, generator=g).to(torch.float16)
+    top = 1.0 - 2.0 ** -11
+    v = (torch.randn(1, S, H, 128, generator=g) * 0.6).clamp(-top, top).to(torch.float16)
+    vs = v.float() * 256
+    assert int(((vs.abs() >= 255.5) & (vs.abs() < 256)).sum()) > 1000
+    check_against_oracle(q.cuda(), k.cuda(), v.cuda(), kc=8, iters=3, name="sketch clamp (fp16)")
+
+
+def test_sketch_tiny_bf16_head():
+    """A bf16 head with max|v| < 2^-120 (shift > 127, so 2^shift is no fp32
+    value): the sketch takes its two-step scaling.  Assignments and the
+    permutation are bit-exact against the oracle.  The rest of such a head
+    is not compared: its residual scale 448 / max|v| overflows fp32 on both
+    sides."""
+    g = torch.Generator().manual_seed(43)
+    S = 900
+    v = (torch.randn(1, S, 1, 128, generator=g, dtype=torch.float64) * 2.0 ** -124).to(torch.bfloat16)
+    a = float(v.double().abs().max())
+    assert 0 < a < 2.0 ** -120 and 7 - int(np.floor(np.log2(a))) > 127
+    kc, iters, seed = 12, 3, 4
+    opts = vc.v_opts(True, kc, iters, seed, 0.0)
+    lay = vc.vc_workspace_layout(v, opts)
+    ws = torch.zeros((lay.total,), dtype=torch.uint8, device="cuda")
+    vc.vc_prepare_v(v.cuda(), opts, ws)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore", invalid="ignore"):
+        hv = O.prepare_v_head(_np(v[0, :, 0]), smooth=True, k=kc, iters=iters, seed=seed, bh=0)
+    assign = ws[lay.assign:lay.assign + 4 * S].view(torch.int32).cpu().numpy()
+    perm = ws[lay.perm:lay.perm + 4 * S].view(torch.int32).cpu().numpy()
+    assert len(np.unique(hv.assign)) > 1
+    assert np.array_equal(assign, hv.assign)
+    assert np.array_equal(perm, hv.perm)
+
+
 @pytest.mark.parametrize("smooth", [0, 1])
 def test_plain_and_smooth_on_outliers(smooth):
     w, q, k, v = _cfg(2, H=2, S=2048)
