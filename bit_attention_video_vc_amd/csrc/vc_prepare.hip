@@ -66,10 +66,10 @@ __device__ __forceinline__ float sketch1(float x, int shift) {
   return fminf(fmaxf(rintf(ldexpf(x, shift)), -255.0f), 255.0f);
 }
 
-// Centroid operands and squared norms for the assignment pass, for
-// centroids c0 .. c1-1 of one (b,h) (c >= k: absent, zero operand, norm
-// 0x7FFFFFFF), from their integer values in LDS, cl[(c - c0) * kD + d]
-// (exact: |c| <= 255 fits bf16, norms < 2^24).  Called by a whole block of
+// Centroid operands (2c, so the matrix core yields 2 x.c) and squared norms
+// for the assignment pass, for centroids c0 .. c1-1 of one (b,h) (c >= k:
+// absent, zero operand, norm 0x7FFFFFFF), from their integer values in LDS,
+// cl[(c - c0) * kD + d] (exact: |2c| <= 510 fits bf16, norms < 2^24).  Called by a whole block of
 // 256 threads after cl is written and a barrier.
 __device__ void write_cent_ops(int bh, int k, const int32_t* cl, int c0, int c1, uint8_t* cent_op, int32_t* cnorm) {
   uint8_t* op = cent_op + static_cast<int64_t>(bh) * kCentOpBytes;
@@ -84,9 +84,9 @@ __device__ void write_cent_ops(int bh, int k, const int32_t* cl, int c0, int c1,
       const int4 hi = *reinterpret_cast<const int4*>(cl + (c - c0) * kD + d0 + 4);
       const int x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)   // exact: small integers
-        w[i] = (__float_as_uint(static_cast<float>(x[2 * i])) >> 16) |
-               (__float_as_uint(static_cast<float>(x[2 * i + 1])) & 0xFFFF0000u);
+      for (int i = 0; i < 4; ++i)   // 2c: exact, at most 8 significant bits
+        w[i] = (__float_as_uint(static_cast<float>(2 * x[2 * i])) >> 16) |
+               (__float_as_uint(static_cast<float>(2 * x[2 * i + 1])) & 0xFFFF0000u);
     }
     *reinterpret_cast<uint4*>(op + static_cast<int64_t>(u) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -160,14 +160,17 @@ __global__ void __launch_bounds__(256) k_kmeans_init(TensorArg v, int S, int H, 
 // One Lloyd assignment pass over asg (asg_tokens: 256..1024) tokens per workgroup.
 //   ACCUM: add the block's per-cluster sketch sums and counts to csum/ccount.
 //   FINAL: write assign[] and the block's cluster histogram (for the sort).
-// Distances run on the matrix core: scores^T = C . X^T with
-// v_mfma_f32_16x16x32_bf16, centroids as the A operand (held in registers
-// for the whole block), 16 tokens as the B operand.  Sketch values and
-// centroids are integers in [-255, 255], exact in bf16; every dot product
-// is an integer below 2^24, so the fp32 accumulation is exact in any order.
-// Lane l then holds the scores of centroids 16ct + 4(l/16) + i for token
-// l%16: an in-lane argmin over its centroids and a 4-lane combine give the
-// cluster, ties to the lowest index.  grid (ceil(S/asg), H, B), 256 threads.
+// Distances run on the matrix core: (2C) . X^T with
+// v_mfma_f32_16x16x32_bf16, doubled centroids as the A operand (held in
+// registers for the whole block), 16 tokens as the B operand; the score of
+// centroid c is ||c||^2 - 2 x.c, which orders as ||x - c||^2 does.  Sketch
+// values and centroids are integers in [-255, 255] (2c in [-510, 510]),
+// exact in bf16; every partial sum of 2 x.c is an integer of magnitude at
+// most 2 * 128 * 255^2 < 2^24, so the fp32 accumulation is exact in any
+// order.  Lane l then holds the scores of centroids 16ct + 4(l/16) + i for
+// token l%16: an in-lane argmin over its centroids and a 4-lane combine give
+// the cluster, ties to the lowest index.  grid (ceil(S/asg), H, B), 256
+// threads.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // Per-cluster sums in LDS, two channels per 64-bit word: each 32-bit half
 // sums t + 256 over the block's tokens of the cluster (t the sketch value,
@@ -182,17 +185,17 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f
 }
 
 // Raw 16-byte loads of one token-tile iteration (16 tokens per wave, lane
-// group g holds dims 32kk + 8g..8g+7).
+// group g holds dims 32kk + 8g..8g+7).  A token past the end reads token
+// S-1 instead (no branch); its result is not used.
 struct TokRaw {
   uint4 r[4];
 };
-__device__ __forceinline__ TokRaw load_tok(const TensorArg& v, int b, int h, int tok, bool valid, int g) {
+__device__ __forceinline__ TokRaw load_tok(const TensorArg& v, int b, int h, int tok, int S, int g) {
   TokRaw t;
+  const uint16_t* row = reinterpret_cast<const uint16_t*>(v.p) + b * v.sB +
+                        static_cast<int64_t>(tok < S ? tok : S - 1) * v.sS + h * v.sH + 8 * g;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    t.r[kk] = valid ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(v.p) + b * v.sB +
-                                                      static_cast<int64_t>(tok) * v.sS + h * v.sH + 32 * kk + 8 * g)
-                    : make_uint4(0, 0, 0, 0);
+  for (int kk = 0; kk < 4; ++kk) t.r[kk] = *reinterpret_cast<const uint4*>(row + 32 * kk);
   return t;
 }
 
@@ -216,9 +219,11 @@ struct SketchScale {
   float pre;   // 2^(shift - 127) when shift > 127
 };
 // Two elements of a dword (element order kept): the bf16 pair of t (the
-// assignment operand) and, for the sums, t + 256 of each.
+// assignment operand) and, for the sums, t + 256 of each as the two halves of
+// one 64-bit word (one 64-bit subtraction: the low half does not borrow).
+constexpr uint64_t kSkBase2 = (static_cast<uint64_t>(kSkBase) << 32) | static_cast<uint32_t>(kSkBase);
 template <int DT, bool BIG>
-__device__ __forceinline__ uint32_t sketch_word(uint32_t w, const SketchScale& k, uint32_t& ulo, uint32_t& uhi) {
+__device__ __forceinline__ uint32_t sketch_word(uint32_t w, const SketchScale& k, uint64_t& u) {
   // bf16: the low element's bits moved up, the high element's masked in place
   float xlo = DT == VC_BF16 ? __uint_as_float(w << 16) : f16_bits_to_f32(w & 0xFFFFu);
   float xhi = DT == VC_BF16 ? __uint_as_float(w & 0xFFFF0000u) : f16_bits_to_f32(w >> 16);
@@ -228,15 +233,14 @@ __device__ __forceinline__ uint32_t sketch_word(uint32_t w, const SketchScale& k
   }
   const float ylo = fmaf(xlo, k.sc, kSkMagic), yhi = fmaf(xhi, k.sc, kSkMagic);
   float tlo = ylo - kSkMagic, thi = yhi - kSkMagic;
-  int32_t blo = __float_as_int(ylo) - kSkBase, bhi = __float_as_int(yhi) - kSkBase;
+  u = ((static_cast<uint64_t>(__float_as_uint(yhi)) << 32) | __float_as_uint(ylo)) - kSkBase2;
   if (DT != VC_BF16) {
     tlo = __builtin_amdgcn_fmed3f(tlo, -255.0f, 255.0f);
     thi = __builtin_amdgcn_fmed3f(thi, -255.0f, 255.0f);
-    blo = min(max(blo, 1), 511);
-    bhi = min(max(bhi, 1), 511);
+    const uint32_t blo = min(max(static_cast<uint32_t>(u), 1u), 511u);
+    const uint32_t bhi = min(max(static_cast<uint32_t>(u >> 32), 1u), 511u);
+    u = (static_cast<uint64_t>(bhi) << 32) | blo;
   }
-  ulo = static_cast<uint32_t>(blo);
-  uhi = static_cast<uint32_t>(bhi);
   // the upper halves of the two fp32 values (exact: at most 8 significant bits)
   return __builtin_amdgcn_perm(__float_as_uint(thi), __float_as_uint(tlo), 0x07060302u);
 }
@@ -280,13 +284,13 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
     constexpr bool BIG = decltype(bigtag)::value;
     const bool valid = tok < S;
     v8bf xb[4];
-    uint32_t u[4][4][2];   // t + 256 of dword q's two elements (ACCUM)
+    uint64_t u[4][4];      // t + 256 of dword q's two elements (ACCUM)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const uint32_t wd[4] = {cur.r[kk].x, cur.r[kk].y, cur.r[kk].z, cur.r[kk].w};
       uint32_t pk[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pk[q] = sketch_word<DT, BIG>(wd[q], skc, u[kk][q][0], u[kk][q][1]);
+      for (int q = 0; q < 4; ++q) pk[q] = sketch_word<DT, BIG>(wd[q], skc, u[kk][q]);
       xb[kk] = __builtin_bit_cast(v8bf, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
     v4f acc[NCT];
@@ -302,8 +306,9 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // absent centroids carry norm 0x7FFFFFFF and never win
-        const int32_t sc = cn[ct][i] == 0x7FFFFFFF ? 0x7FFFFFFF : cn[ct][i] - 2 * static_cast<int32_t>(acc[ct][i]);
+        // absent centroids have a zero operand (so a zero dot product) and
+        // norm 0x7FFFFFFF: never below the starting best
+        const int32_t sc = cn[ct][i] - static_cast<int32_t>(acc[ct][i]);
         const bool lt = sc < best;
         best = lt ? sc : best;
         bc = lt ? 16 * ct + 4 * g + i : bc;
@@ -327,8 +332,7 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            atomicAdd(&sums[bc * kPairPitch + 16 * kk + 4 * g + q],
-                      (static_cast<uint64_t>(u[kk][q][1]) << 32) | u[kk][q][0]);
+            atomicAdd(&sums[bc * kPairPitch + 16 * kk + 4 * g + q], u[kk][q]);
       }
     }
   };
@@ -336,11 +340,11 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
   // while one is processed
   auto run = [&](auto bigtag) {
     int tok = s0 + w * 16 + l16;
-    TokRaw b0 = load_tok(v, b, h, tok, tok < S, g), b1;
+    TokRaw b0 = load_tok(v, b, h, tok, S, g), b1;
     for (int tt = 0; tt < kIters; tt += 2) {
-      b1 = load_tok(v, b, h, tok + 64, tok + 64 < S, g);
+      b1 = load_tok(v, b, h, tok + 64, S, g);
       assign_tokens(bigtag, b0, tok);
-      if (tt + 2 < kIters) b0 = load_tok(v, b, h, tok + 128, tok + 128 < S, g);
+      if (tt + 2 < kIters) b0 = load_tok(v, b, h, tok + 128, S, g);
       assign_tokens(bigtag, b1, tok + 64);
       tok += 128;
     }
