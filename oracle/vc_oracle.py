@@ -474,7 +474,8 @@ def sigma_of(s_q, s_k, sm_scale) -> np.ndarray:
 
 def attend_head(hq: HeadQK, hv: HeadV, rows=None, *, sm_scale=DEFAULT_SM_SCALE,
                 pcast: str = "expcast", quant: bool = True, q_raw=None, k_raw=None,
-                mode: str = "online", int_max: bool = True, repair: bool = True) -> np.ndarray:
+                mode: str = "online", int_max: bool = True, repair: bool = True,
+                code_delta=None, m_delta=None, ties=None, tie_width: float = 2e-3) -> np.ndarray:
     """Online-softmax attention for the given query rows of one head; returns float64 [R, D].
 
     Tiles of 128 permuted keys are visited in ascending order [ABS: the online
@@ -498,6 +499,20 @@ def attend_head(hq: HeadQK, hv: HeadV, rows=None, *, sm_scale=DEFAULT_SM_SCALE,
       unquantised residual, all scales 1;
       mode="two_pass" takes every code against the final maximum;
       int_max=False keeps a real-valued running maximum (pcast != "expcast").
+
+    Rounding-decision hooks (parity tests only; they change no result unless
+    given): the matrix core sums a score's 128 products in its own order, so
+    its fp32 score can differ from this one (exact, rounded once) by a few
+    ulps, and an ExpCast argument or a tile maximum that lies that close to a
+    rounding boundary can round the other way on the GPU.
+      ties: a list that receives, for the first requested row, every such
+        near-boundary decision as (kind, b, j, delta, distance): kind "code"
+        for key j of tile b whose fp32 ExpCast argument is within tie_width
+        of a half-integer (delta = +1 if it rounded down, -1 if up), kind
+        "max" for tile b whose fp32 max*sigma is within tie_width of an
+        integer (delta = the other possible ceiling minus this one; j = -1);
+      code_delta {(b, j): delta}: key j of tile b takes code + delta;
+      m_delta {b: delta}: tile b's ceil(max*sigma) is taken + delta.
     """
     S, D = hv.resid.shape
     nblk = (S + BLOCK - 1) // BLOCK
@@ -526,18 +541,41 @@ def attend_head(hq: HeadQK, hv: HeadV, rows=None, *, sm_scale=DEFAULT_SM_SCALE,
             np.full((R, 1), float(np.float64(sm_scale)) * math.log2(math.e))
         return ks, acc, sig
 
-    def probs(acc, sig, M):
+    def probs(acc, sig, M, b=None):
         if pcast == "expcast":
-            c = expcast_codes(acc, (F32(8) * sig).astype(F32), M)
+            s8 = (F32(8) * sig).astype(F32)
+            c = expcast_codes(acc, s8, M)
+            if ties is not None and b is not None:
+                x = (acc[:1].astype(np.float64) * np.asarray(s8, np.float64)[:1] +
+                     (120.0 - 8.0 * np.asarray(M, np.float64)[:1])).astype(F32).astype(np.float64)[0]
+                fr = x - np.floor(x)
+                for j in np.nonzero((x >= 0) & (np.abs(fr - 0.5) < tie_width))[0]:
+                    ties.append(("code", b, int(j), 1 if fr[j] < 0.5 else -1, float(abs(fr[j] - 0.5))))
+            if code_delta and b is not None:
+                c = c.copy()
+                for (tb, j), dlt in code_delta.items():
+                    if tb == b:
+                        c[:, j] = np.clip(c[:, j] + dlt, 0, 126)
             return e4m3_decode(c)
         t = acc.astype(np.float64) * np.asarray(sig, np.float64)
         p = 256.0 * np.exp2(t - M)
         return e4m3_decode(e4m3_encode(p)) if pcast == "exp_e4m3" else p
 
-    def tile_max(acc, sig):
+    def tile_max(acc, sig, b=None):
         m = (np.max(acc, axis=1, keepdims=True).astype(F32) * sig).astype(F32) if quant else \
             np.max(acc * np.asarray(sig, np.float64), axis=1, keepdims=True)
-        return np.ceil(m.astype(np.float64)) if int_max else m.astype(np.float64)
+        if not int_max:
+            return m.astype(np.float64)
+        c = np.ceil(m.astype(np.float64))
+        if ties is not None and b is not None:
+            f = float(m[0, 0]) - math.floor(float(m[0, 0]))
+            if 0 < f < tie_width or f == 0.0:
+                ties.append(("max", b, -1, 1 if f == 0.0 else -1, f))
+            elif f > 1.0 - tie_width:
+                ties.append(("max", b, -1, 1, 1.0 - f))
+        if m_delta and b in m_delta:
+            c = c + m_delta[b]
+        return c
 
     M = np.full((R, 1), -np.inf)
     if mode == "two_pass":
@@ -549,12 +587,12 @@ def attend_head(hq: HeadQK, hv: HeadV, rows=None, *, sm_scale=DEFAULT_SM_SCALE,
     for b in range(nblk):
         ks, acc, sig = scores(b)
         if mode == "online":
-            Mn = np.maximum(M, tile_max(acc, sig))
+            Mn = np.maximum(M, tile_max(acc, sig, b))
             alpha = np.where(np.isfinite(M), np.exp2(M - Mn), 0.0)
             l *= alpha
             num *= alpha
             M = Mn
-        P = probs(acc, sig, M)
+        P = probs(acc, sig, M, b)
         r = P.sum(axis=1, keepdims=True)
         l += r
         num += P @ Vd[ks] + r * mu[b][None, :]

@@ -6,6 +6,7 @@ output within relative L2 <= 5e-3 of the oracle's (the two differ only by
 the FP8 MFMA's fp32 accumulation order and the rare probability codes that
 this flips), and within 4% of exact fp64 attention.
 """
+import itertools
 import sys
 
 import numpy as np
@@ -23,6 +24,14 @@ TOL_ORACLE = 5e-3
 # meet the per-head bound with one 16-query sub-tile far off (at S=4096 a
 # 5% error in 16 rows adds only ~0.3% to the head's norm)
 TOL_ROW = 2e-2
+# A row above TOL_ROW passes only as the oracle's own row with one or two
+# near-boundary rounding decisions taken the other way (explain_row): the
+# matrix core sums a score's 128 FP8 products in its own order, so an ExpCast
+# argument within ~1e-4 of a half-integer (or a tile maximum that close to an
+# integer) can round the other way; one flipped code of a dominant key moves
+# its row by a few percent.  The GPU row must then match that alternative
+# within TOL_FLIP.
+TOL_FLIP = 5e-3
 # the accuracy target against exact fp64 attention
 TOL_EXACT = 0.04
 # The kernel must add nothing to the method's own error: its rel-L2 against
@@ -183,12 +192,31 @@ def _np(t):
     return t.detach().double().cpu().numpy()
 
 
+def explain_row(hq, hv, row, got, sm):
+    """The near-boundary rounding decisions of the oracle's row `row` (at most
+    two, among the eight nearest) that, taken the other way, give `got`
+    within TOL_FLIP; None if none do."""
+    ties = []
+    O.attend_head(hq, hv, np.array([row]), sm_scale=sm, ties=ties)
+    cands = sorted(ties, key=lambda t: t[4])[:8]
+    for n in (1, 2):
+        for sel in itertools.combinations(cands, n):
+            cd = {(b, j): d for (kind, b, j, d, _) in sel if kind == "code"}
+            md = {b: d for (kind, b, j, d, _) in sel if kind == "max"}
+            alt = O.bf16_round(O.attend_head(hq, hv, np.array([row]), sm_scale=sm, code_delta=cd, m_delta=md))[0]
+            e = O.rel_l2(got, alt)
+            if e <= TOL_FLIP:
+                return sel, e
+    return None
+
+
 def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0.0, rows=None, heads=None,
                          sm_scale=0.0, name="", target_met=None, v_format="e4m3"):
     """Run the GPU path and compare every prepared product and the output with the oracle.
 
     Output gates per head: rel-L2 vs the oracle <= TOL_ORACLE, every row's
-    rel-L2 vs the oracle's row <= TOL_ROW, and rel-L2 vs exact fp64 attention
+    rel-L2 vs the oracle's row <= TOL_ROW (or the row explained by
+    explain_row within TOL_FLIP), and rel-L2 vs exact fp64 attention
     <= EXACT_RATIO x the oracle's own + EXACT_SLACK.  The 4% target vs exact
     is gated on every head where the oracle meets it; a head where the oracle
     itself is above it is a miss of the method, listed in run.target_misses.
@@ -266,7 +294,12 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
         errs_or_ex.append(e_or_ex)
         row_errs.append(float(row_e.max()))
         assert e <= TOL_ORACLE, f"{tag}: rel-L2 vs oracle {e:.3e}"
-        assert row_e.max() <= TOL_ROW, f"{tag}: row {int(r[np.argmax(row_e)])} rel-L2 vs oracle {row_e.max():.3e}"
+        for i in np.nonzero(row_e > TOL_ROW)[0]:
+            expl = explain_row(hq, hv, int(r[i]), got[i], sm)
+            assert expl is not None, \
+                f"{tag}: row {int(r[i])} rel-L2 vs oracle {row_e[i]:.3e}, not a near-boundary rounding flip"
+            say(f"{tag}: row {int(r[i])} rel-L2 vs oracle {row_e[i]:.3e} is the oracle with "
+                f"{[t[:4] for t in expl[0]]} rounded the other way (then {expl[1]:.1e})")
         assert e_ex <= EXACT_RATIO * e_or_ex + EXACT_SLACK, \
             f"{tag}: rel-L2 vs exact {e_ex:.3e}, the oracle's own {e_or_ex:.3e}"
         if e_or_ex <= TOL_EXACT:

@@ -238,3 +238,47 @@ def test_softmax_temperature_two_keys():
     assert abs(out[0, 0] - 0.8) < 0.02, out[0, 0]
     assert np.array_equal(out[0], out[1])
     assert np.all(np.abs(out[0, 1:]) < 1e-12)
+
+
+def test_rounding_decision_hooks():
+    """The parity tests' hooks: without them nothing changes; every reported
+    near-boundary decision is within the width and names a real code; moving
+    that code by its delta changes exactly that key's probability (the row
+    then equals a hand-made recomputation with the one code replaced)."""
+    q, k, v = _head(31, S=600)
+    hv = O.prepare_v_head(v, k=4, iters=2)
+    hq = O.prepare_qk_head(q, k, hv.perm)
+    base = O.attend_head(hq, hv)
+    assert np.array_equal(base, O.attend_head(hq, hv, code_delta={}, m_delta={}))
+    found = None
+    for row in range(0, 600, 7):
+        ties = []
+        out = O.attend_head(hq, hv, np.array([row]), ties=ties, tie_width=0.05)
+        assert np.array_equal(out[0], base[row])
+        for kind, b, j, d, dist in ties:
+            assert dist < 0.05 and d in (-1, 1)
+            if kind == "code" and found is None:
+                found = (row, b, j, d)
+    assert found is not None, "no near-boundary code in 86 rows at width 0.05"
+    row, b, j, d = found
+    alt = O.attend_head(hq, hv, np.array([row]), code_delta={(b, j): d})[0]
+    assert not np.array_equal(alt, base[row])
+    # the same row by hand: online softmax over the tiles with that one code moved
+    Qd = O.e4m3_decode(hq.q8[[row]])
+    Kd = O.e4m3_decode(hq.k8)
+    Vd = hv.v_values()
+    S = Kd.shape[0]
+    M, l, num = -np.inf, 0.0, np.zeros(128)
+    for t in range((S + 127) // 128):
+        ks = slice(128 * t, min(S, 128 * (t + 1)))
+        acc = (Qd @ Kd[ks].T).astype(np.float32)
+        sig = O.sigma_of(hq.q_scale[row // 128], hq.k_scale[t], O.DEFAULT_SM_SCALE)
+        Mn = max(M, math.ceil(float(np.float32(np.float32(acc.max()) * np.float32(sig)))))
+        a = 2.0 ** (M - Mn) if np.isfinite(M) else 0.0
+        c = O.expcast_codes(acc, np.float32(8) * np.float32(sig), np.array([[Mn]]))
+        if t == b:
+            c[0, j] = min(max(c[0, j] + d, 0), 126)
+        P = O.e4m3_decode(c)
+        r = P.sum()
+        l, num, M = a * l + r, a * num + (P @ Vd[ks])[0] + r * hv.mean[t], Mn
+    assert np.allclose(alt, num / l, rtol=1e-12, atol=0)
