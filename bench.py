@@ -76,6 +76,14 @@ def _code_only(text: str) -> str:
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
+def attention_kernels(w) -> str:
+    """The kernels vc_attention_fwd launches for workload w (the library's attn_split rule)."""
+    nblk = -(-w.S // 128)
+    if w.repair_budget == 0 and -(-nblk // 16) == 2 and w.B * w.H * nblk <= 256:
+        return "vc_attention_fwd (k_vc_attn_halves: one workgroup per query block, keys in two halves)"
+    return "vc_attention_fwd (k_vc_attn_fwd + k_vc_attn_tail + k_vc_attn_merge)"
+
+
 def kernel_sources_sha256() -> str:
     """Hash of the attention kernels' code (comments and blank lines left
     out, so a comment edit keeps a traffic record taken on the same code)."""
@@ -274,8 +282,9 @@ def main() -> int:
                    "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
                    "compute_units": torch.cuda.get_device_properties(0).multi_processor_count},
         "roofline": {
-            # the attention call: whole work items, the cut last round, the merge
-            "kernel": "vc_attention_fwd (k_vc_attn_fwd + k_vc_attn_tail + k_vc_attn_merge)",
+            # the attention call: whole work items, the cut last round, the merge;
+            # or, for a short launch, the one-workgroup-per-query-block form
+            "kernel": attention_kernels(w),
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": PEAK_FP8_TFLOPS,

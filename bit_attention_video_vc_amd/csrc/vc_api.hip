@@ -342,7 +342,8 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   float sm = aopts ? aopts->sm_scale : 0.0f;
   if (!(sm >= 0.0f) || std::isinf(sm)) return fail(VC_ERR_ARG, "sm_scale must be finite and >= 0");
   if (sm == 0.0f) sm = static_cast<float>(1.0 / std::sqrt(128.0));
-  const int64_t total = p.split.whole + p.split.tail_wg;   // whole items, then the tail workgroups
+  // whole items, then the tail workgroups; or the short-launch form's query blocks
+  const int64_t total = p.split.halves ? static_cast<int64_t>(p.B) * p.H * p.nblk : p.split.whole + p.split.tail_wg;
   if (total > vc::kMaxAttnWorkgroups)
     return fail(VC_ERR_UNSUPPORTED, "B*H*ceil(S/256) = %lld exceeds %lld attention workgroups", (long long)total,
                 (long long)vc::kMaxAttnWorkgroups);
@@ -374,6 +375,8 @@ vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts, 
   tl.per = p.split.per;
   tl.ngrp = p.split.ngrp;
   tl.part = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(ws)) + p.lay.attn_part);
+  tl.halves = p.split.halves ? static_cast<int>(total) : 0;
+  tl.ka = p.split.ka;
   a.sm_scale = sm;
   a.v_format = opts->v_format;
   const hipError_t e = vc::launch_attention(a, tl, static_cast<hipStream_t>(stream));

@@ -563,6 +563,57 @@ struct StepCopies {
   }
 };
 
+// The copies of one step of a key half (the short-launch kernel: waves
+// 4h..4h+3 own half h and copy its tiles): K(tk) with its scale into kdst
+// and, when vdst is set, V(tv) into vdst, all at once at the start of the
+// step before the tiles' use.  (Spread over the step's first half as the
+// whole-item kernel spreads its copies, they land later, the barrier waits
+// longer, and the short launches ran 9-13% slower.)
+template <int VF>
+struct HalfCopies {
+  const TileCtx& c;
+  int tk, tv;
+  uint8_t* kdst;
+  uint8_t* vdst;
+  static constexpr int kHalfThreads = kAttnThreads / 2;
+  static constexpr int kK = kTileBytes / (16 * kHalfThreads);                          // K copies per wave
+  static constexpr int kV = (VF ? kFp4CodeBytes : kTileBytes) / (16 * kHalfThreads);  // V code copies per wave
+  __device__ __forceinline__ HalfCopies(const TileCtx& ctx, int k_tile, int v_tile, uint8_t* kd, uint8_t* vd)
+      : c(ctx), tk(k_tile), tv(v_tile), kdst(kd), vdst(vd) {}
+  static_assert(kK % 2 == 0, "K copies in two halves");
+  __device__ __forceinline__ void issue_k(int j0, int j1) const {
+    const int hw = c.w & 3;   // wave within the half
+    const uint32_t koff = static_cast<uint32_t>(tk) * kTileBytes + static_cast<uint32_t>(hw) * 1024;
+    if (j0 == 0 && hw == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.sr, (__attribute__((address_space(3))) void*)(kdst + kTileBytes), 4,
+                                               static_cast<uint32_t>(tk) * 4, 0, 0, 0);
+#pragma unroll
+    for (int j = j0; j < j1; ++j)
+      copy16_to_lds_s(c.kr, static_cast<uint32_t>(c.lane16), koff + j * (16 * kHalfThreads),
+                      kdst + j * (16 * kHalfThreads) + hw * 1024);
+  }
+  __device__ __forceinline__ void issue_v() const {
+    if (!vdst) return;
+    const int hw = c.w & 3;
+    const uint32_t voff = static_cast<uint32_t>(tv) * kTileBytes + static_cast<uint32_t>(hw) * 1024;
+#pragma unroll
+    for (int j = 0; j < kV; ++j)
+      copy16_to_lds_s(c.vr, static_cast<uint32_t>(c.lane16), voff + j * (16 * kHalfThreads),
+                      vdst + j * (16 * kHalfThreads) + hw * 1024);
+    if (VF && hw == 1)   // MXFP4: the tile's 512 scale bytes (and 512 unused bytes of the slot)
+      copy16_to_lds_s(c.vr, static_cast<uint32_t>(c.lane16), voff - 1024 + kFp4CodeBytes, vdst + kFp4CodeBytes);
+  }
+  __device__ __forceinline__ void issue_all() const {
+    issue_k(0, kK);
+    issue_v();
+  }
+};
+// The MFMA phase's copy points do nothing in the halves mode (its copies go
+// out at the start of the step).
+struct NoCopies {
+  __device__ __forceinline__ void issue(int) const {}
+};
+
 // Deferred block-mean restore of one group of 16 tiles:
 // O^T[dt][qi] += A_dt . B_qi over the group's tiles, A = mu/s_v (bf16 high
 // and low parts, 16 channels x 16 tiles), B = the row-sum weights (16 tiles
@@ -651,13 +702,26 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane16, 
 // barrier of its own.  Tile indices past the last tile are clamped to it
 // and a score tile past the end is masked out entirely, which leaves the
 // state unchanged (no rise, codes 0): every step runs the same code.
-template <int VF, int J>
+//
+// HALVES (the short-launch kernel, each half of the workgroup on its own key
+// range with two-slot rings): K(kb+2) is in kcur and V(kb) in vcur; the step
+// first copies K(kb+3) into kfree and V(kb+1) into vfree (the slots that
+// held K(kb+1) and V(kb-1), both last read in step kb-1), all at once, and
+// its barrier waits for them; a group's restore operands are read from
+// global memory, for every group that holds a real tile of the half, at the
+// group's last step (a half shorter than the step count runs masked steps
+// past its end, whose zero row sums would overwrite the weight slots of a
+// partial last group before any restore after the loop; the step count, a
+// multiple of 16 no smaller than either half, ends every such group).
+template <int VF, int J, bool HALVES = false>
 __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_t* kcur, uint8_t* kfree,
                                           const uint8_t* vcur, uint8_t* vfree, const v8i (&qop)[2], TileAcc& acc) {
   const int nblk = c.nblk, last = nblk - 1, g = c.lane16 >> 8;   // lane group, from the kept 16*lane
   const StepCopies<VF> cp(c, kb + kStages + 1 < last ? kb + kStages + 1 : last,
                           kb + kStages - 1 < last ? kb + kStages - 1 : last, kb + kStages - 1, kfree, vfree);
   static_assert(2 * kDmaPerTile + 2 == 6, "six copy parts, one per sub-tile");
+  if constexpr (HALVES)
+    HalfCopies<VF>(c, kb + 3 < last ? kb + 3 : last, kb + 1 < last ? kb + 1 : last, kfree, vfree).issue_all();
   v8i Pn[2];
   float d[2], ks_new;
   bool rose[2];
@@ -666,14 +730,24 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
     float mn[2];
     // tile kb's row sum goes to l and to the restore weight of tile kb%16
     // of its group, held by lane group (kb/4)%4 in slot J
-    mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, acc.sig, acc.st, d, rose, acc.sh, acc.mh, sn, Pn, mn, acc.O,
-                   acc.rr[J], (c.lane16 >> 8) == ((kb >> 2) & 3), cp);
+    if constexpr (HALVES)
+      mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, acc.sig, acc.st, d, rose, acc.sh, acc.mh, sn, Pn, mn, acc.O,
+                     acc.rr[J], (c.lane16 >> 8) == ((kb >> 2) & 3), NoCopies{});
+    else
+      mfma_phase<VF>(kcur, vcur, c.lane16, qop, acc.P, acc.sig, acc.st, d, rose, acc.sh, acc.mh, sn, Pn, mn, acc.O,
+                     acc.rr[J], (c.lane16 >> 8) == ((kb >> 2) & 3), cp);
     // K(kb+2)'s scale (replicated per lane after the tile), read before the
     // barrier: the next step refills this buffer.  Wave-uniform, so it is
     // kept in a scalar register.
     ks_new = __int_as_float(__builtin_amdgcn_readfirstlane(
         *reinterpret_cast<const int*>(kcur + kTileBytes + (c.lane16 >> 2))));
-    step_barrier<VF>();
+    if constexpr (HALVES) {
+      // every copy of this step has landed (s_waitcnt vmcnt(0) lgkmcnt(0))
+      __builtin_amdgcn_s_waitcnt(0x70);
+      __builtin_amdgcn_s_barrier();
+    } else {
+      step_barrier<VF>();
+    }
     if (__builtin_expect(kb + 3 >= nblk, 0)) {
       // tile kb+2 is the last tile (keys past S masked) or past it (all masked)
       mask_tile<VF>(sn, g, kb + 2 == last ? c.kval_last : 0);
@@ -722,17 +796,37 @@ __device__ __forceinline__ void tile_step(const TileCtx& c, int kb, const uint8_
   acc.P[0] = Pn[0];
   acc.P[1] = Pn[1];
   if ((kb & (kMuOpGroup - 1)) == kMuOpGroup - 1) {
-    // the group's operand rows were copied by steps kb-18 .. kb-3, which
-    // the barrier of step kb-1 has made visible
-    // in two halves of four channel sub-tiles (fewer live registers)
-    const uint8_t* grp = (kb / kMuOpGroup) & 1 ? c.grp1 : c.grp0;
-    v4s bh[2], bl[2];
-    restore_weights(acc.rr, bh, bl);
+    if constexpr (HALVES) {
+      if (kb - (kMuOpGroup - 1) < nblk) {
+        // rows 16G .. 16G+15 of this half's operands, 8 bytes per lane
+        const uint8_t* rows = c.muop + static_cast<int64_t>(kb / kMuOpGroup) * kMuOpGroup * kMuOpRowBytes +
+                              (c.lane16 >> 1);
+        v4s bh[2], bl[2];
+        restore_weights(acc.rr, bh, bl);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      v4s A[4][2];
-      restore_ops_lds(grp, c.lane16, half, A);
-      restore_mfma<4>(A, 4 * half, bh, bl, acc.O);
+        for (int half = 0; half < 2; ++half) {
+          v4s A[4][2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+              A[i][hl] = *reinterpret_cast<const v4s*>(rows + (2 * (4 * half + i) + hl) * kMuOpRowBytes);
+          restore_mfma<4>(A, 4 * half, bh, bl, acc.O);
+        }
+      }
+    } else {
+      // the group's operand rows were copied by steps kb-18 .. kb-3, which
+      // the barrier of step kb-1 has made visible
+      // in two halves of four channel sub-tiles (fewer live registers)
+      const uint8_t* grp = (kb / kMuOpGroup) & 1 ? c.grp1 : c.grp0;
+      v4s bh[2], bl[2];
+      restore_weights(acc.rr, bh, bl);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        v4s A[4][2];
+        restore_ops_lds(grp, c.lane16, half, A);
+        restore_mfma<4>(A, 4 * half, bh, bl, acc.O);
+      }
     }
   }
 }
@@ -1144,8 +1238,193 @@ __global__ void __launch_bounds__(256) k_vc_attn_merge(AttnArgs a, AttnTail tl) 
   }
 }
 
+// Short launches (no more query blocks than compute units, attn_split's
+// `halves`): one workgroup per (b,h) and 128-query block qb.  Waves 0-3 take
+// key tiles [0, ka) and waves 4-7 tiles [ka, nblk), ka = 16 * ceil(ngrp/2),
+// each wave owning the same 32 queries (w % 4) of qb in both halves, so the
+// per-wave work of a step is that of the whole-item kernel.  Each half
+// streams its tiles through its own two K and two V slots; both halves run
+// ka steps (the shorter one masked past its end) under one barrier per step.
+// Then waves 4-7 leave O, l and their reference exponent in LDS and waves
+// 0-3 add them to their own with the weights 2^(e_i - max e) -- the merge of
+// the cut items, inside the workgroup -- and write the output.
+struct HalfLds {
+  uint8_t *k0, *k1, *k2, *k3, *v0, *v1, *v2, *v3;
+};
+template <int VF>
+__device__ __forceinline__ void attn_halves(const AttnArgs& a, int bh, int qb, int ka, const HalfLds& L) {
+  const int nfull = a.nblk;
+  const int b = bh / a.H, h = bh - b * a.H;
+  int tid_raw = threadIdx.x;
+  asm volatile("" : "+v"(tid_raw));
+  const int tid = tid_raw, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int S = a.S;
+  const int half = w >> 2, wq = w & 3;
+  const int kv0 = half ? ka : 0, kv1 = half ? nfull : (ka < nfull ? ka : nfull);
+  const int nblk = kv1 - kv0;           // this half's tiles (>= 1)
+  uint8_t* const k0 = half ? L.k2 : L.k0;
+  uint8_t* const k1 = half ? L.k3 : L.k1;
+  uint8_t* const v0 = half ? L.v2 : L.v0;
+  uint8_t* const v1 = half ? L.v3 : L.v1;
+
+  TileCtx c;
+  c.kr = head_rsrc(a.k8 + (static_cast<int64_t>(bh) * nfull + kv0) * kTileBytes,
+                   static_cast<uint32_t>(nblk) * kTileBytes);
+  c.vr = head_rsrc(a.v8 + (static_cast<int64_t>(bh) * nfull + kv0) * kTileBytes,
+                   static_cast<uint32_t>(nblk) * kTileBytes);
+  const int nrows = muop_rows(nfull);
+  c.muop = a.v_muop + (static_cast<int64_t>(bh) * nrows + kv0) * kMuOpRowBytes;
+  c.mr = head_rsrc(c.muop, static_cast<uint32_t>(nrows - kv0) * kMuOpRowBytes);
+  c.ks = a.k_scale + static_cast<int64_t>(bh) * nfull + kv0;
+  c.sr = head_rsrc(c.ks, static_cast<uint32_t>(nblk) * 4);
+  c.grp0 = nullptr;
+  c.grp1 = nullptr;
+  c.sqs = a.q_scale[static_cast<int64_t>(bh) * nfull + qb];
+  c.sm_scale = a.sm_scale;
+  c.nblk = nblk;
+  c.kval_last = kv1 == nfull ? S - (nfull - 1) * kBlock : kBlock;
+  c.tid = tid;
+  c.w = w;
+  c.lane = lane;
+  {
+    int l16b = lane * 16;
+    asm volatile("" : "+v"(l16b));
+    c.lane16 = l16b;
+  }
+  c.g = g;
+  c.l16 = l16;
+  const float sqs = c.sqs;
+  const uint8_t* qtile = a.q8 + (static_cast<int64_t>(bh) * nfull + qb) * kTileBytes;
+  v8i qop[2];
+  qop[0] = ld_op_global(qtile, 2 * wq, lane);
+  qop[1] = ld_op_global(qtile, 2 * wq + 1, lane);
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  TileAcc acc;
+  acc.st.M[0] = acc.st.M[1] = kNegBig;
+  acc.st.l[0] = acc.st.l[1] = 0.0f;
+  acc.st.se = 0x7F7F7F7F;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc.O[dt][0] = acc.O[dt][1] = zero;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc.rr[j][0] = acc.rr[j][1] = 0.0f;
+
+  // ---- prologue: K(0), V(0), K(1); scores and codes of tile 0, scores of
+  // tile 1; then K(2) into the slot of K(0) ----
+  const int last = nblk - 1;
+  HalfCopies<VF>(c, 0, 0, k0, v0).issue_all();
+  HalfCopies<VF>(c, last < 1 ? last : 1, 0, k1, nullptr).issue_all();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  {
+    v4f sc[8][2];
+    score_tile(k0, lane, qop, sc);
+    if (nblk == 1 && c.kval_last < kBlock) mask_tile<VF>(sc, g, c.kval_last);
+    softmax_tile(sc, ((sqs * c.ks[0]) * a.sm_scale) * kLog2e, acc.st, acc.P);
+  }
+  score_tile(k1, lane, qop, acc.sh);
+  if (nblk <= 2) mask_tile<VF>(acc.sh, g, nblk == 2 ? c.kval_last : 0);
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    acc.mh[qi] = max4(acc.sh[0][qi]);
+#pragma unroll
+    for (int t = 1; t < 8; ++t) acc.mh[qi] = max_acc4(acc.mh[qi], acc.sh[t][qi]);
+  }
+  acc.sig = ((sqs * c.ks[last < 1 ? last : 1]) * a.sm_scale) * kLog2e;
+  __syncthreads();   // k0 is refilled
+  HalfCopies<VF>(c, last < 2 ? last : 2, 0, k0, nullptr).issue_all();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // Step kb reads K(kb+2) from slot kb%2 and V(kb) from slot kb%2.  ka is a
+  // multiple of 16, so the loop has no remainder.
+  for (int kb = 0; kb < ka; kb += 4) {
+    tile_step<VF, 0, true>(c, kb, k0, k1, v0, v1, qop, acc);
+    tile_step<VF, 1, true>(c, kb + 1, k1, k0, v1, v0, qop, acc);
+    tile_step<VF, 2, true>(c, kb + 2, k0, k1, v0, v1, qop, acc);
+    tile_step<VF, 3, true>(c, kb + 3, k1, k0, v1, v0, qop, acc);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const int lane_p = c.lane16 >> 4, g_p = lane_p >> 4, l16_p = lane_p & 15;
+  // (every group's restore ran in the loop, a partial last group's too:
+  // its blocks past the head's end have zero operands and zero weights)
+
+  // ---- the two halves meet in LDS (every wave is done with the slots) ----
+  __syncthreads();
+  float e[2];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi)
+    e[qi] = acc.st.M[qi] - static_cast<float>(static_cast<int>((acc.st.se >> (8 * qi)) & 0xFF) - 127);
+  // the partner's O, lane-interleaved, in K buffer wq; its l [2][16] and
+  // e [2][16] in V buffer 0
+  float* const xo = reinterpret_cast<float*>(wq == 0 ? L.k0 : wq == 1 ? L.k1 : wq == 2 ? L.k2 : L.k3);
+  float* const xl = reinterpret_cast<float*>(L.v0) + wq * 64;
+  if (half) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) *reinterpret_cast<v4f*>(xo + ((dt * 2 + qi) * 64 + lane_p) * 4) = acc.O[dt][qi];
+    if (g_p == 0) {
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        xl[qi * 16 + l16_p] = acc.st.l[qi];
+        xl[32 + qi * 16 + l16_p] = e[qi];
+      }
+    }
+  }
+  __syncthreads();
+  if (half) return;
+  const float sv = a.hdr[bh].v_scale;
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const float lb = xl[qi * 16 + l16_p], eb = xl[32 + qi * 16 + l16_p];
+    const float E = fmaxf(e[qi], eb);
+    const float wa = ldexpf(1.0f, static_cast<int>(fmaxf(e[qi] - E, -200.0f)));
+    const float wb = ldexpf(1.0f, static_cast<int>(fmaxf(eb - E, -200.0f)));
+    const float f = sv / (wa * acc.st.l[qi] + wb * lb);
+    const int q = qb * kBlock + 16 * (2 * wq + qi) + l16_p;
+    if (q < S) {
+      uint16_t* orow = a.out + b * a.osB + static_cast<int64_t>(q) * a.osS + h * a.osH;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v4f ob = *reinterpret_cast<const v4f*>(xo + ((dt * 2 + qi) * 64 + lane_p) * 4);
+        const v4f o = wa * acc.O[dt][qi] + wb * ob;
+        const uint32_t lo = f32_to_bf16_bits(o[0] * f) | (f32_to_bf16_bits(o[1] * f) << 16);
+        const uint32_t hi = f32_to_bf16_bits(o[2] * f) | (f32_to_bf16_bits(o[3] * f) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g_p) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+template <int VF>
+__global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_halves(AttnArgs a, int ka) {
+  static_assert(kStages == 4, "four K and four V buffers, two of each per half");
+  __shared__ __align__(16) uint8_t kbuf0[kKBufBytes];
+  __shared__ __align__(16) uint8_t kbuf1[kKBufBytes];
+  __shared__ __align__(16) uint8_t kbuf2[kKBufBytes];
+  __shared__ __align__(16) uint8_t kbuf3[kKBufBytes];
+  __shared__ __align__(16) uint8_t vbuf0[VTile<VF>::kBytes];
+  __shared__ __align__(16) uint8_t vbuf1[VTile<VF>::kBytes];
+  __shared__ __align__(16) uint8_t vbuf2[VTile<VF>::kBytes];
+  __shared__ __align__(16) uint8_t vbuf3[VTile<VF>::kBytes];
+  const HalfLds L = {kbuf0, kbuf1, kbuf2, kbuf3, vbuf0, vbuf1, vbuf2, vbuf3};
+  const int nq = a.nblk;
+  const int item = xcd_order(gridDim.x, blockIdx.x);
+  const int bh = item / nq;
+  attn_halves<VF>(a, bh, item - bh * nq, ka, L);
+}
+
 hipError_t launch_attention(const AttnArgs& a, const AttnTail& tl, hipStream_t st) {
   const bool fp4 = a.v_format == VC_V_MXFP4;
+  if (tl.halves > 0) {
+    // one workgroup per (b,h) and query block
+    if (fp4)
+      hipLaunchKernelGGL(k_vc_attn_halves<VC_V_MXFP4>, dim3(tl.halves), dim3(kAttnThreads), 0, st, a, tl.ka);
+    else
+      hipLaunchKernelGGL(k_vc_attn_halves<VC_V_E4M3>, dim3(tl.halves), dim3(kAttnThreads), 0, st, a, tl.ka);
+    return hipGetLastError();
+  }
   if (a.whole > 0) {
     // (MXFP4 workspaces have no repair set)
     if (fp4)

@@ -53,6 +53,14 @@ __host__ __device__ inline int asg_tokens(int64_t BH, int S) {
 // exponent in a partial slot and the merge kernel combines the pieces of an
 // item exactly in powers of two.  The repair tiles need every item's final
 // maximum, so workspaces with a repair set are not split.
+//
+// A short launch -- at most kAttnSlots query blocks in all, of two 16-tile
+// groups per item (2048 < S <= 4096) -- runs `halves` instead: one workgroup
+// per query block, its waves in two halves over key tiles [0, 16) and
+// [16, nblk), merged inside the workgroup; no partial slots and no merge
+// launch.  (Each half streams its own K and V tiles, twice the tile copies
+// per step of the cut form, which costs more than the merge saves once the
+// halves are longer than one group.)
 constexpr int kAttnSlots = 256;           // MI355X compute units
 constexpr int kAttnGroup = 16;            // tiles per piece-boundary group
 struct AttnSplit {
@@ -62,16 +70,24 @@ struct AttnSplit {
   int tail_wg;        // workgroups over the cut items
   int per;            // groups per tail workgroup
   int ngrp;           // groups per item
+  int halves;         // 1: the short-launch form, B*H*nblk workgroups
+  int ka;             // its first half's tiles
 };
 __host__ __device__ inline AttnSplit attn_split(int64_t BH, int nblk, int nrep) {
   AttnSplit p;
   p.items = BH * ((nblk + 1) / 2);
   p.ngrp = (nblk + kAttnGroup - 1) / kAttnGroup;
   p.whole = p.items;
-  p.tail = p.tail_wg = p.per = 0;
+  p.tail = p.tail_wg = p.per = p.halves = p.ka = 0;
   const int R = static_cast<int>(p.items % kAttnSlots);
   if (nrep > 0 || R == 0 || p.ngrp < 2) return p;
   const int per = static_cast<int>((static_cast<int64_t>(R) * p.ngrp + kAttnSlots - 1) / kAttnSlots);
+  if (p.ngrp == 2 && BH * nblk <= kAttnSlots) {
+    p.whole = 0;
+    p.halves = 1;
+    p.ka = kAttnGroup;
+    return p;
+  }
   if (per >= p.ngrp) return p;           // no group saved per compute unit
   p.whole = p.items - R;
   p.tail = R;

@@ -54,10 +54,13 @@ struct AttnArgs {
 
 // The cut items (attn_split): tail_wg workgroups run the `tail` items after
 // the whole ones in runs of `per` 16-tile groups (ngrp per item), with
-// partial slots at `part`, then the merge launch.
+// partial slots at `part`, then the merge launch; or, with `halves`, the
+// short-launch form in place of all of that.
 struct AttnTail {
   int tail, tail_wg, per, ngrp;
   float* part;
+  int halves;         // the short-launch form (attn_split): its B*H*nblk workgroups, or 0
+  int ka;             // its key halves: tiles [0, ka) and [ka, nblk)
 };
 
 hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_opts& o, const WsPtrs& ws,

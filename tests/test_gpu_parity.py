@@ -592,22 +592,51 @@ SPLIT_CASES = [
     (1, 6, 8492, "e4m3", None),                     # 204 items of 5 groups, runs of 4 crossing item boundaries
     (1, 20, 4196, "e4m3", [(0, 0), (0, 15), (0, 19)]),  # 256 items whole, then 84 cut (heads 15-19)
     (1, 6, 8492, "mxfp4", None),                    # the 4-bit residual's anchor exponent in the partials
-    (2, 4, 4096, "e4m3", None),                     # config 2's class: 128 items, two pieces each
 ]
 
 
 @pytest.mark.parametrize("B,H,S,v_format,heads", SPLIT_CASES,
                          ids=["S4500_three_pieces", "S8492_runs_cross_items", "H20_whole_then_cut",
-                              "S8492_mxfp4", "B2_S4096_halves"])
+                              "S8492_mxfp4"])
 def test_key_axis_split(B, H, S, v_format, heads):
     from test_split_plan import plan
-    assert plan(B * H, -(-S // 128)) is not None, "the shape must be cut"
+    p = plan(B * H, -(-S // 128))
+    assert p is not None and not p.get("halves"), "the shape must be cut"
     w, q, k, v = _cfg(2, B=B, H=H, S=S)
     rows = np.unique(np.concatenate([np.arange(0, S, 3), np.arange(max(0, S - 130), S)]))
     run = check_against_oracle(q, k, v, kc=8, iters=2, rows=rows, heads=heads,
                                name=f"split B={B} H={H} S={S} {v_format}", v_format=v_format)
     # repeated calls on one prepared workspace rewrite the partial slots and
     # merge them in the same order: the same bytes every time
+    for rep in range(3):
+        again = torch.empty_like(run.out)
+        vc.vc_attention_fwd(again, run.opts, run.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again, run.out), f"call {rep + 2} differs from the first"
+
+
+HALVES_CASES = [
+    # (B, H, S, v_format): the short-launch form, one workgroup per query block, keys in two halves
+    (2, 4, 4096, "e4m3"),      # config 2's class: two halves of 16 tiles
+    (1, 8, 4046, "e4m3"),      # the second half's last tile ragged (78 keys)
+    (1, 14, 2049, "e4m3"),     # second half one tile with one key: 15 masked steps after it
+    (1, 6, 3000, "e4m3"),      # halves of 16 and 8 tiles, the second ragged: 8 masked steps
+    (1, 6, 3000, "mxfp4"),     # the 4-bit residual's anchor exponents meet in the merge
+    (1, 8, 4096, "mxfp4"),     # config 2 with the 4-bit residual
+]
+
+
+@pytest.mark.parametrize("B,H,S,v_format", HALVES_CASES,
+                         ids=["B2_S4096", "S4046_ragged", "S2049_one_key_half", "S3000_unequal",
+                              "S3000_mxfp4", "S4096_mxfp4"])
+def test_short_launch_halves(B, H, S, v_format):
+    from test_split_plan import plan
+    p = plan(B * H, -(-S // 128))
+    assert p is not None and p.get("halves"), "the shape must take the short-launch form"
+    w, q, k, v = _cfg(2, B=B, H=H, S=S)
+    run = check_against_oracle(q, k, v, kc=8, iters=2, name=f"halves B={B} H={H} S={S} {v_format}",
+                               v_format=v_format)
+    assert not run.target_misses or v_format == "mxfp4"
     for rep in range(3):
         again = torch.empty_like(run.out)
         vc.vc_attention_fwd(again, run.opts, run.ws)

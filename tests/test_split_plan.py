@@ -1,5 +1,9 @@
 """Host-side checks of the attention work split (no GPU).
 
+A short launch (at most 256 query blocks, two 16-tile groups per item)
+runs instead one workgroup per query block with its keys in two halves
+merged inside the workgroup; it needs no partial slots.
+
 A work item is one (b,h) and pair of 128-query blocks.  The first
 items - R run whole (R = items mod 256, the partial last round of the 256
 compute units); the last R are cut along the key axis into runs of `per`
@@ -34,6 +38,9 @@ def plan(BH, nblk, nrep=0):
     if nrep > 0 or R == 0 or ngrp < 2:
         return None
     per = -(-R * ngrp // SLOTS)
+    if ngrp == 2 and BH * nblk <= SLOTS:
+        # the short-launch form: one workgroup per query block, key halves at 16 tiles
+        return dict(halves=True, wg=BH * nblk, ka=GROUP, ngrp=ngrp)
     if per >= ngrp:
         return None
     return dict(items=items, whole=items - R, tail=R, per=per, ngrp=ngrp, tail_wg=-(-R * ngrp // per))
@@ -76,6 +83,12 @@ def test_runs_cover_every_group_once_and_merge_finds_the_slots(BH, S):
     p = plan(BH, nblk)
     if p is None:
         return
+    if p.get("halves"):
+        # two halves of whole 16-tile groups, the second one non-empty and no
+        # longer than the first (which sets the step count), one round
+        ka = p["ka"]
+        assert ka % GROUP == 0 and 0 < nblk - ka <= ka and p["wg"] <= SLOTS
+        return
     cover, written = {}, {}
     for t, ps in pieces(p, nblk).items():
         assert 1 <= len(ps) <= 2
@@ -102,7 +115,7 @@ def test_layout_reserves_two_partial_slots_per_tail_workgroup(B, H, S, beta):
     lay = vc.vc_workspace_layout(d, vc.v_opts(True, 8, 1, 0, beta))
     nrep = lay.nrep
     p = plan(B * H, -(-S // 128), nrep)
-    want = 0 if p is None else 2 * p["tail_wg"] * PART_BYTES
+    want = 0 if p is None or p.get("halves") else 2 * p["tail_wg"] * PART_BYTES
     assert lay.scratch - lay.attn_part >= want
     assert lay.scratch - lay.attn_part < want + 256            # the region's size, 256-byte aligned
     assert lay.attn_part % 256 == 0
