@@ -136,7 +136,8 @@ typedef struct {
  *   attn_part   vc_attention_fwd's partial results for work items it cuts
  *               along the key axis (the partial last round of workgroups,
  *               or every item of a launch with fewer items than compute
- *               units); empty when nothing is cut (always with repair)
+ *               units); empty when nothing is cut (always with repair) and
+ *               for the short-launch form
  *   scratch     internal (k-means state, sort counters, repair scores)
  * Tile formats (16384 B, 128 rows x 128 columns of codes):
  *   row tile (q8, k8, rep_k8): the byte for (row r, column d) is at
@@ -247,7 +248,10 @@ vc_status vc_prepare_qk(const vc_desc* qd, const void* q, const vc_desc* kd, con
  * there are fewer items than compute units) are cut along the key axis and
  * their pieces merged exactly (powers of two) by a second kernel, which uses
  * the workspace's attn_part region.  Workspaces with a repair set are not
- * cut. */
+ * cut.  A short launch -- at most 256 query blocks in all, 2048 < S <= 4096,
+ * no repair set -- runs instead one workgroup per (b,h) and query block with
+ * its key tiles in two halves merged inside the workgroup (the same
+ * arithmetic; no attn_part, no second kernel). */
 vc_status vc_attention_fwd(const vc_desc* od, void* out, const vc_v_opts* opts,
                            const vc_attn_opts* aopts, const void* ws, size_t ws_bytes,
                            void* stream);
