@@ -24,6 +24,7 @@ CASES = [
     (1, {}, 0.0, True),
     (2, {}, 0.0, False),
     (2, {"S": 1000}, 0.01, False),   # ragged tail and repair tiles
+    (2, {"S": 4500, "H": 3}, 0.0, False),   # the attention call cut along the key axis, then merged
 ]
 
 
@@ -33,7 +34,7 @@ def _fresh(t: torch.Tensor, seed: int) -> torch.Tensor:
     return (t.float() * 0.9 + noise * 0.5).to(t.dtype)
 
 
-@pytest.mark.parametrize("cid,kw,beta,unbatched", CASES, ids=["config1_SH128", "config2", "config2_S1000_repair"])
+@pytest.mark.parametrize("cid,kw,beta,unbatched", CASES, ids=["config1_SH128", "config2", "config2_S1000_repair", "config2_S4500_cut"])
 def test_graph_replays_match_eager(cid, kw, beta, unbatched):
     w = synth.workload(cid, **kw)
     q, k, v = (t.cuda() for t in synth.generate(w, "cpu"))
