@@ -721,14 +721,16 @@ __global__ void __launch_bounds__(256) k_v_quant_pack(TensorArg v, int S, const 
 // 32u .. 32u+31) is exactly the 32 values that FP4 operand lane group u of
 // the P.V product holds, nibble n being position 32u + n: the key slots of
 // the tile are relabelled to match (mx_pos_of_slot; the K rows follow).
-// grid (nblk, H, B), 256 threads; thread = 2 (channel, group) pairs.
-__device__ __forceinline__ uint32_t e2m1_encode(float y) {
-  const float a = fabsf(y);
-  // thresholds of round half to even on the grid 0, .5, 1, 1.5, 2, 3, 4, 6
-  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
-                     (a > 5.0f);
-  return c | ((__float_as_uint(y) >> 28) & 8u);
-}
+// The codes come from the gfx950 conversion v_cvt_scalef32_pk_fp4_f32, two
+// values per instruction: it gives the E2M1 code of src / scale, rounded to
+// nearest even, saturated at +-6, with the input's sign -- the definition
+// above for scale = X = 2^e (checked against the oracle's encoder on every
+// E2M1 tie and boundary, signed zeros, saturation and e from -127 to 127,
+// subnormal scales included).
+// grid (nblk, H, B), 64 threads: thread t takes group u = t / 16 and
+// channels d = 8(t % 16) .. +7, all 32 positions of the group (one 16-byte
+// row load per position), so a channel's 32 codes and its scale form in one
+// thread.
 // Smallest e with amax <= 6 * 2^e, for amax = m * 2^k (m in [0.5, 1)):
 // e = k - 3 when m <= 0.75, else k - 2; 0 for amax == 0; clamped to the
 // E8M0 range.
@@ -739,18 +741,23 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   const int e = k - (m <= 0.75f ? 3 : 2);
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
+constexpr int kFp4PackThreads = 64;
 template <int DT>
-__global__ void __launch_bounds__(256) k_v_quant_pack_fp4(TensorArg v, int S, const int32_t* perm,
-                                                          const float* v_mean, vc_head_hdr* hdr, uint8_t* v8,
-                                                          uint8_t* v_muop) {
-  __shared__ float res[kBlock][kD + 1];   // residual of the tile (padded rows against bank conflicts)
-  __shared__ float mu[kD];
+__global__ void __launch_bounds__(kFp4PackThreads) k_v_quant_pack_fp4(TensorArg v, int S, const int32_t* perm,
+                                                                     const float* v_mean, vc_head_hdr* hdr,
+                                                                     uint8_t* v8, uint8_t* v_muop) {
+  __shared__ int32_t pp[kBlock];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h, blk = blockIdx.x, nblk = gridDim.x;
-  if (threadIdx.x < kD) {
-    const int ch = threadIdx.x;
-    const float m = v_mean[(static_cast<int64_t>(bh) * nblk + blk) * kD + ch];
-    mu[ch] = m;
-    // restore operand: mu (s_v = 1) split into bf16 high and low parts
+  const int t = threadIdx.x, u = t >> 4, c8 = (t & 15) * 8;
+  const int p0 = blk * kBlock, n = S - p0 < kBlock ? S - p0 : kBlock;
+  // the tile's tokens (a position past the end takes the tile's first token; its residual is 0)
+  for (int j = t; j < kBlock; j += kFp4PackThreads) pp[j] = perm[static_cast<int64_t>(bh) * S + p0 + (j < n ? j : 0)];
+  const float* mrow = v_mean + (static_cast<int64_t>(bh) * nblk + blk) * kD;
+  // restore operands: mu (s_v = 1) split into bf16 high and low parts, channels t and t + 64
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int ch = t + 64 * half;
+    const float m = mrow[ch];
     const uint16_t hi = static_cast<uint16_t>(f32_to_bf16_bits(m));
     const uint16_t lo = static_cast<uint16_t>(f32_to_bf16_bits(m - __uint_as_float(static_cast<uint32_t>(hi) << 16)));
     const int p = blk % kMuOpGroup, row = (blk - p) + 2 * (ch >> 4);
@@ -759,39 +766,48 @@ __global__ void __launch_bounds__(256) k_v_quant_pack_fp4(TensorArg v, int S, co
     *reinterpret_cast<uint16_t*>(base + static_cast<int64_t>(row) * kMuOpRowBytes + off) = hi;
     *reinterpret_cast<uint16_t*>(base + static_cast<int64_t>(row + 1) * kMuOpRowBytes + off) = lo;
   }
-  if (blk == 0 && threadIdx.x == 0) {
+  if (blk == 0 && t == 0) {
     hdr[bh].v_scale = 1.0f;
     hdr[bh].v_inv = 1.0f;
   }
-  float x[kPackIt][8];
-  bool live[kPackIt];
-  gather_tile_rows<DT>(v, S, perm, b, h, bh, blk, x, live);
+  const float4 m0 = *reinterpret_cast<const float4*>(mrow + c8);
+  const float4 m1 = *reinterpret_cast<const float4*>(mrow + c8 + 4);
+  const float mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
   __syncthreads();
-  const int c8 = (threadIdx.x & 15) * 8;
+  // the group's 32 rows, channels c8 .. c8+7: every load issued before any use
+  uint4 raw[32];
 #pragma unroll
-  for (int it = 0; it < kPackIt; ++it) {
-    const int j = (threadIdx.x + 256 * it) >> 4;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) res[j][c8 + e] = live[it] ? x[it][e] - mu[c8 + e] : 0.0f;
-  }
-  __syncthreads();
+  for (int i = 0; i < 32; ++i)
+    raw[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(v.p) + b * v.sB +
+                                             static_cast<int64_t>(pp[32 * u + i]) * v.sS + h * v.sH + c8);
+  const int live = n - 32 * u;   // real positions of the group (<= 0: none)
   uint8_t* tile = v8 + (static_cast<int64_t>(bh) * nblk + blk) * kTileBytes;
-  for (int task = threadIdx.x; task < kD * 4; task += blockDim.x) {
-    const int d = task & (kD - 1), u = task >> 7;     // channel, group = lane group
-    // nibble n of lane group u holds permuted position 32u + n of the tile
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float r[32];
     float amax = 0.0f;
-#pragma unroll 8
-    for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(res[32 * u + n][d]));
-    const int e = mx_exponent(amax);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 8
-    for (int n = 0; n < 32; ++n) {
-      const float y = ldexpf(res[32 * u + n][d], -e);
-      w[n >> 3] |= e2m1_encode(y) << (4 * (n & 7));
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t w = (e >> 1) == 0 ? raw[i].x : (e >> 1) == 1 ? raw[i].y : (e >> 1) == 2 ? raw[i].z : raw[i].w;
+      const float x = DT == VC_BF16 ? __uint_as_float(e & 1 ? (w & 0xFFFF0000u) : (w << 16))
+                                    : f16_bits_to_f32(e & 1 ? (w >> 16) : (w & 0xFFFFu));
+      r[i] = i < live ? x - mu[e] : 0.0f;
+      amax = fmaxf(amax, fabsf(r[i]));
     }
-    const int lane = u * 16 + (d & 15), dt = d >> 4;
-    *reinterpret_cast<uint4*>(tile + (dt * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    tile[8192 + lane * 8 + dt] = static_cast<uint8_t>(e + 127);
+    const int ex = mx_exponent(amax);
+    const float sc = ldexpf(1.0f, ex);
+    // nibble n of lane group u holds position 32u + n: byte b = n / 2 of the 16
+    uint32_t q[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {   // word qq: positions 8qq .. 8qq+7, byte select an immediate
+      q[qq] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[8 * qq], r[8 * qq + 1], sc, 0);
+      q[qq] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q[qq], r[8 * qq + 2], r[8 * qq + 3], sc, 1);
+      q[qq] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q[qq], r[8 * qq + 4], r[8 * qq + 5], sc, 2);
+      q[qq] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q[qq], r[8 * qq + 6], r[8 * qq + 7], sc, 3);
+    }
+    const int d = c8 + e, lane = u * 16 + (d & 15), dt = d >> 4;
+    *reinterpret_cast<uint4*>(tile + (dt * 64 + lane) * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+    tile[8192 + lane * 8 + dt] = static_cast<uint8_t>(ex + 127);
   }
 }
 
@@ -1193,7 +1209,7 @@ hipError_t launch_prepare_v(const TensorArg& v, int B, int S, int H, const vc_v_
   VC_LAUNCH_CHECK();
   const bool bf16 = v.dtype == VC_BF16;
   if (o.v_format == VC_V_MXFP4)
-    hipLaunchKernelGGL(bf16 ? k_v_quant_pack_fp4<VC_BF16> : k_v_quant_pack_fp4<VC_F16>, gblk, dim3(256), 0, st, v, S,
+    hipLaunchKernelGGL(bf16 ? k_v_quant_pack_fp4<VC_BF16> : k_v_quant_pack_fp4<VC_F16>, gblk, dim3(kFp4PackThreads), 0, st, v, S,
                        ws.perm, ws.v_mean, ws.hdr, ws.v8, ws.v_muop);
   else
     hipLaunchKernelGGL(bf16 ? k_v_quant_pack<VC_BF16> : k_v_quant_pack<VC_F16>, gblk, dim3(256), 0, st, v, S, ws.perm,
