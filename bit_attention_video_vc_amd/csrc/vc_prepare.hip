@@ -250,6 +250,11 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
                                                        const uint8_t* cent_op, const int32_t* cnorm,
                                                        int64_t* csum, int32_t* ccount, int32_t* assign,
                                                        int32_t* chunk_hist) {
+  // with at most 32 clusters (NCT <= 2) the sums are kept twice, lanes of
+  // even and odd token index adding into their own copy: tokens of one
+  // cluster in a lane group then meet on one LDS address half as often
+  constexpr int kCopies = NCT <= 2 ? 2 : 1;
+  constexpr int kCopyPitch = kMaxK / kCopies * kPairPitch;
   __shared__ uint64_t sums[ACCUM ? kMaxK * kPairPitch : 1];
   __shared__ int32_t cnt[kMaxK];
   const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y, bh = b * H + h;
@@ -258,7 +263,7 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
   const bool big = DT == VC_BF16 && shift > 127;
   const SketchScale skc = {ldexpf(1.0f, min(shift, 127)), ldexpf(1.0f, shift - 127)};
   if (ACCUM)
-    for (int i = tid; i < k * kPairPitch; i += 256) sums[i] = 0;
+    for (int i = tid; i < kMaxK * kPairPitch; i += 256) sums[i] = 0;
   if (tid < kMaxK) cnt[tid] = 0;
   // centroid operands (prepared with the centroids) and norms
   v8bf ca[NCT][4];
@@ -332,7 +337,8 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            atomicAdd(&sums[bc * kPairPitch + 16 * kk + 4 * g + q], u[kk][q]);
+            atomicAdd(&sums[(kCopies == 2 ? (l16 & 1) * kCopyPitch : 0) + bc * kPairPitch + 16 * kk + 4 * g + q],
+                      u[kk][q]);
       }
     }
   };
@@ -359,7 +365,9 @@ __global__ void __launch_bounds__(256) k_kmeans_assign(TensorArg v, int S, int k
     // values)
     auto block_sum = [&](int i) {
       const int c = i / kD, d = i % kD;
-      const uint64_t wd = sums[c * kPairPitch + (d >> 1)];
+      // (the copies' halves add without a carry: the block's tokens are split between them)
+      const int at = c * kPairPitch + (d >> 1);
+      const uint64_t wd = sums[at] + (kCopies == 2 ? sums[kCopyPitch + at] : 0);
       return static_cast<int32_t>(d & 1 ? wd >> 32 : wd & 0xFFFFFFFFu) - 256 * cnt[c];
     };
     if (wide_sums(S)) {
