@@ -41,3 +41,20 @@ def test_prepare_byte_model():
     assert rep["prepare_v_algorithmic_GBps"] == round(17 * n / 1e-3 / 1e9, 1)
     # Q and K: read 2 B, write 1 B each
     assert rep["prepare_qk_algorithmic_GBps"] == round(6 * n / 1e-3 / 1e9, 1)
+
+
+def test_roofline_kernel_label_follows_the_launch_plan():
+    """bench.py names the short-launch kernel exactly for the workloads the
+    library's work split runs in that form (the rule of attn_split, restated
+    by tests/test_split_plan.py)."""
+    sys.path.insert(0, ROOT)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import bench
+    import synth
+    from test_split_plan import plan
+    for cid, kw in [(1, {}), (2, {}), (2, {"S": 2049, "H": 14}), (2, {"S": 4500, "H": 3}), (2, {"S": 4096, "H": 9}),
+                    (3, {}), (4, {}), (4, {"H": 7}), (5, {})]:
+        w = synth.workload(cid, **kw)
+        p = plan(w.B * w.H, -(-w.S // 128), 1 if w.repair_budget > 0 else 0)
+        halves = bool(p and p.get("halves"))
+        assert ("k_vc_attn_halves" in bench.attention_kernels(w)) == halves, (cid, kw)
