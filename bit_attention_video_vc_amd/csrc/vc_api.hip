@@ -263,6 +263,7 @@ const char* vc_status_string(vc_status s) {
     case VC_ERR_UNSUPPORTED: return "VC_ERR_UNSUPPORTED";
     case VC_ERR_WORKSPACE: return "VC_ERR_WORKSPACE";
     case VC_ERR_DEVICE: return "VC_ERR_DEVICE";
+    default: break;
   }
   return "VC_ERR_UNKNOWN";
 }

@@ -62,7 +62,10 @@ typedef enum {
   VC_ERR_ARG = 1,          /* null pointer, bad size, bad stride or option   */
   VC_ERR_UNSUPPORTED = 2,  /* D != 128, unsupported dtype or k, not gfx950   */
   VC_ERR_WORKSPACE = 3,    /* workspace smaller than vc_workspace_layout's   */
-  VC_ERR_DEVICE = 4        /* HIP runtime or kernel launch failure           */
+  VC_ERR_DEVICE = 4,       /* HIP runtime or kernel launch failure           */
+  VC_STATUS_INT_RANGE_ = 0x7FFFFFFF  /* not a status: gives the enum the range of
+                                        int32, so that vc_status_string is
+                                        defined for any int a caller passes  */
 } vc_status;
 
 typedef enum { VC_F16 = 0, VC_BF16 = 1 } vc_dtype;
