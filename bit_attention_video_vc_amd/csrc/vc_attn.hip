@@ -54,6 +54,8 @@
 //     sums and its reference exponent in a partial slot, and k_vc_attn_merge
 //     adds an item's pieces with power-of-two weights, the online softmax's
 //     own rescale.
+#include <type_traits>
+
 #include "vc_common.hpp"
 #include "vc_kernels.hpp"
 
@@ -706,7 +708,8 @@ __device__ __forceinline__ void restore_ops_lds(const uint8_t* grp, int lane16, 
 // HALVES (the short-launch kernel, each half of the workgroup on its own key
 // range with two-slot rings): K(kb+2) is in kcur and V(kb) in vcur; the step
 // first copies K(kb+3) into kfree and V(kb+1) into vfree (the slots that
-// held K(kb+1) and V(kb-1), both last read in step kb-1), all at once, and
+// held K(kb+1) and V(kb-1), or K(0) at step 0, all last read before the
+// previous barrier), all at once, and
 // its barrier waits for them; a group's restore operands are read from
 // global memory, for every group that holds a real tile of the half, at the
 // group's last step (a half shorter than the step count runs masked steps
@@ -1243,13 +1246,16 @@ __global__ void __launch_bounds__(256) k_vc_attn_merge(AttnArgs a, AttnTail tl) 
 // key tiles [0, ka) and waves 4-7 tiles [ka, nblk), ka = 16 * ceil(ngrp/2),
 // each wave owning the same 32 queries (w % 4) of qb in both halves, so the
 // per-wave work of a step is that of the whole-item kernel.  Each half
-// streams its tiles through its own two K and two V slots; both halves run
+// streams its tiles through its own four slots, a two-slot K ring and a
+// two-slot V ring (the prologue fills all four at once); both halves run
 // ka steps (the shorter one masked past its end) under one barrier per step.
-// Then waves 4-7 leave O, l and their reference exponent in LDS and waves
-// 0-3 add them to their own with the weights 2^(e_i - max e) -- the merge of
-// the cut items, inside the workgroup -- and write the output.
+// Then each wave and its partner in the other half swap half of O, and l
+// and their reference exponents, through LDS, and each adds the partner's
+// part to its own with the weights 2^(e_i - max e) -- the merge of the cut
+// items, inside the workgroup -- and writes its 64 output channels.
 struct HalfLds {
   uint8_t *k0, *k1, *k2, *k3, *v0, *v1, *v2, *v3;
+  uint8_t* junk;      // 8 waves x 256 bytes: landing room of the L2 warm-up
 };
 template <int VF>
 __device__ __forceinline__ void attn_halves(const AttnArgs& a, int bh, int qb, int ka, const HalfLds& L) {
@@ -1267,6 +1273,30 @@ __device__ __forceinline__ void attn_halves(const AttnArgs& a, int bh, int qb, i
   uint8_t* const k1 = half ? L.k3 : L.k1;
   uint8_t* const v0 = half ? L.v2 : L.v0;
   uint8_t* const v1 = half ? L.v3 : L.v1;
+
+  // L2 warm-up.  The head's nblk workgroups (one per query block, placed on
+  // one XCD by xcd_order where the head's blocks fill it) each touch one
+  // 128-byte line per lane: K tile qb (waves 0-1), V tile qb (waves 2-3)
+  // and every nblk-th line of the restore operands (waves 4-7), so the
+  // head's tiles come into L2 at once, at the start, and the copies of the
+  // steps find them there instead of each missing in turn.  The four bytes
+  // a lane fetches land in a buffer of their own that no one reads.
+  {
+    const uint32_t line = static_cast<uint32_t>(tid & 127) * 128;
+    uint8_t* const junk = L.junk + w * 256;
+    if (w < 4) {
+      const uint8_t* const base = (w < 2 ? a.k8 : a.v8) + static_cast<int64_t>(bh) * nfull * kTileBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(head_rsrc(base, static_cast<uint32_t>(nfull) * kTileBytes),
+                                               (__attribute__((address_space(3))) void*)junk, 4,
+                                               static_cast<uint32_t>(qb) * kTileBytes + line, 0, 0, 0);
+    } else {
+      const int nrows_h = muop_rows(nfull);
+      const uint8_t* const base = a.v_muop + static_cast<int64_t>(bh) * nrows_h * kMuOpRowBytes;
+      const uint32_t l = static_cast<uint32_t>(tid - 256) * static_cast<uint32_t>(nfull) + static_cast<uint32_t>(qb);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(head_rsrc(base, static_cast<uint32_t>(nrows_h) * kMuOpRowBytes),
+                                               (__attribute__((address_space(3))) void*)junk, 4, l * 128, 0, 0, 0);
+    }
+  }
 
   TileCtx c;
   c.kr = head_rsrc(a.k8 + (static_cast<int64_t>(bh) * nfull + kv0) * kTileBytes,
@@ -1309,11 +1339,12 @@ __device__ __forceinline__ void attn_halves(const AttnArgs& a, int bh, int qb, i
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc.rr[j][0] = acc.rr[j][1] = 0.0f;
 
-  // ---- prologue: K(0), V(0), K(1); scores and codes of tile 0, scores of
-  // tile 1; then K(2) into the slot of K(0) ----
+  // ---- prologue: K(0) into k0, V(0) into v0, K(1) into k1 and K(2) into
+  // v1, all at once; scores and codes of tile 0, scores of tile 1 ----
   const int last = nblk - 1;
   HalfCopies<VF>(c, 0, 0, k0, v0).issue_all();
   HalfCopies<VF>(c, last < 1 ? last : 1, 0, k1, nullptr).issue_all();
+  HalfCopies<VF>(c, last < 2 ? last : 2, 0, v1, nullptr).issue_all();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   {
@@ -1331,18 +1362,17 @@ __device__ __forceinline__ void attn_halves(const AttnArgs& a, int bh, int qb, i
     for (int t = 1; t < 8; ++t) acc.mh[qi] = max_acc4(acc.mh[qi], acc.sh[t][qi]);
   }
   acc.sig = ((sqs * c.ks[last < 1 ? last : 1]) * a.sm_scale) * kLog2e;
-  __syncthreads();   // k0 is refilled
-  HalfCopies<VF>(c, last < 2 ? last : 2, 0, k0, nullptr).issue_all();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  __syncthreads();   // k0 and k1 are refilled by step 0
 
-  // Step kb reads K(kb+2) from slot kb%2 and V(kb) from slot kb%2.  ka is a
-  // multiple of 16, so the loop has no remainder.
+  // The four slots are two rings: K(kb+2) is in v1 for even kb and in k1
+  // for odd kb, V(kb) in v0 for even kb and in k0 for odd kb (step 0 puts
+  // V(1) where K(0) was).  ka is a multiple of 16, so the loop has no
+  // remainder.
   for (int kb = 0; kb < ka; kb += 4) {
-    tile_step<VF, 0, true>(c, kb, k0, k1, v0, v1, qop, acc);
-    tile_step<VF, 1, true>(c, kb + 1, k1, k0, v1, v0, qop, acc);
-    tile_step<VF, 2, true>(c, kb + 2, k0, k1, v0, v1, qop, acc);
-    tile_step<VF, 3, true>(c, kb + 3, k1, k0, v1, v0, qop, acc);
+    tile_step<VF, 0, true>(c, kb, v1, k1, v0, k0, qop, acc);
+    tile_step<VF, 1, true>(c, kb + 1, k1, v1, k0, v0, qop, acc);
+    tile_step<VF, 2, true>(c, kb + 2, v1, k1, v0, k0, qop, acc);
+    tile_step<VF, 3, true>(c, kb + 3, k1, v1, k0, v0, qop, acc);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const int lane_p = c.lane16 >> 4, g_p = lane_p >> 4, l16_p = lane_p & 15;
@@ -1355,44 +1385,62 @@ __device__ __forceinline__ void attn_halves(const AttnArgs& a, int bh, int qb, i
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi)
     e[qi] = acc.st.M[qi] - static_cast<float>(static_cast<int>((acc.st.se >> (8 * qi)) & 0xFF) - 127);
-  // the partner's O, lane-interleaved, in K buffer wq; its l [2][16] and
-  // e [2][16] in V buffer 0
+  // Each wave and its partner (w ^ 4, the same queries in the other half)
+  // merge and write half of the channel sub-tiles: half 0 dt 0-3, half 1
+  // dt 4-7.  Each leaves the other's four, lane-interleaved, in K buffer
+  // wq (dt 0-3 in its first 8 KB, dt 4-7 in the second) and its l [2][16]
+  // and e [2][16] in V buffer 0 (64 floats per half and wave).
   float* const xo = reinterpret_cast<float*>(wq == 0 ? L.k0 : wq == 1 ? L.k1 : wq == 2 ? L.k2 : L.k3);
-  float* const xl = reinterpret_cast<float*>(L.v0) + wq * 64;
-  if (half) {
+  float* const xl = reinterpret_cast<float*>(L.v0) + wq * 128;
+  // (the sub-tile indices are constants in each branch: O stays in registers)
+  const auto send = [&](auto ds) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int qi = 0; qi < 2; ++qi) *reinterpret_cast<v4f*>(xo + ((dt * 2 + qi) * 64 + lane_p) * 4) = acc.O[dt][qi];
-    if (g_p == 0) {
+      for (int qi = 0; qi < 2; ++qi)
+        *reinterpret_cast<v4f*>(xo + (((ds + i) * 2 + qi) * 64 + lane_p) * 4) = acc.O[ds + i][qi];
+  };
+  if (half)
+    send(std::integral_constant<int, 0>{});
+  else
+    send(std::integral_constant<int, 4>{});
+  if (g_p == 0) {
 #pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
-        xl[qi * 16 + l16_p] = acc.st.l[qi];
-        xl[32 + qi * 16 + l16_p] = e[qi];
-      }
+    for (int qi = 0; qi < 2; ++qi) {
+      xl[half * 64 + qi * 16 + l16_p] = acc.st.l[qi];
+      xl[half * 64 + 32 + qi * 16 + l16_p] = e[qi];
     }
   }
   __syncthreads();
-  if (half) return;
   const float sv = a.hdr[bh].v_scale;
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi) {
-    const float lb = xl[qi * 16 + l16_p], eb = xl[32 + qi * 16 + l16_p];
-    const float E = fmaxf(e[qi], eb);
-    const float wa = ldexpf(1.0f, static_cast<int>(fmaxf(e[qi] - E, -200.0f)));
+    // (l, e) of half 0 and of half 1; the weights 2^(e_i - max e)
+    const float lp = xl[(1 - half) * 64 + qi * 16 + l16_p], ep = xl[(1 - half) * 64 + 32 + qi * 16 + l16_p];
+    const float la = half ? lp : acc.st.l[qi], ea = half ? ep : e[qi];
+    const float lb = half ? acc.st.l[qi] : lp, eb = half ? e[qi] : ep;
+    const float E = fmaxf(ea, eb);
+    const float wa = ldexpf(1.0f, static_cast<int>(fmaxf(ea - E, -200.0f)));
     const float wb = ldexpf(1.0f, static_cast<int>(fmaxf(eb - E, -200.0f)));
-    const float f = sv / (wa * acc.st.l[qi] + wb * lb);
+    const float f = sv / (wa * la + wb * lb);
     const int q = qb * kBlock + 16 * (2 * wq + qi) + l16_p;
     if (q < S) {
       uint16_t* orow = a.out + b * a.osB + static_cast<int64_t>(q) * a.osS + h * a.osH;
+      const auto write = [&](auto d0, auto mine_b) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const v4f ob = *reinterpret_cast<const v4f*>(xo + ((dt * 2 + qi) * 64 + lane_p) * 4);
-        const v4f o = wa * acc.O[dt][qi] + wb * ob;
-        const uint32_t lo = f32_to_bf16_bits(o[0] * f) | (f32_to_bf16_bits(o[1] * f) << 16);
-        const uint32_t hi = f32_to_bf16_bits(o[2] * f) | (f32_to_bf16_bits(o[3] * f) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g_p) = make_uint2(lo, hi);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int dt = d0 + i;
+          const v4f op = *reinterpret_cast<const v4f*>(xo + ((dt * 2 + qi) * 64 + lane_p) * 4);
+          const v4f o = mine_b ? wa * op + wb * acc.O[dt][qi] : wa * acc.O[dt][qi] + wb * op;
+          const uint32_t lo = f32_to_bf16_bits(o[0] * f) | (f32_to_bf16_bits(o[1] * f) << 16);
+          const uint32_t hi = f32_to_bf16_bits(o[2] * f) | (f32_to_bf16_bits(o[3] * f) << 16);
+          *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g_p) = make_uint2(lo, hi);
+        }
+      };
+      if (half)
+        write(std::integral_constant<int, 4>{}, std::true_type{});
+      else
+        write(std::integral_constant<int, 0>{}, std::false_type{});
     }
   }
 }
@@ -1404,11 +1452,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_vc_attn_halves(AttnArgs a, 
   __shared__ __align__(16) uint8_t kbuf1[kKBufBytes];
   __shared__ __align__(16) uint8_t kbuf2[kKBufBytes];
   __shared__ __align__(16) uint8_t kbuf3[kKBufBytes];
-  __shared__ __align__(16) uint8_t vbuf0[VTile<VF>::kBytes];
-  __shared__ __align__(16) uint8_t vbuf1[VTile<VF>::kBytes];
-  __shared__ __align__(16) uint8_t vbuf2[VTile<VF>::kBytes];
-  __shared__ __align__(16) uint8_t vbuf3[VTile<VF>::kBytes];
-  const HalfLds L = {kbuf0, kbuf1, kbuf2, kbuf3, vbuf0, vbuf1, vbuf2, vbuf3};
+  // (every slot takes K and V tiles in turn, so all are K-sized)
+  __shared__ __align__(16) uint8_t vbuf0[kKBufBytes];
+  __shared__ __align__(16) uint8_t vbuf1[kKBufBytes];
+  __shared__ __align__(16) uint8_t vbuf2[kKBufBytes];
+  __shared__ __align__(16) uint8_t vbuf3[kKBufBytes];
+  __shared__ __align__(16) uint8_t junk[kAttnWaves * 256];
+  const HalfLds L = {kbuf0, kbuf1, kbuf2, kbuf3, vbuf0, vbuf1, vbuf2, vbuf3, junk};
   const int nq = a.nblk;
   const int item = xcd_order(gridDim.x, blockIdx.x);
   const int bh = item / nq;
