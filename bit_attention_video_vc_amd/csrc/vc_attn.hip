@@ -1274,10 +1274,10 @@ __device__ __forceinline__ void attn_halves(const AttnArgs& a, int bh, int qb, i
   uint8_t* const v0 = half ? L.v2 : L.v0;
   uint8_t* const v1 = half ? L.v3 : L.v1;
 
-  // L2 warm-up.  The head's nblk workgroups (one per query block, placed on
+  // L2 warm-up.  The head's nfull workgroups (one per query block, placed on
   // one XCD by xcd_order where the head's blocks fill it) each touch one
   // 128-byte line per lane: K tile qb (waves 0-1), V tile qb (waves 2-3)
-  // and every nblk-th line of the restore operands (waves 4-7), so the
+  // and every nfull-th line of the restore operands (waves 4-7), so the
   // head's tiles come into L2 at once, at the start, and the copies of the
   // steps find them there instead of each missing in turn.  The four bytes
   // a lane fetches land in a buffer of their own that no one reads.
