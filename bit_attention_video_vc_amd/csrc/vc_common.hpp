@@ -29,10 +29,10 @@ constexpr int kMuOpRowBytes = 512;
 constexpr int kMuOpGroup = 16;
 __host__ __device__ inline int muop_rows(int nblk) { return kMuOpGroup * ((nblk + 3 + kMuOpGroup - 1) / kMuOpGroup); }
 // Tokens per k-means assignment / sort chunk (one workgroup each): 1024,
-// halved down to 256 while the B*H*chunks grid would not fill the GPU
+// halved down to 128 while the B*H*chunks grid would not fill the GPU
 // several times over (short sequences).
 constexpr int kAsgTokMax = 1024;
-constexpr int kAsgTokMin = 256;
+constexpr int kAsgTokMin = 128;
 __host__ __device__ inline int asg_tokens(int64_t BH, int S) {
   int t = kAsgTokMax;
   while (t > kAsgTokMin && BH * ((S + t - 1) / t) < 1024) t >>= 1;

@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(256) k_kmeans_init(TensorArg v, int S, int H, 
   write_cent_ops(bh, k, cl, 0, kMaxK, cent_op, cnorm);
 }
 
-// One Lloyd assignment pass over asg (asg_tokens: 256..1024) tokens per workgroup.
+// One Lloyd assignment pass over asg (asg_tokens: 128..1024) tokens per workgroup.
 //   ACCUM: add the block's per-cluster sketch sums and counts to csum/ccount.
 //   FINAL: write assign[] and the block's cluster histogram (for the sort).
 // Distances run on the matrix core: (2C) . X^T with
@@ -482,8 +482,8 @@ __global__ void __launch_bounds__(64 * kScanRows) k_cluster_scan(int S, int k, i
 
 // Stable counting-sort scatter: perm[pos] = token, ordered by (cluster, token).
 // One asg-token chunk per workgroup, walked in token order in passes of
-// 256; ranks within a wave come from ballots.  grid (ceil(S/1024), H, B),
-// 256 threads.
+// 256 (one pass of 128 when asg = 128); ranks within a wave come from
+// ballots.  grid (ceil(S/asg), H, B), 256 threads.
 __global__ void __launch_bounds__(256) k_cluster_scatter(int S, int k, int asg, const int32_t* assign,
                                                          const int32_t* chunk_off, int32_t* perm) {
   __shared__ int32_t wcount[4][kMaxK];
@@ -494,11 +494,11 @@ __global__ void __launch_bounds__(256) k_cluster_scatter(int S, int k, int asg, 
   const int32_t* off = chunk_off + (static_cast<int64_t>(bh) * nchunk + blockIdx.x) * k;
   if (tid < kMaxK) run[tid] = 0;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int it = 0; it < asg / 256; ++it) {
+  for (int it = 0; it < (asg + 255) / 256; ++it) {
     for (int i = tid; i < 4 * kMaxK; i += 256) (&wcount[0][0])[i] = 0;
     __syncthreads();
     const int s = blockIdx.x * asg + it * 256 + tid;
-    const bool valid = s < S;
+    const bool valid = it * 256 + tid < asg && s < S;
     const int c = valid ? assign[static_cast<int64_t>(bh) * S + s] : -1;
     uint64_t rem = __ballot(valid);
     int rank = 0;
