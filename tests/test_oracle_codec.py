@@ -29,14 +29,17 @@ def test_decode_matches_torch_all_codes():
 
 
 def test_decode_anchor_values():
+    # the OCP OFP8 specification's named E4M3 points (tests/golden/ocp_e4m3_anchors.txt)
+    from golden import rows
     d = O.e4m3_decode
-    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
-    assert d(0x08) == 2.0 ** -6          # smallest normal
-    assert d(0x01) == 2.0 ** -9          # smallest subnormal
-    assert d(0x38) == 1.0
-    assert d(0x78) == 256.0
-    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
-    assert d(0x80) == 0.0 and np.signbit(d(0x80))
+    anchors = rows("ocp_e4m3_anchors.txt")
+    assert len(anchors) == 11
+    for code, value, *_ in anchors:
+        got, want = float(d(int(code, 16))), float(value)
+        if np.isnan(want):
+            assert np.isnan(got), code
+        else:
+            assert got == want and np.signbit(got) == np.signbit(want), (code, got, want)
     assert np.sum(~np.isnan(O.e4m3_decode(ALL))) == 254
     # codes 0..126 are strictly increasing in value
     assert np.all(np.diff(O.e4m3_decode(np.arange(127))) > 0)

@@ -62,9 +62,15 @@ def test_init_positions_distinct_in_range():
 
 
 # SplitMix64's published outputs from state 0 (the first three of its
-# sequence): output i is the mixer applied to state i*gamma.
-SM64_OUT = (0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F)
-GAMMA = 0x9E3779B97F4A7C15
+# sequence, tests/golden/splitmix64_state0.txt): output i is the mixer
+# applied to state i*gamma.
+def _sm64_fixture():
+    from golden import rows
+    r = {name: int(value, 16) for name, value in rows("splitmix64_state0.txt")}
+    return r["gamma"], (r["1"], r["2"], r["3"])
+
+
+GAMMA, SM64_OUT = _sm64_fixture()
 
 
 def test_init_positions_values_from_published_outputs():

@@ -13,6 +13,18 @@ from oracle import vc_oracle as O
 
 
 # --------------------------------------------------------------- E2M1 codec
+def test_e2m1_decode_matches_the_mx_specification_table():
+    # every code against the OCP MX specification's E2M1 values
+    # (tests/golden/ocp_e2m1_values.txt), signs of zero included
+    from golden import rows
+    table = rows("ocp_e2m1_values.txt")
+    assert len(table) == 16
+    d = O.e2m1_decode(np.arange(16))
+    for code, value in table:
+        got, want = float(d[int(code, 16)]), float(value)
+        assert got == want and np.signbit(got) == np.signbit(want), (code, got, want)
+
+
 def test_e2m1_decode_is_the_2e1m_float_with_bias_1():
     # Properties that fix a 1-sign, 2-exponent, 1-mantissa float with
     # exponent bias 1: code 2 (exponent 1, mantissa 0) is 1.0; each exponent
