@@ -358,18 +358,19 @@ def test_kmeans_options(kc, iters, seed):
     check_against_oracle(q, k, v, kc=kc, iters=iters, seed=seed, name=f"k={kc} T={iters} seed={seed}")
 
 
-def test_kmeans_sums_past_int32():
+@pytest.mark.parametrize("S", [8422400, 1 << 24], ids=["S8422400", "S_max_2^24"])
+def test_kmeans_sums_past_int32(S):
     """k-means at a length where a cluster's sketch sum passes 2^31.
 
-    S = 8422400 tokens with channel 0 = 1.9921875 (sketch +255) except a run
-    of 200 tokens at -1.9921875 (sketch -255) around cluster 1's initial
-    position; every other channel is 0.  With k=2 and one iteration the
-    centroids must come out (255, 0, ...) and (-255, 0, ...): cluster 0's
-    sum is 255 * 8422200 > 2^31 - 1, so a 32-bit accumulation would wrap
-    and pull both centroids to -255.  The answer is known by construction:
-    A tokens in cluster 0, the run in cluster 1, the permutation A then the
-    run, each ascending."""
-    S, seed = 8422400, 5
+    S tokens (8422400, and the largest supported length 2^24) with channel
+    0 = 1.9921875 (sketch +255) except a run of 200 tokens at -1.9921875
+    (sketch -255) around cluster 1's initial position; every other channel
+    is 0.  With k=2 and one iteration the centroids must come out
+    (255, 0, ...) and (-255, 0, ...): cluster 0's sum is 255 * (S - 200) >
+    2^31 - 1, so a 32-bit accumulation would wrap and pull both centroids
+    to -255.  The answer is known by construction: A tokens in cluster 0,
+    the run in cluster 1, the permutation A then the run, each ascending."""
+    seed = 5
     init = O.init_positions(S, 2, seed, 0)
     lo, hi = max(S // 2, int(init[1]) - 100), min(S, max(S // 2, int(init[1]) - 100) + 200)
     assert int(init[0]) < S // 2 and lo <= int(init[1]) < hi and hi - lo == 200
