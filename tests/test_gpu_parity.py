@@ -211,7 +211,7 @@ def explain_row(hq, hv, row, got, sm):
 
 
 def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0.0, rows=None, heads=None,
-                         sm_scale=0.0, name="", target_met=None, v_format="e4m3"):
+                         sm_scale=0.0, name="", target_met=None, v_format="e4m3", out=None):
     """Run the GPU path and compare every prepared product and the output with the oracle.
 
     Output gates per head: rel-L2 vs the oracle <= TOL_ORACLE, every row's
@@ -227,7 +227,7 @@ def check_against_oracle(q, k, v, *, smooth=True, kc=32, iters=5, seed=0, beta=0
         f"v_format={v_format}")
     fmt = vc.VC_V_MXFP4 if v_format == "mxfp4" else vc.VC_V_E4M3
     opts = vc.v_opts(smooth, kc, iters, seed, beta, fmt)
-    run = GpuRun(q, k, v, opts, sm_scale)
+    run = GpuRun(q, k, v, opts, sm_scale, out=out)
     B, S, H = run.B, run.S, run.H
     q4, k4, v4, o4 = (t if t.dim() == 4 else t[None] for t in (q, k, v, run.out))
     sm = O.DEFAULT_SM_SCALE if sm_scale == 0.0 else np.float32(sm_scale)
@@ -356,6 +356,24 @@ def test_kmeans_options(kc, iters, seed):
     # centroids' offset), on two batches of two heads
     w, q, k, v = _cfg(2, B=2, H=2, S=1000)
     check_against_oracle(q, k, v, kc=kc, iters=iters, seed=seed, name=f"k={kc} T={iters} seed={seed}")
+
+
+def test_largest_head_count():
+    """The most heads one launch takes: H = 65535 (the grid's second
+    dimension), B = 1, S = 130 (a full tile and a ragged one of 2 keys).
+    Inputs are drawn on the GPU from a seeded generator; five heads (both
+    ends, the middle, the neighbours of the ends) are checked against the
+    oracle in full, and the output, filled with NaN before the call, must
+    come out finite everywhere: every head's every row is written."""
+    B, H, S = 1, 65535, 130
+    g = torch.Generator(device="cuda").manual_seed(65535)
+    q, k, v = (torch.randn((B, S, H, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    out = torch.full((B, S, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    heads = [(0, 0), (0, 1), (0, 32767), (0, 65533), (0, 65534)]
+    check_against_oracle(q, k, v, kc=4, iters=2, seed=3, heads=heads, name=f"heads B={B} H={H} S={S}", out=out)
+    assert bool(torch.isfinite(out).all()), "output rows left unwritten"
+    del q, k, v, out
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("S", [8422400, 1 << 24], ids=["S8422400", "S_max_2^24"])
