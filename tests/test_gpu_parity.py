@@ -358,19 +358,22 @@ def test_kmeans_options(kc, iters, seed):
     check_against_oracle(q, k, v, kc=kc, iters=iters, seed=seed, name=f"k={kc} T={iters} seed={seed}")
 
 
-def test_largest_head_count():
+@pytest.mark.parametrize("B,H,S", [(1, 65535, 130), (16, 65535, 1)], ids=["H65535_S130", "BH_max_S1"])
+def test_largest_head_count(B, H, S):
     """The most heads one launch takes: H = 65535 (the grid's second
-    dimension), B = 1, S = 130 (a full tile and a ragged one of 2 keys).
-    Inputs are drawn on the GPU from a seeded generator; five heads (both
-    ends, the middle, the neighbours of the ends) are checked against the
-    oracle in full, and the output, filled with NaN before the call, must
-    come out finite everywhere: every head's every row is written."""
-    B, H, S = 1, 65535, 130
-    g = torch.Generator(device="cuda").manual_seed(65535)
+    dimension) with B = 1 and S = 130 (a full tile and a ragged one of 2
+    keys); and B = 16 (the third dimension) for B*H = 1048560, next to the
+    2^20 limit, at the degenerate length S = 1 (one key per head).  Inputs
+    are drawn on the GPU from a seeded generator; five heads (both ends,
+    the middle, the neighbours of the ends) are checked against the oracle
+    in full, and the output, filled with NaN before the call, must come out
+    finite everywhere: every head's every row is written."""
+    g = torch.Generator(device="cuda").manual_seed(65535 + B)
     q, k, v = (torch.randn((B, S, H, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
     out = torch.full((B, S, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
-    heads = [(0, 0), (0, 1), (0, 32767), (0, 65533), (0, 65534)]
-    check_against_oracle(q, k, v, kc=4, iters=2, seed=3, heads=heads, name=f"heads B={B} H={H} S={S}", out=out)
+    heads = [(0, 0), (0, 1), (B // 2, H // 2), (B - 1, H - 2), (B - 1, H - 1)]
+    check_against_oracle(q, k, v, kc=min(4, S), iters=2, seed=3, heads=heads, name=f"heads B={B} H={H} S={S}",
+                         out=out)
     assert bool(torch.isfinite(out).all()), "output rows left unwritten"
     del q, k, v, out
     torch.cuda.empty_cache()
